@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for batched paged-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the library.  It shares
+no code with the HIP path; the two meet only in the seeded inputs of
+``workloads``.
+
+The arithmetic lives in ``oracle.c`` (plain C, two-pass softmax in double
+precision); this module marshals arrays into it.  See that file's header for
+the passages of the documentation each step follows.
+
+Parity status of each function:
+  decode          pinned (tests/test_oracle.py: brute force, closed forms,
+                  logsumexp, sink, window, causal prefix, GQA, page permutation,
+                  page-size repack, merge of disjoint ranges, hand-worked
+                  golden cases)
+  merge_states    pinned (merge of disjoint key ranges equals the union)
+  decode, lse with sinks present: the keys-only reading of the LSE is a
+                  reading, not fixed by the pages -> parity unpinned for that
+                  combination.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16, F16 = 0, 1
+_ERRORS = {1: "bad argument", 2: "visible key maps outside the page pool", 3: "out of memory"}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [
+            p, i64, i64,                 # q
+            p, i64, i64, i64,            # k
+            p, i64, i64, i64,            # v
+            ctypes.c_int, i64, i64, i64, i64, i64, i64,
+            p, i64, i64,                 # block tables
+            p, ctypes.c_double, i64, i64,
+            p, i64, i64,                 # sinks, key range
+            p, i64,                      # sel
+            p, p, p, ctypes.c_int]
+        lib.oracle_merge_states.restype = None
+        lib.oracle_merge_states.argtypes = [p, p, i64, i64, p, p, p]
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        _lib = lib
+    return _lib
+
+
+def _bits(t):
+    """A torch bf16/fp16 tensor as a uint16 numpy view (no copy), plus its dtype code."""
+    import torch
+    code = {torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16), code
+
+
+def _i32(t):
+    a = t.detach().cpu().numpy() if hasattr(t, "detach") else np.asarray(t)
+    assert a.dtype == np.int32
+    return a
+
+
+def decode_bits(bits: int, dtype: int) -> float:
+    lib = _load()
+    return lib.oracle_decode_bf16(bits) if dtype == BF16 else lib.oracle_decode_f16(bits)
+
+
+def decode(inputs: dict, sel=None, key_range=None, nthreads: int = 0,
+           sinks="inputs"):
+    """Reference attention for an inputs dict (see ``workloads``).
+
+    Returns (out [count, D], lse [count], lse_with_sink [count]) as float64
+    numpy arrays; ``count`` is B*Lq*Hq in row-major (row, head) order, or
+    len(sel) for an explicit list of flat indices row*Hq + head.
+    """
+    lib = _load()
+    q, k, v = inputs["q"], inputs["k_cache"], inputs["v_cache"]
+    qb, code = _bits(q)
+    kb, kcode = _bits(k)
+    vb, vcode = _bits(v)
+    assert code == kcode == vcode
+    assert qb.strides[-1] == 2 and kb.strides[-1] == 2 and vb.strides[-1] == 2
+    e = 2  # bytes per element
+    bt = _i32(inputs["block_tables"])
+    n = np.ascontiguousarray(_i32(inputs["seq_lens_kv"]))
+    assert bt.strides[1] == 4
+    s = inputs["sinks"] if isinstance(sinks, str) else sinks
+    s_arr = None if s is None else np.ascontiguousarray(
+        s.detach().cpu().numpy() if hasattr(s, "detach") else np.asarray(s), dtype=np.float32)
+    R, Hq, D = q.shape
+    B = bt.shape[0]
+    Lq = int(inputs["q_len_per_req"])
+    assert R == B * Lq
+    P, Hkv, ps, Dk = k.shape
+    assert Dk == D and tuple(v.shape) == tuple(k.shape)
+    if sel is None:
+        sel_arr, count = None, R * Hq
+    else:
+        sel_arr = np.ascontiguousarray(np.asarray(sel, dtype=np.int64))
+        count = sel_arr.size
+    out = np.empty((count, D), dtype=np.float64)
+    lse = np.empty((count,), dtype=np.float64)
+    lse_ws = np.empty((count,), dtype=np.float64)
+    klo, khi = (0, np.iinfo(np.int64).max) if key_range is None else key_range
+    ptr = lambda a: None if a is None else a.ctypes.data
+    st = lib.oracle_decode(
+        ptr(qb), qb.strides[0] // e, qb.strides[1] // e,
+        ptr(kb), kb.strides[0] // e, kb.strides[1] // e, kb.strides[2] // e,
+        ptr(vb), vb.strides[0] // e, vb.strides[1] // e, vb.strides[2] // e,
+        code, B, Hq, Hkv, D, ps, P,
+        ptr(bt), bt.strides[0] // 4, bt.shape[1],
+        ptr(n), float(inputs["scale"]), Lq, int(inputs["window_left"]),
+        ptr(s_arr), int(klo), int(khi),
+        ptr(sel_arr), count,
+        ptr(out), ptr(lse), ptr(lse_ws), int(nthreads))
+    if st != 0:
+        raise ValueError(f"oracle_decode: {_ERRORS.get(st, st)}")
+    return out, lse, lse_ws
+
+
+def merge_states(o, lse, sink=None):
+    """Merge S partial states (o [S, D], lse [S], base 2) of one row."""
+    lib = _load()
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    l = np.ascontiguousarray(lse, dtype=np.float64)
+    S, D = o.shape
+    out = np.empty((D,), dtype=np.float64)
+    res = np.empty((1,), dtype=np.float64)
+    sk = None if sink is None else np.array([sink], dtype=np.float64)
+    lib.oracle_merge_states(o.ctypes.data, l.ctypes.data, S, D,
+                            None if sk is None else sk.ctypes.data,
+                            out.ctypes.data, res.ctypes.data)
+    return out, float(res[0])

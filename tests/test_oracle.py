@@ -1,0 +1,432 @@
+"""Pins for the fp64 CPU oracle (runs without a GPU).
+
+Each test checks the oracle against something other than itself: the
+documentation's statements, closed forms, textbook identities, library routines
+(torch.softmax / torch.logsumexp in fp64 on densely gathered K/V) and
+brute force on tiny inputs.  The passages are those of
+flashinfer.cudnn.cudnn_batch_decode_with_kv_cache (Parameters, Note) and
+flashinfer.attention.prims_ts.batch_prefill (summary: causal is bottom-right
+aligned, a window keeps at most window_left + 1 keys per causal row).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import oracle
+import workloads
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+LOG2E = 1.0 / math.log(2.0)
+
+
+# ----------------------------------------------------------------------------
+# independent dense brute force built from torch library routines
+# ----------------------------------------------------------------------------
+def dense_reference(inp, with_sinks=True):
+    """Gather each request's K/V densely with torch indexing, then fp64
+    torch.softmax over an explicit boolean mask (plus an appended sink logit
+    column whose value row is zero) and torch.logsumexp * log2(e)."""
+    q = inp["q"].double()
+    k = inp["k_cache"].double()
+    v = inp["v_cache"].double()
+    bt = inp["block_tables"].long()
+    n_all = inp["seq_lens_kv"].long()
+    Lq, wl, scale = inp["q_len_per_req"], inp["window_left"], inp["scale"]
+    sinks = inp["sinks"] if with_sinks else None
+    R, Hq, D = q.shape
+    P, Hkv, ps, _ = k.shape
+    g = Hq // Hkv
+    outs = torch.zeros(R, Hq, D, dtype=torch.float64)
+    lses = torch.full((R, Hq), -math.inf, dtype=torch.float64)
+    for b in range(bt.shape[0]):
+        n = int(n_all[b])
+        j = torch.arange(n)
+        pages = bt[b, j // ps]
+        slots = j % ps
+        for h in range(Hq):
+            kvh = h // g
+            Kd = k[pages, kvh, slots]            # [n, D]
+            Vd = v[pages, kvh, slots]
+            for i in range(Lq):
+                r = b * Lq + i
+                diag = n - Lq + i
+                mask = j <= diag
+                if wl >= 0:
+                    mask &= j >= diag - wl
+                s = scale * (Kd @ q[r, h])
+                s = torch.where(mask, s, torch.tensor(-math.inf, dtype=torch.float64))
+                if not bool(mask.any()):
+                    continue
+                lses[r, h] = torch.logsumexp(s, 0) * LOG2E
+                if sinks is not None:
+                    s = torch.cat([s, torch.tensor([float(sinks[h])], dtype=torch.float64)])
+                    Vx = torch.cat([Vd, torch.zeros(1, D, dtype=torch.float64)])
+                else:
+                    Vx = Vd
+                p = torch.softmax(s, 0)
+                outs[r, h] = p @ Vx
+    return outs.reshape(R * Hq, D).numpy(), lses.reshape(-1).numpy()
+
+
+def run(inp, **kw):
+    out, lse, lse_ws = oracle.decode(inp, **kw)
+    return out, lse, lse_ws
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"inf": math.inf, "nan": math.nan}))
+
+
+def test_format_fixture():
+    gold = json.load(open(os.path.join(GOLD, "float_formats.json")))
+    for code, key in ((oracle.BF16, "bf16"), (oracle.F16, "fp16")):
+        for bits, expr in gold[key]:
+            got = oracle.decode_bits(int(bits, 16), code)
+            want = _ev(expr)
+            if math.isnan(want):
+                assert math.isnan(got), (key, bits)
+            else:
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), (key, bits, got)
+
+
+def test_formats_exhaustive_vs_library():
+    """All 65536 codes against numpy's binary16 and torch's bfloat16."""
+    codes = np.arange(65536, dtype=np.uint16)
+    f16 = codes.view(np.float16).astype(np.float64)
+    bf16 = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    for code, ref in ((oracle.F16, f16), (oracle.BF16, bf16)):
+        got = np.array([oracle.decode_bits(int(c), code) for c in codes])
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ----------------------------------------------------------------------------
+# hand-worked cases
+# ----------------------------------------------------------------------------
+def _golden_inputs(common, case):
+    dt = torch.bfloat16
+    q = torch.tensor(case["q"], dtype=torch.float32).to(dt)
+    k = torch.tensor(common["k_cache"], dtype=torch.float32).to(dt)
+    v = torch.tensor(common["v_cache"], dtype=torch.float32).to(dt)
+    return dict(q=q, k_cache=k, v_cache=v,
+                block_tables=torch.tensor(common["block_tables"], dtype=torch.int32),
+                seq_lens_kv=torch.tensor(common["seq_lens_kv"], dtype=torch.int32),
+                sinks=None if case["sinks"] is None else torch.tensor(case["sinks"], dtype=torch.float32),
+                scale=case["scale"], q_len_per_req=case["q_len_per_req"],
+                window_left=case["window_left"])
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLD, "hand_worked.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_hand_worked(case):
+    gold = json.load(open(os.path.join(GOLD, "hand_worked.json")))
+    inp = _golden_inputs(gold["common"], case)
+    out, lse, lse_ws = run(inp)
+    env = {"__builtins__": {}, "e": math.e, "log2": math.log2, "ln": math.log}
+    want_out = np.array([[eval(x, env) for x in row] for row in case["out"]], dtype=np.float64)
+    want_lse = np.array([eval(x, env) for x in case["lse"]], dtype=np.float64)
+    want_ws = np.array([eval(x, env) for x in case["lse_with_sink"]], dtype=np.float64)
+    np.testing.assert_allclose(out, want_out, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_ws, want_ws, rtol=0, atol=1e-13)
+    ref_out, ref_lse = dense_reference(inp)
+    np.testing.assert_allclose(ref_out, want_out, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# brute force over random tiny shapes
+# ----------------------------------------------------------------------------
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(B=st.integers(1, 3), g=st.sampled_from([1, 2, 3]), Hkv=st.integers(1, 2),
+       D=st.sampled_from([1, 3, 8]), ps=st.sampled_from([1, 2, 3, 5]),
+       Lq=st.integers(1, 3), wl=st.sampled_from([-1, 0, 1, 4]),
+       sinks=st.booleans(), dtype=st.sampled_from(["bf16", "fp16"]),
+       seed=st.integers(0, 10_000), data=st.data())
+def test_brute_force_tiny(B, g, Hkv, D, ps, Lq, wl, sinks, dtype, seed, data):
+    lens = data.draw(st.lists(st.integers(Lq, 12), min_size=B, max_size=B))
+    inp = workloads.make_case(B=B, Hq=g * Hkv, Hkv=Hkv, D=D, page_size=ps, seq_lens=lens,
+                              q_len_per_req=Lq, window_left=wl, sinks=sinks, dtype=dtype,
+                              seed=seed, extra_pages=2, bt_pad=1, q_pad_heads=1)
+    out, lse, _ = run(inp)
+    ref_out, ref_lse = dense_reference(inp)
+    np.testing.assert_allclose(out, ref_out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_small_configs():
+    """The tiny workload and a cut-down copy of each other workload's structure."""
+    for inp in [workloads.make_config("tiny"),
+                workloads.make_case(B=3, Hq=8, Hkv=2, D=16, page_size=4, seq_lens=(4, 9, 17),
+                                    q_len_per_req=4, seed=3),
+                workloads.make_case(B=2, Hq=8, Hkv=1, D=8, page_size=16, seq_lens=(40, 33),
+                                    window_left=7, sinks=True, dtype="fp16", value_std=0.5,
+                                    seed=4)]:
+        out, lse, _ = run(inp)
+        ref_out, ref_lse = dense_reference(inp)
+        np.testing.assert_allclose(out, ref_out, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# closed forms and invariants
+# ----------------------------------------------------------------------------
+def _case(**kw):
+    base = dict(B=2, Hq=4, Hkv=2, D=8, page_size=4, seq_lens=(7, 13), seed=11)
+    base.update(kw)
+    return workloads.make_case(**base)
+
+
+def test_lse_is_logsumexp_times_log2e():
+    """Note / LSE convention: lse = torch.logsumexp(scaled scores) * log2(e)."""
+    inp = _case(seq_lens=(30, 17), q_len_per_req=1)
+    _, lse, _ = run(inp)
+    q, bt = inp["q"].double(), inp["block_tables"].long()
+    k = inp["k_cache"].double()
+    for b, n in enumerate(inp["seq_lens_kv"].tolist()):
+        j = torch.arange(n)
+        for h in range(4):
+            kd = k[bt[b, j // 4], h // 2, j % 4]
+            s = inp["scale"] * (kd @ q[b, h])
+            want = float(torch.logsumexp(s, 0)) / math.log(2.0)
+            assert abs(lse[b * 4 + h] - want) < 1e-12
+
+
+def test_zero_query_is_mean_of_visible_values():
+    """q = 0: every visible key gets the same weight -> out = mean of visible V
+    rows and lse = log2(#visible).  With a window the count is
+    min(window_left + 1, diag + 1) (batch_prefill summary: at most
+    window_left + 1 keys per causal row)."""
+    for wl in (-1, 0, 2, 5, 100):
+        inp = _case(seq_lens=(7, 13), q_len_per_req=3, window_left=wl)
+        inp["q"] = torch.zeros_like(inp["q"])
+        out, lse, _ = run(inp)
+        bt = inp["block_tables"].long()
+        v = inp["v_cache"].double()
+        for b, n in enumerate((7, 13)):
+            for i in range(3):
+                diag = n - 3 + i
+                cnt = diag + 1 if wl < 0 else min(wl + 1, diag + 1)
+                lo = diag + 1 - cnt
+                j = torch.arange(lo, diag + 1)
+                for h in range(4):
+                    vd = v[bt[b, j // 4], h // 2, j % 4]
+                    r = (b * 3 + i) * 4 + h
+                    np.testing.assert_allclose(out[r], vd.mean(0).numpy(), atol=1e-14, rtol=0)
+                    assert abs(lse[r] - math.log2(cnt)) < 1e-13
+
+
+def test_single_visible_key():
+    """One visible key: out is that key's value row, lse = score * log2(e)."""
+    inp = _case(seq_lens=(1, 5), q_len_per_req=1, window_left=0)
+    out, lse, _ = run(inp)
+    q, k, v, bt = (inp["q"].double(), inp["k_cache"].double(), inp["v_cache"].double(),
+                   inp["block_tables"].long())
+    for b, n in enumerate((1, 5)):
+        j = n - 1
+        for h in range(4):
+            page, slot = bt[b, j // 4], j % 4
+            r = b * 4 + h
+            np.testing.assert_array_equal(out[r], v[page, h // 2, slot].numpy())
+            s = inp["scale"] * float(q[b, h] @ k[page, h // 2, slot])
+            assert abs(lse[r] - s / math.log(2)) < 1e-13
+
+
+def test_window_at_least_n_is_no_window():
+    a = _case(seq_lens=(7, 13), window_left=-1, q_len_per_req=2)
+    b = _case(seq_lens=(7, 13), window_left=12, q_len_per_req=2)
+    oa, la, _ = run(a)
+    ob, lb, _ = run(b)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_causal_row_equals_prefix_decode():
+    """Parameters / q_len_per_req: row i sees keys 0 .. n - Lq + i, i.e. it is
+    a one-token decode on the prefix of n - Lq + 1 + i keys."""
+    Lq = 4
+    for wl in (-1, 3):
+        multi = _case(B=1, seq_lens=(21,), q_len_per_req=Lq, window_left=wl, sinks=True)
+        om, lm, _ = run(multi)
+        for i in range(Lq):
+            single = dict(multi)
+            single["q"] = multi["q"][i:i + 1]
+            single["q_len_per_req"] = 1
+            single["seq_lens_kv"] = torch.tensor([21 - Lq + 1 + i], dtype=torch.int32)
+            os_, ls, _ = run(single)
+            np.testing.assert_array_equal(om[i * 4:(i + 1) * 4], os_)
+            np.testing.assert_array_equal(lm[i * 4:(i + 1) * 4], ls)
+
+
+def test_last_causal_row_is_unmasked():
+    multi = _case(B=2, seq_lens=(9, 14), q_len_per_req=3)
+    om, lm, _ = run(multi)
+    for b, n in enumerate((9, 14)):
+        single = dict(multi)
+        single["q"] = multi["q"][b * 3 + 2:b * 3 + 3]
+        single["q_len_per_req"] = 1
+        single["block_tables"] = multi["block_tables"][b:b + 1]
+        single["seq_lens_kv"] = torch.tensor([n], dtype=torch.int32)
+        os_, ls, _ = run(single)
+        r = (b * 3 + 2) * 4
+        np.testing.assert_array_equal(om[r:r + 4], os_)
+
+
+def test_gqa_equals_mha_on_repeated_heads():
+    """Note: query head h reads kv head h // (Hq / Hkv).  Repeating every kv
+    head g times gives an MHA cache with identical results."""
+    g = 3
+    inp = _case(Hq=6, Hkv=2, seq_lens=(9, 14), q_len_per_req=2, window_left=4, sinks=True)
+    o1, l1, _ = run(inp)
+    mha = dict(inp)
+    mha["k_cache"] = inp["k_cache"].repeat_interleave(g, dim=1).contiguous()
+    mha["v_cache"] = inp["v_cache"].repeat_interleave(g, dim=1).contiguous()
+    o2, l2, _ = run(mha)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_mha_head_isolation():
+    """Hq = Hkv: changing kv head 1 changes only query head 1."""
+    inp = _case(Hq=2, Hkv=2, seq_lens=(9, 14))
+    o1, _, _ = run(inp)
+    mod = dict(inp)
+    mod["k_cache"] = inp["k_cache"].clone()
+    mod["k_cache"][:, 1] = -mod["k_cache"][:, 1]
+    o2, _, _ = run(mod)
+    o1, o2 = o1.reshape(-1, 2, 8), o2.reshape(-1, 2, 8)
+    np.testing.assert_array_equal(o1[:, 0], o2[:, 0])
+    assert np.abs(o1[:, 1] - o2[:, 1]).max() > 1e-3
+
+
+def test_page_permutation_invariance():
+    """Permuting physical pages and rewriting block_tables leaves every output
+    unchanged (Parameters / block_tables: the table is the only page map)."""
+    inp = _case(seq_lens=(7, 13), q_len_per_req=2, window_left=3, sinks=True, extra_pages=4)
+    o1, l1, w1 = run(inp)
+    P = inp["k_cache"].shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(P)
+    moved = dict(inp)
+    moved["k_cache"] = inp["k_cache"][perm].contiguous()     # new page x holds old page perm[x]
+    moved["v_cache"] = inp["v_cache"][perm].contiguous()
+    moved["block_tables"] = inv[inp["block_tables"].long()].to(torch.int32)
+    o2, l2, w2 = run(moved)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(w1, w2)
+
+
+def test_page_size_repack_invariance():
+    """The same logical keys stored with page sizes 1, 4 and 16 give identical
+    results (key j lives in page j // page_size, slot j % page_size)."""
+    base = _case(page_size=16, seq_lens=(7, 13), q_len_per_req=2, window_left=5, sinks=True)
+    o1, l1, _ = run(base)
+    bt = base["block_tables"].long()
+    for ps in (1, 4):
+        ks, vs, rows = [], [], []
+        for b, n in enumerate((7, 13)):
+            j = torch.arange(n)
+            kd = base["k_cache"][bt[b, j // 16], :, j % 16]     # [n, Hkv, D]
+            vd = base["v_cache"][bt[b, j // 16], :, j % 16]
+            npg = -(-n // ps)
+            pad = npg * ps - n
+            kd = torch.cat([kd, torch.zeros(pad, *kd.shape[1:], dtype=kd.dtype)])
+            vd = torch.cat([vd, torch.zeros(pad, *vd.shape[1:], dtype=vd.dtype)])
+            ks.append(kd.view(npg, ps, *kd.shape[1:]).transpose(1, 2))
+            vs.append(vd.view(npg, ps, *vd.shape[1:]).transpose(1, 2))
+            rows.append(npg)
+        k = torch.cat(ks).contiguous()
+        v = torch.cat(vs).contiguous()
+        C = max(rows)
+        table = torch.zeros((2, C), dtype=torch.int32)
+        off = 0
+        for b, npg in enumerate(rows):
+            table[b, :npg] = torch.arange(off, off + npg, dtype=torch.int32)
+            off += npg
+        rep = dict(base, k_cache=k, v_cache=v, block_tables=table)
+        o2, l2, _ = run(rep)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_sink_is_extra_logit_with_zero_value():
+    """Parameters / sinks: out_sink = out_nosink * S / (S + e^sink) with
+    S = 2^lse (keys only); lse is unchanged; lse_with_sink = log2(S + e^sink)."""
+    inp = _case(seq_lens=(7, 13), q_len_per_req=2, window_left=4, sinks=True)
+    o_s, l_s, w_s = run(inp)
+    o_n, l_n, w_n = run(inp, sinks=None)
+    np.testing.assert_array_equal(l_s, l_n)
+    np.testing.assert_array_equal(l_n, w_n)
+    Hq = 4
+    sink = np.tile(inp["sinks"].double().numpy(), o_s.shape[0] // Hq)
+    S = np.exp2(l_n)
+    factor = S / (S + np.exp(sink))
+    np.testing.assert_allclose(o_s, o_n * factor[:, None], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(w_s, np.log2(S + np.exp(sink)), rtol=1e-13, atol=1e-13)
+
+
+def test_sink_limits():
+    inp = _case(seq_lens=(7, 13), sinks=True)
+    o_n, _, _ = run(inp, sinks=None)
+    o_lo, _, _ = run(inp, sinks=torch.full((4,), -1e30))
+    np.testing.assert_array_equal(o_lo, o_n)
+    o_hi, _, _ = run(inp, sinks=torch.full((4,), 80.0))
+    assert np.abs(o_hi).max() < 1e-25
+
+
+def test_merge_of_disjoint_ranges_equals_union():
+    """Note / LSE convention: base-2 LSE states of disjoint key ranges merge
+    (cascade merge) to the state of their union, sinks applied once."""
+    inp = _case(seq_lens=(29, 31), q_len_per_req=2, window_left=-1, sinks=True)
+    o_full, l_full, _ = run(inp)
+    cuts = [0, 5, 11, 12, 30, 1 << 40]
+    parts = [run(inp, key_range=(a, b), sinks=None) for a, b in zip(cuts[:-1], cuts[1:])]
+    sinks = inp["sinks"].double().numpy()
+    for idx in range(o_full.shape[0]):
+        o = np.stack([p[0][idx] for p in parts])
+        l = np.array([p[1][idx] for p in parts])
+        mo, ml = oracle.merge_states(o, l, sink=sinks[idx % 4])
+        np.testing.assert_allclose(mo, o_full[idx], rtol=1e-12, atol=1e-14)
+        assert abs(ml - l_full[idx]) < 1e-12
+
+
+def test_empty_rows_are_zero_and_minus_inf():
+    """Out of contract (n < q_len_per_req): rows with no visible key give
+    out = 0 and lse = -inf, never NaN."""
+    inp = _case(B=2, seq_lens=(1, 6), q_len_per_req=3)
+    out, lse, _ = run(inp)
+    rows = out.reshape(2, 3, 4, 8)
+    l = lse.reshape(2, 3, 4)
+    assert np.all(rows[0, :2] == 0) and np.all(np.isneginf(l[0, :2]))
+    assert np.all(np.isfinite(l[0, 2])) and np.all(np.isfinite(l[1]))
+
+
+def test_selected_rows_match_full():
+    inp = _case(seq_lens=(7, 13), q_len_per_req=2, sinks=True)
+    o, l, w = run(inp)
+    sel = [15, 0, 3, 9]
+    o2, l2, w2 = run(inp, sel=sel)
+    np.testing.assert_array_equal(o[sel], o2)
+    np.testing.assert_array_equal(l[sel], l2)
+
+
+def test_poison_never_read():
+    """NaN in every slot past a request's length, in unused pages and in a
+    page that padding columns point to: the oracle never dereferences them."""
+    clean = workloads.make_config("tiny")
+    bad = workloads.make_config("tiny", poison=True)
+    o1, l1, _ = run(clean)
+    o2, l2, _ = run(bad)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
