@@ -1,0 +1,338 @@
+// api.cpp -- C ABI of the paged-KV decode library: argument validation,
+// shape-only launch planning, the split-KV workspace and kernel launches.
+//
+// Planning never reads device data (sequence lengths stay on the device), so
+// a call is safe to capture in a HIP graph once its workspace exists; this is
+// the capture-safe alternative to a planner that reads the lengths on the host
+// (flashinfer.attention.prims_ts.batch_decode_with_paged_kv_cache, summary).
+#include "pkvd.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "decode_args.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct Shapes {
+  int64_t R, Hq, D, P, Hkv, ps, B, C;
+  bool bf16;
+};
+
+struct Plan {
+  int path;          // pkvd::kPathValu or pkvd::kPathMfma
+  int rows_per_tile;
+  int row_tiles;
+  int splits;
+  int split_blocks;
+  int64_t workgroups;
+  size_t ws_bytes;
+};
+
+// Shape checks shared by every entry point.  Returns PKVD_OK or an error.
+int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* bt,
+                 int32_t Lq, int32_t wl, Shapes* s) {
+  if (!q || !k || !bt) return fail(PKVD_ERR_INVALID_ARG, "q, k_cache and block_tables are required");
+  if (q->ndim != 3) return fail(PKVD_ERR_INVALID_ARG, "q must be 3-D (B*q_len_per_req, Hq, D)");
+  if (q->dtype != PKVD_BF16 && q->dtype != PKVD_F16)
+    return fail(PKVD_ERR_INVALID_ARG, "q must be bf16 or fp16");
+  if (k->ndim != 4) return fail(PKVD_ERR_INVALID_ARG, "k_cache must be 4-D (pages, Hkv, page_size, D)");
+  if (bt->ndim != 2 || bt->dtype != PKVD_I32)
+    return fail(PKVD_ERR_INVALID_ARG, "block_tables must be a 2-D int32 tensor (B, C)");
+  if (Lq < 1) return fail(PKVD_ERR_INVALID_ARG, "q_len_per_req must be >= 1");
+  if (wl < -1) return fail(PKVD_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
+  s->R = q->shape[0];
+  s->Hq = q->shape[1];
+  s->D = q->shape[2];
+  s->P = k->shape[0];
+  s->Hkv = k->shape[1];
+  s->ps = k->shape[2];
+  s->B = bt->shape[0];
+  s->C = bt->shape[1];
+  s->bf16 = q->dtype == PKVD_BF16;
+  if (s->R < 1 || s->Hq < 1 || s->D < 1 || s->P < 1 || s->Hkv < 1 || s->ps < 1 || s->B < 1 ||
+      s->C < 1)
+    return fail(PKVD_ERR_INVALID_ARG, "every dimension must be >= 1");
+  if (k->shape[3] != s->D) return fail(PKVD_ERR_INVALID_ARG, "k_cache head_dim differs from q");
+  if (s->R != s->B * Lq)
+    return fail(PKVD_ERR_INVALID_ARG, "q.shape[0]=%lld is not B*q_len_per_req=%lld",
+                (long long)s->R, (long long)(s->B * Lq));
+  if (s->Hq % s->Hkv)
+    return fail(PKVD_ERR_INVALID_ARG, "num_heads_qo=%lld is not a multiple of num_heads_kv=%lld",
+                (long long)s->Hq, (long long)s->Hkv);
+  if (s->D != 64 && s->D != 128)
+    return fail(PKVD_ERR_UNSUPPORTED, "head_dim=%lld not built (64 and 128 are)", (long long)s->D);
+  if (s->ps > 256) return fail(PKVD_ERR_UNSUPPORTED, "page_size=%lld > 256", (long long)s->ps);
+  if (s->B > 65535 || s->P > INT32_MAX || s->C * s->ps > (1LL << 30) ||
+      s->R * s->Hq > (1LL << 30) || s->Hq > 65535)
+    return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
+  return PKVD_OK;
+}
+
+Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
+  Plan p{};
+  const int64_t g = s.Hq / s.Hkv;
+  const int64_t R = g * Lq;
+  int forced = env_int("PKVD_FORCE_PATH", -1);
+  if (forced != pkvd::kPathValu) forced = -1;   // only the VALU path is built so far
+  p.path = pkvd::kPathValu;
+  p.rows_per_tile = R <= 4 ? 4 : 8;
+  p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
+
+  int64_t kcap = s.C * s.ps;
+  if (wl >= 0) kcap = std::min<int64_t>(kcap, (int64_t)wl + Lq);
+  const int64_t max_blocks = (kcap + pkvd::kBlockKeys - 1) / pkvd::kBlockKeys + 1;
+  const int64_t units = s.B * s.Hkv * p.row_tiles;
+  const int64_t target = std::max(1, env_int("PKVD_TARGET_WGS", 2048));
+  const int64_t min_blocks = std::max(1, env_int("PKVD_MIN_SPLIT_BLOCKS", 8));
+  int64_t S = (target + units - 1) / units;
+  S = std::min(S, (max_blocks + min_blocks - 1) / min_blocks);
+  const int forced_s = env_int("PKVD_NUM_SPLITS", 0);
+  if (forced_s > 0) S = forced_s;
+  S = std::max<int64_t>(1, std::min(S, max_blocks));
+  int64_t sb = (max_blocks + S - 1) / S;
+  S = (max_blocks + sb - 1) / sb;
+  if (S == 1) sb = max_blocks;
+  p.splits = (int)S;
+  p.split_blocks = (int)sb;
+  p.workgroups = S * s.Hkv * p.row_tiles * s.B;
+  const int64_t NR = s.R * s.Hq;
+  p.ws_bytes = S > 1 ? (size_t)(S * NR * (s.D + 1) * 4 + 256) : 0;
+  return p;
+}
+
+// Library-owned split-KV workspace, one per device.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+Workspace g_ws[64];
+
+int ensure_workspace(size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PKVD_ERR_HIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      // hipFree waits for work that may still read the old buffer
+      e = hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    e = hipMalloc(&w.ptr, bytes);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      return fail(PKVD_ERR_WORKSPACE, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return PKVD_OK;
+}
+
+bool contiguous(const pkvd_tensor* t) {
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->strides[i] != expect) return false;
+    expect *= t->shape[i];
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkvd_version(void) { return "0.1.0"; }
+
+const char* pkvd_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkvd_status_string(int status) {
+  switch (status) {
+    case PKVD_OK: return "ok";
+    case PKVD_ERR_INVALID_ARG: return "invalid argument";
+    case PKVD_ERR_UNSUPPORTED: return "unsupported";
+    case PKVD_ERR_WORKSPACE: return "workspace allocation failed";
+    case PKVD_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                     const pkvd_tensor* block_tables, int32_t q_len_per_req, int32_t window_left,
+                     int64_t out[6]) {
+  Shapes s;
+  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
+  if (st != PKVD_OK) return st;
+  if (!out) return fail(PKVD_ERR_INVALID_ARG, "out is NULL");
+  Plan p = make_plan(s, q_len_per_req, window_left);
+  out[0] = p.path;
+  out[1] = p.rows_per_tile;
+  out[2] = p.row_tiles;
+  out[3] = p.splits;
+  out[4] = p.split_blocks;
+  out[5] = p.workgroups;
+  return PKVD_OK;
+}
+
+int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                                const pkvd_tensor* block_tables, int32_t q_len_per_req,
+                                int32_t window_left, size_t* bytes) {
+  Shapes s;
+  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
+  if (st != PKVD_OK) return st;
+  if (!bytes) return fail(PKVD_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_plan(s, q_len_per_req, window_left).ws_bytes;
+  return PKVD_OK;
+}
+
+int pkvd_reserve_workspace(size_t bytes) {
+  void* p = nullptr;
+  g_last_error.clear();
+  if (bytes == 0) return PKVD_OK;
+  return ensure_workspace(bytes, &p);
+}
+
+int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_tensor* v_cache,
+                const pkvd_tensor* block_tables, const pkvd_tensor* seq_lens_kv, float scale,
+                int32_t q_len_per_req, int32_t window_left, const pkvd_tensor* sinks,
+                pkvd_tensor* out, pkvd_tensor* lse, void* stream) {
+  g_last_error.clear();
+  Shapes s;
+  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
+  if (st != PKVD_OK) return st;
+  const pkvd_tensor* k = k_cache;
+  const pkvd_tensor* v = v_cache;
+  if (!v || !seq_lens_kv || !out) return fail(PKVD_ERR_INVALID_ARG, "v_cache, seq_lens_kv and out are required");
+  if (!q->data || !k->data || !v->data || !block_tables->data || !seq_lens_kv->data || !out->data)
+    return fail(PKVD_ERR_INVALID_ARG, "NULL data pointer");
+  if (!isfinite(scale)) return fail(PKVD_ERR_INVALID_ARG, "scale must be finite");
+  // q: head_dim innermost and dense, rows 16-byte aligned
+  if (q->strides[2] != 1) return fail(PKVD_ERR_INVALID_ARG, "q must have head_dim innermost and dense");
+  if (!aligned16(q->data) || q->strides[0] % 8 || q->strides[1] % 8)
+    return fail(PKVD_ERR_INVALID_ARG, "q rows must start 16-byte aligned");
+  // K / V
+  for (const pkvd_tensor* t : {k, v}) {
+    const char* nm = t == k ? "k_cache" : "v_cache";
+    if (t->ndim != 4 || t->dtype != q->dtype)
+      return fail(PKVD_ERR_INVALID_ARG, "%s must be 4-D with q's dtype", nm);
+    if (t->shape[0] != s.P || t->shape[1] != s.Hkv || t->shape[2] != s.ps || t->shape[3] != s.D)
+      return fail(PKVD_ERR_INVALID_ARG, "k_cache and v_cache shapes differ");
+    if (t->strides[3] != 1 || (s.ps > 1 && t->strides[2] != s.D))
+      return fail(PKVD_ERR_INVALID_ARG, "%s pages must hold contiguous [page_size, head_dim] tiles", nm);
+    if (!aligned16(t->data) || t->strides[0] % 8 || t->strides[1] % 8)
+      return fail(PKVD_ERR_INVALID_ARG, "%s tiles must be 16-byte aligned", nm);
+    if (t->strides[0] < 0 || t->strides[1] < 0)
+      return fail(PKVD_ERR_INVALID_ARG, "%s strides must be non-negative", nm);
+  }
+  if (s.Hq / s.Hkv < 1) return fail(PKVD_ERR_INVALID_ARG, "num_heads_qo < num_heads_kv");
+  // tables
+  if (block_tables->strides[1] != 1 || block_tables->strides[0] < s.C)
+    return fail(PKVD_ERR_INVALID_ARG, "block_tables rows must be contiguous and not overlap");
+  if (seq_lens_kv->ndim != 1 || seq_lens_kv->dtype != PKVD_I32 || seq_lens_kv->shape[0] != s.B ||
+      (s.B > 1 && seq_lens_kv->strides[0] != 1))
+    return fail(PKVD_ERR_INVALID_ARG, "seq_lens_kv must be a contiguous int32 (B,) tensor");
+  if (sinks) {
+    if (!sinks->data || sinks->ndim != 1 || sinks->dtype != PKVD_F32 || sinks->shape[0] != s.Hq ||
+        (s.Hq > 1 && sinks->strides[0] != 1))
+      return fail(PKVD_ERR_INVALID_ARG, "sinks must be a contiguous float32 (num_heads_qo,) tensor");
+  }
+  if (out->ndim != 3 || out->dtype != q->dtype || out->shape[0] != s.R || out->shape[1] != s.Hq ||
+      out->shape[2] != s.D || !contiguous(out))
+    return fail(PKVD_ERR_INVALID_ARG, "out must be contiguous (B*q_len_per_req, Hq, D) with q's dtype");
+  if (lse) {
+    if (!lse->data || lse->ndim != 2 || lse->dtype != PKVD_F32 || lse->shape[0] != s.R ||
+        lse->shape[1] != s.Hq || !contiguous(lse))
+      return fail(PKVD_ERR_INVALID_ARG, "lse must be contiguous float32 (B*q_len_per_req, Hq)");
+  }
+
+  const Plan p = make_plan(s, q_len_per_req, window_left);
+  pkvd::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_sr = q->strides[0];
+  a.q_sh = q->strides[1];
+  a.k = static_cast<const uint16_t*>(k->data);
+  a.k_sp = k->strides[0];
+  a.k_sh = k->strides[1];
+  a.v = static_cast<const uint16_t*>(v->data);
+  a.v_sp = v->strides[0];
+  a.v_sh = v->strides[1];
+  a.bt = static_cast<const int32_t*>(block_tables->data);
+  a.bt_sr = block_tables->strides[0];
+  a.seq_lens = static_cast<const int32_t*>(seq_lens_kv->data);
+  a.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
+  a.out = static_cast<uint16_t*>(out->data);
+  a.lse = lse ? static_cast<float*>(lse->data) : nullptr;
+  a.B = (int32_t)s.B;
+  a.Hq = (int32_t)s.Hq;
+  a.Hkv = (int32_t)s.Hkv;
+  a.g = (int32_t)(s.Hq / s.Hkv);
+  a.Lq = q_len_per_req;
+  a.ps = (int32_t)s.ps;
+  a.P = (int32_t)s.P;
+  a.C = (int32_t)s.C;
+  a.window_left = window_left;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.num_splits = p.splits;
+  a.split_blocks = p.split_blocks;
+  a.row_tiles = p.row_tiles;
+  if (p.splits > 1) {
+    void* ws = nullptr;
+    st = ensure_workspace(p.ws_bytes, &ws);
+    if (st != PKVD_OK) return st;
+    const int64_t NR = s.R * s.Hq;
+    a.ws_lse = static_cast<float*>(ws);
+    // partial outputs start 256-byte aligned after the LSE block
+    uintptr_t o = reinterpret_cast<uintptr_t>(a.ws_lse + p.splits * NR);
+    o = (o + 255) & ~uintptr_t(255);
+    a.ws_o = reinterpret_cast<float*>(o);
+  }
+  if (env_int("PKVD_LOG", 0))
+    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d splits=%d blocks/split=%d wgs=%lld\n",
+            p.path, p.rows_per_tile, p.row_tiles, p.splits, p.split_blocks,
+            (long long)p.workgroups);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, (int)s.D, s.bf16, hs);
+  if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (p.splits > 1) {
+    e = pkvd::launch_merge(a, (int)s.D, s.bf16, hs);
+    if (e != hipSuccess) return fail(PKVD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  }
+  return PKVD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// decode_args.h -- launch arguments shared by the host planner (api.cpp) and
+// the device kernels (decode_kernels.hip).  Internal; not part of the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace pkvd {
+
+constexpr int kBlockKeys = 16;   // keys per block: the unit a wave loads and scores
+constexpr int kWaves = 4;        // waves per workgroup of the decode kernels
+constexpr int kThreads = 64 * kWaves;
+
+enum Path : int { kPathValu = 0, kPathMfma = 1 };
+
+struct DecodeArgs {
+  // inputs (element strides)
+  const uint16_t* q;
+  int64_t q_sr, q_sh;              // q[r * q_sr + h * q_sh + d]
+  const uint16_t* k;
+  int64_t k_sp, k_sh;              // k[page * k_sp + kvh * k_sh + slot * D + d]
+  const uint16_t* v;
+  int64_t v_sp, v_sh;
+  const int32_t* bt;
+  int64_t bt_sr;                   // bt[b * bt_sr + c]
+  const int32_t* seq_lens;
+  const float* sinks;              // nullptr: no sinks
+  // outputs
+  uint16_t* out;                   // contiguous (B * Lq, Hq, D)
+  float* lse;                      // nullptr: not requested
+  float* ws_o;                     // split partials [S][B * Lq * Hq][D]   (S > 1)
+  float* ws_lse;                   // [S][B * Lq * Hq]
+  // shapes
+  int32_t B, Hq, Hkv, g, Lq, ps, P, C;
+  int32_t window_left;
+  float scale_log2;                // scale * log2(e): scores are kept in base 2
+  int32_t num_splits;              // S
+  int32_t split_blocks;            // 16-key blocks per split
+  int32_t row_tiles;               // row tiles per (request, kv head)
+};
+
+// Launchers (decode_kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, int head_dim,
+                         bool bf16, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+
+}  // namespace pkvd
