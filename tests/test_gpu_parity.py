@@ -169,7 +169,9 @@ def test_edge_sweep(case, splits):
         out, lse = run_gpu(to_dev(inp))
     finally:
         os.environ.pop("PKVD_NUM_SPLITS", None)
-    compare(_edge_id(case), out, lse, ref_out, ref_lse)
+    # outputs far above 1 (value_std > 1) carry bf16 rounding of up to 2^-8 |out|
+    atol = max(OUT_ATOL, 2.0 ** -7 * float(np.abs(ref_out).max()))
+    compare(_edge_id(case), out, lse, ref_out, ref_lse, out_atol=atol)
 
 
 def test_combined_kv_tensor():
