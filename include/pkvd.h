@@ -27,8 +27,8 @@
  *     the contract forbids) yields out = 0 and lse = -inf.
  *
  * Threading: calls may come from any host thread.  Calls that can overlap on
- * one device share that device's split-KV workspace and must be ordered by
- * the caller (same stream, or events between streams).
+ * one device share that device's workspace and must be ordered by the caller
+ * (same stream, or events between streams).
  */
 #ifndef PKVD_H_
 #define PKVD_H_
@@ -102,10 +102,13 @@ typedef struct {
  *                (Note / LSE convention).
  *   stream       hipStream_t (passed as void*); NULL = the default stream.
  *
- * Supported: D in {64, 128}; 1 <= page_size <= 256; Hq % Hkv == 0.
+ * Supported: D in {64, 128}; 1 <= page_size <= 256; Hq % Hkv == 0;
+ * B <= 8192 requests.
  * Work is only enqueued; the call never synchronises and never reads device
- * data on the host.  A split-KV workspace is allocated on the first call that
- * needs it (and grown later if needed); see pkvd_reserve_workspace.
+ * data on the host: one persistent kernel splits the total work evenly over
+ * its waves from seq_lens_kv on the device.  A workspace for the partial
+ * states of units cut between waves is allocated on the first call (and
+ * grown later if needed); see pkvd_reserve_workspace.
  * Errors: PKVD_ERR_INVALID_ARG / PKVD_ERR_UNSUPPORTED are detected before any
  * HIP call; the message is available from pkvd_last_error().
  */
@@ -115,8 +118,9 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
                 pkvd_tensor* out, pkvd_tensor* lse, void* stream);
 
 /*
- * pkvd_decode_workspace_bytes -- bytes of split-KV workspace the plan for
- * these shapes needs on the current device (0 when no split is used).  Same
+ * pkvd_decode_workspace_bytes -- bytes of workspace (partial states, two per
+ * wave of the persistent grid) the plan for these shapes needs on the current
+ * device.  Same
  * arguments as pkvd_decode minus the data; only shapes are read.  Returns
  * a status; the size is written to *bytes.
  */
@@ -135,8 +139,10 @@ int pkvd_reserve_workspace(size_t bytes);
 /*
  * pkvd_decode_plan -- the launch plan pkvd_decode would use for these shapes:
  * out[0] = path (0 = VALU dot products, 1 = MFMA), out[1] = rows per tile,
- * out[2] = row tiles per (request, kv head), out[3] = KV splits,
- * out[4] = 16-key blocks per split, out[5] = workgroups of the decode kernel.
+ * out[2] = row tiles per (request, kv head), out[3] = waves of the persistent
+ * grid, out[4] = minimum 16-key blocks per participating wave,
+ * out[5] = workgroups of the decode kernel.  With no device present the plan
+ * assumes an MI355X (256 CUs, two workgroups per CU).
  */
 int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
                      const pkvd_tensor* block_tables, int32_t q_len_per_req,

@@ -23,7 +23,8 @@ __all__ = ["decode", "plan", "workspace_bytes", "reserve_workspace", "library_pa
            "PkvdError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpkvd.so")
+# PKVD_LIBRARY selects another build of the same library (A/B comparisons)
+_LIB_PATH = os.environ.get("PKVD_LIBRARY") or os.path.join(_HERE, "libpkvd.so")
 
 _BF16, _F16, _F32, _I32 = 0, 1, 2, 3
 _DT = {torch.bfloat16: _BF16, torch.float16: _F16, torch.float32: _F32, torch.int32: _I32}
@@ -149,7 +150,7 @@ def plan(q, k_cache, block_tables, q_len_per_req: int = 1, window_left: int = -1
     res = (ctypes.c_int64 * 6)()
     _check(_lib.pkvd_decode_plan(_ref(_desc(q)), _ref(_desc(k_cache)), _ref(_desc(block_tables)),
                                  int(q_len_per_req), int(window_left), ctypes.byref(res)))
-    keys = ("path", "rows_per_tile", "row_tiles", "splits", "split_blocks", "workgroups")
+    keys = ("path", "rows_per_tile", "row_tiles", "waves", "min_wave_blocks", "workgroups")
     d = dict(zip(keys, list(res)))
     d["path"] = {0: "valu", 1: "mfma"}[d["path"]]
     return d

@@ -49,13 +49,14 @@ struct Shapes {
 };
 
 struct Plan {
-  int path;          // pkvd::kPathValu or pkvd::kPathMfma
+  int path;             // pkvd::kPathValu or pkvd::kPathMfma; -1: not plannable
   int rows_per_tile;
   int row_tiles;
-  int splits;
-  int split_blocks;
+  int num_waves;        // waves of the persistent grid
+  int min_wave_blocks;  // minimum 16-key blocks per participating wave
   int64_t workgroups;
-  size_t ws_bytes;
+  size_t ws_bytes;      // partial states: 2 slots per wave
+  int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
 };
 
 // Shape checks shared by every entry point.  Returns PKVD_OK or an error.
@@ -92,53 +93,93 @@ int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* 
   if (s->D != 64 && s->D != 128)
     return fail(PKVD_ERR_UNSUPPORTED, "head_dim=%lld not built (64 and 128 are)", (long long)s->D);
   if (s->ps > 256) return fail(PKVD_ERR_UNSUPPORTED, "page_size=%lld > 256", (long long)s->ps);
-  if (s->B > 65535 || s->P > INT32_MAX || s->C * s->ps > (1LL << 30) ||
-      s->R * s->Hq > (1LL << 30) || s->Hq > 65535)
+  if (s->B > pkvd::kMaxBatch)
+    return fail(PKVD_ERR_UNSUPPORTED, "batch of %lld requests > %d", (long long)s->B,
+                pkvd::kMaxBatch);
+  if (s->P > INT32_MAX || s->C * s->ps > (1LL << 30) || s->R * s->Hq > (1LL << 30) ||
+      s->Hq > 65535)
     return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
   return PKVD_OK;
+}
+
+// CUs of the current device and resident workgroups per CU for a kernel; an
+// MI355X (256 CUs, 2 workgroups per CU) is assumed when no device answers.
+struct DeviceFit {
+  int cus = 256;
+  int blocks_per_cu = 2;
+};
+
+DeviceFit device_fit(int path, int rt, const Shapes& s) {
+  DeviceFit f;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return f;
+  }
+  static std::mutex mu;
+  static int cached_cus[64] = {0};
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64) {
+    if (!cached_cus[dev]) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+          n > 0)
+        cached_cus[dev] = n;
+      else
+        (void)hipGetLastError();
+    }
+    if (cached_cus[dev]) f.cus = cached_cus[dev];
+  }
+  const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
+  const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
+                                           pkvd::decode_lds_bytes((int)s.B));
+  if (n > 0) f.blocks_per_cu = n;
+  else (void)hipGetLastError();
+  return f;
 }
 
 Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   Plan p{};
   const int64_t g = s.Hq / s.Hkv;
   const int64_t R = g * Lq;
-  int forced = env_int("PKVD_FORCE_PATH", -1);
-  if (forced != pkvd::kPathValu) forced = -1;   // only the VALU path is built so far
   p.path = pkvd::kPathValu;
   p.rows_per_tile = R <= 4 ? 4 : 8;
   p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
+  p.units = s.B * s.Hkv * p.row_tiles;
 
+  // the linear block space must fit int32: units * blocks per unit
   int64_t kcap = s.C * s.ps;
   if (wl >= 0) kcap = std::min<int64_t>(kcap, (int64_t)wl + Lq);
   const int64_t max_blocks = (kcap + pkvd::kBlockKeys - 1) / pkvd::kBlockKeys + 1;
-  const int64_t units = s.B * s.Hkv * p.row_tiles;
-  const int64_t target = std::max(1, env_int("PKVD_TARGET_WGS", 2048));
-  const int64_t min_blocks = std::max(1, env_int("PKVD_MIN_SPLIT_BLOCKS", 8));
-  int64_t S = (target + units - 1) / units;
-  S = std::min(S, (max_blocks + min_blocks - 1) / min_blocks);
-  const int forced_s = env_int("PKVD_NUM_SPLITS", 0);
-  if (forced_s > 0) S = forced_s;
-  S = std::max<int64_t>(1, std::min(S, max_blocks));
-  int64_t sb = (max_blocks + S - 1) / S;
-  S = (max_blocks + sb - 1) / sb;
-  if (S == 1) sb = max_blocks;
-  p.splits = (int)S;
-  p.split_blocks = (int)sb;
-  p.workgroups = S * s.Hkv * p.row_tiles * s.B;
-  const int64_t NR = s.R * s.Hq;
-  p.ws_bytes = S > 1 ? (size_t)(S * NR * (s.D + 1) * 4 + 256) : 0;
+  if (p.units * max_blocks >= INT32_MAX) return Plan{-1};
+
+  const DeviceFit f = device_fit(p.path, p.rows_per_tile, s);
+  int64_t nw = (int64_t)f.cus * f.blocks_per_cu * pkvd::kWaves;
+  const int forced = env_int("PKVD_WAVES", 0);
+  if (forced > 0) nw = forced;
+  p.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 8));
+  // no more waves than the largest possible work can occupy
+  nw = std::min<int64_t>(nw, (p.units * max_blocks + p.min_wave_blocks - 1) / p.min_wave_blocks);
+  nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
+  p.num_waves = (int)nw;
+  p.workgroups = (nw + pkvd::kWaves - 1) / pkvd::kWaves;
+  p.ws_bytes = (size_t)(2 * nw * p.rows_per_tile * (s.D + 1) * 4 + 256);
   return p;
 }
 
-// Library-owned split-KV workspace, one per device.
+// Library-owned split-KV workspace, one per device: fp32 partial states and
+// the per-unit arrival counters.  Counters are zeroed when allocated and every
+// call leaves them at zero (the last split of a unit resets its counter).
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  int32_t* counters = nullptr;
+  int64_t n_counters = 0;
 };
 std::mutex g_ws_mutex;
 Workspace g_ws[64];
 
-int ensure_workspace(size_t bytes, void** out) {
+int ensure_workspace(size_t bytes, int64_t n_counters, void** out, int32_t** counters) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -147,8 +188,7 @@ int ensure_workspace(size_t bytes, void** out) {
   Workspace& w = g_ws[dev];
   if (w.bytes < bytes) {
     if (w.ptr) {
-      // hipFree waits for work that may still read the old buffer
-      e = hipFree(w.ptr);
+      e = hipFree(w.ptr);   // waits for work that may still use the old buffer
       w.ptr = nullptr;
       w.bytes = 0;
       if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
@@ -160,7 +200,26 @@ int ensure_workspace(size_t bytes, void** out) {
     }
     w.bytes = bytes;
   }
+  if (w.n_counters < n_counters) {
+    if (w.counters) {
+      e = hipFree(w.counters);
+      w.counters = nullptr;
+      w.n_counters = 0;
+      if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    const int64_t n = std::max<int64_t>(n_counters, 1024);
+    e = hipMalloc(reinterpret_cast<void**>(&w.counters), (size_t)n * sizeof(int32_t));
+    if (e != hipSuccess) {
+      w.counters = nullptr;
+      return fail(PKVD_ERR_WORKSPACE, "hipMalloc(counters): %s", hipGetErrorString(e));
+    }
+    e = hipMemset(w.counters, 0, (size_t)n * sizeof(int32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipMemset(counters): %s", hipGetErrorString(e));
+    w.n_counters = n;
+  }
   *out = w.ptr;
+  *counters = w.counters;
   return PKVD_OK;
 }
 
@@ -200,11 +259,12 @@ int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
   if (st != PKVD_OK) return st;
   if (!out) return fail(PKVD_ERR_INVALID_ARG, "out is NULL");
   Plan p = make_plan(s, q_len_per_req, window_left);
+  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
   out[0] = p.path;
   out[1] = p.rows_per_tile;
   out[2] = p.row_tiles;
-  out[3] = p.splits;
-  out[4] = p.split_blocks;
+  out[3] = p.num_waves;
+  out[4] = p.min_wave_blocks;
   out[5] = p.workgroups;
   return PKVD_OK;
 }
@@ -216,15 +276,21 @@ int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache
   int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
   if (st != PKVD_OK) return st;
   if (!bytes) return fail(PKVD_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = make_plan(s, q_len_per_req, window_left).ws_bytes;
+  const Plan p = make_plan(s, q_len_per_req, window_left);
+  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
+  *bytes = p.ws_bytes;
   return PKVD_OK;
 }
 
 int pkvd_reserve_workspace(size_t bytes) {
   void* p = nullptr;
+  int32_t* c = nullptr;
   g_last_error.clear();
   if (bytes == 0) return PKVD_OK;
-  return ensure_workspace(bytes, &p);
+  // counters: one per (request, kv head, row tile).  A plan whose partials
+  // fit in `bytes` has at least 2 splits of >= 65 floats per unit, so it
+  // needs at most bytes / 520 counters.
+  return ensure_workspace(bytes, (int64_t)(bytes / 512 + 1024), &p, &c);
 }
 
 int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_tensor* v_cache,
@@ -281,6 +347,7 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   }
 
   const Plan p = make_plan(s, q_len_per_req, window_left);
+  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
   pkvd::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
   a.q_sr = q->strides[0];
@@ -307,31 +374,30 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   a.C = (int32_t)s.C;
   a.window_left = window_left;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.num_splits = p.splits;
-  a.split_blocks = p.split_blocks;
+  a.D = (int32_t)s.D;
   a.row_tiles = p.row_tiles;
-  if (p.splits > 1) {
-    void* ws = nullptr;
-    st = ensure_workspace(p.ws_bytes, &ws);
-    if (st != PKVD_OK) return st;
-    const int64_t NR = s.R * s.Hq;
-    a.ws_lse = static_cast<float*>(ws);
-    // partial outputs start 256-byte aligned after the LSE block
-    uintptr_t o = reinterpret_cast<uintptr_t>(a.ws_lse + p.splits * NR);
-    o = (o + 255) & ~uintptr_t(255);
-    a.ws_o = reinterpret_cast<float*>(o);
+  a.num_waves = p.num_waves;
+  a.min_wave_blocks = p.min_wave_blocks;
+#ifdef PKVD_TRACE
+  {
+    const char* t = getenv("PKVD_TRACE_PTR");   // device buffer of >= waves * 16 uint64
+    a.trace = t ? reinterpret_cast<uint64_t*>(strtoull(t, nullptr, 0)) : nullptr;
   }
+#endif
+  void* ws = nullptr;
+  st = ensure_workspace(p.ws_bytes, p.units, &ws, &a.counters);
+  if (st != PKVD_OK) return st;
+  a.ws_lse = static_cast<float*>(ws);
+  // partial outputs start 256-byte aligned after the LSE block
+  uintptr_t o = reinterpret_cast<uintptr_t>(a.ws_lse + (size_t)2 * p.num_waves * p.rows_per_tile);
+  o = (o + 255) & ~uintptr_t(255);
+  a.ws_o = reinterpret_cast<float*>(o);
   if (env_int("PKVD_LOG", 0))
-    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d splits=%d blocks/split=%d wgs=%lld\n",
-            p.path, p.rows_per_tile, p.row_tiles, p.splits, p.split_blocks,
-            (long long)p.workgroups);
+    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d\n", p.path,
+            p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, (int)s.D, s.bf16, hs);
+  hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  if (p.splits > 1) {
-    e = pkvd::launch_merge(a, (int)s.D, s.bf16, hs);
-    if (e != hipSuccess) return fail(PKVD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
-  }
   return PKVD_OK;
 }
 

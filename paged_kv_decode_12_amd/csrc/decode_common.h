@@ -1,0 +1,316 @@
+// decode_common.h -- device helpers shared by the VALU and MFMA decode kernels:
+// element formats, wavefront primitives, the key range of a request, the
+// per-workgroup page list, and the split epilogue that merges partial
+// attention states with the base-2 LSE rule.
+//
+// Reference semantics: flashinfer.cudnn.cudnn_batch_decode_with_kv_cache
+// (Parameters: q_len_per_req, window_left, sinks; Note: LSE convention).
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "decode_args.h"
+
+namespace pkvd {
+namespace dev {
+
+constexpr float kTau = 8.0f;          // lazy-rescale threshold, base-2 units
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes: 8 bf16/fp16 values
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+// read of K/V page data, used once per call
+#ifndef PKVD_NT_LOADS
+#define PKVD_NT_LOADS 1
+#endif
+__device__ __forceinline__ u32x4 load16_stream(const uint16_t* p) {
+#if PKVD_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+// Device-coherent scalar accesses for data exchanged between workgroups of one
+// launch (split partials).  Agent-scope relaxed atomics compile to plain
+// loads/stores that bypass the per-XCD L2 (sc1), so no L2 write-back or
+// invalidate is needed around the exchange.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Instrumented builds (-DPKVD_TRACE) stamp the 100 MHz real-time counter at
+// numbered points of each wave; normal builds compile these away.
+#ifdef PKVD_TRACE
+#define PKVD_STAMP(a, gw, k)                                                      \
+  do {                                                                            \
+    if ((a).trace && __lane_id() == 0)                                            \
+      (a).trace[(int64_t)(gw) * 16 + (k)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#define PKVD_COUNT(a, gw, k, v)                                                   \
+  do {                                                                            \
+    if ((a).trace && __lane_id() == 0) (a).trace[(int64_t)(gw) * 16 + (k)] = (v); \
+  } while (0)
+#else
+#define PKVD_STAMP(a, gw, k) ((void)0)
+#define PKVD_COUNT(a, gw, k, v) ((void)0)
+#endif
+
+// ---------------------------------------------------------------------------
+// element formats (storage: 16-bit patterns in uint16/uint32 words)
+// ---------------------------------------------------------------------------
+template <bool BF16>
+struct Fmt;
+
+template <>
+struct Fmt<true> {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+  static __device__ __forceinline__ uint16_t encode(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);   // round to nearest even
+  }
+};
+
+template <>
+struct Fmt<false> {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  c, false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2_t, u).x;
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2_t, u).y;
+  }
+  static __device__ __forceinline__ uint16_t encode(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront primitives
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7-i within each 8
+constexpr int kDppRor8 = 0x128;         // lane i <- lane (i+8) mod 16 within each 16
+
+// Sum over an aligned lane octet; every lane of the octet gets the total.
+__device__ __forceinline__ float octet_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ float shfl_xor(float x, int m) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The values of x held by a lane pair: lanes l and l ^ 16 (SWAP = 16) or
+// l and l ^ 32 (SWAP = 32).  Both lanes of a pair receive the same (lo, hi):
+// lo from the lane with the bit clear, hi from the lane with it set.
+struct Pair {
+  float lo, hi;
+};
+template <int SWAP>
+__device__ __forceinline__ Pair lane_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if constexpr (SWAP == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a state with running max m merged under a common max M >= m.
+__device__ __forceinline__ float rescale(float m, float M) {
+  return m == -INFINITY ? 0.f : fast_exp2(m - M);
+}
+
+// ---------------------------------------------------------------------------
+// key range of one request and its split
+// ---------------------------------------------------------------------------
+// Keys some row of request b may see: [lo(row 0), n - 1], where row 0 has the
+// lowest diagonal n - Lq (Parameters / q_len_per_req) and the window keeps
+// window_left keys before the diagonal (Parameters / window_left).  The range
+// is cut into 16-key blocks aligned to the absolute key index; splits take
+// consecutive runs of split_blocks blocks.
+struct UnitRange {
+  int n;          // sequence length, clamped to the block table's capacity
+  int key_lo;     // first key some row sees
+  int first_blk;  // block holding key_lo
+  int nblk;       // blocks covering [key_lo, n)
+};
+
+__device__ __forceinline__ UnitRange unit_range_n(const DecodeArgs& a, int n_raw) {
+  UnitRange u;
+  const int cap = a.C * a.ps;
+  const int n = n_raw < 0 ? 0 : (n_raw > cap ? cap : n_raw);
+  u.n = n;
+  const int lo = (a.window_left < 0) ? 0 : n - a.Lq - a.window_left;
+  u.key_lo = lo < 0 ? 0 : lo;
+  if (u.key_lo >= n) {
+    u.first_blk = 0;
+    u.nblk = 0;
+  } else {
+    u.first_blk = u.key_lo / kBlockKeys;
+    u.nblk = (n - 1) / kBlockKeys - u.first_blk + 1;
+  }
+  return u;
+}
+
+__device__ __forceinline__ UnitRange unit_range(const DecodeArgs& a, int b) {
+  return unit_range_n(a, a.seq_lens[b]);
+}
+
+// Final value of one output element: out = O / (L + e^{sink}) and, for d == 0,
+// lse = M + log2 L (keys only).  An empty row (L = 0) gives out = 0 and
+// lse = -inf.  M and L are in base-2 units (Parameters / sinks; Note / LSE
+// convention).
+template <bool BF16>
+__device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, float M, float L,
+                                             float O) {
+  if (!(L > 0.f)) return 0.f;
+  float Z = L;
+  if (a.sinks) Z += fast_exp2(a.sinks[qhead] * kLog2e - M);
+  return O / Z;
+}
+
+// ---------------------------------------------------------------------------
+// balanced persistent schedule
+// ---------------------------------------------------------------------------
+// The work is the linear block space of all units (request b, kv head, row
+// tile) in that order; request b owns [pref[b], pref[b + 1]) and each of its
+// Hkv * row_tiles units holds nblk(b) consecutive blocks.  With T blocks in
+// total and NW waves, wave w owns [floor(w T / NW), floor((w + 1) T / NW)),
+// so every wave streams the same number of blocks (to within one) whatever
+// the mix of sequence lengths.  NW <= T keeps every range non-empty.
+
+__device__ __forceinline__ int64_t wave_begin(int64_t T, int NW, int w) {
+  return T * w / NW;
+}
+// The wave whose range holds linear block x.
+__device__ __forceinline__ int wave_of(int64_t x, int64_t T, int NW) {
+  return (int)(((x + 1) * NW - 1) / T);
+}
+
+// Builds pref[0..B] and the raw lengths nlen[0..B-1] in LDS (one workgroup,
+// ends with a barrier) and returns T = pref[B].  Requests with no visible key
+// get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
+template <bool BF16>
+__device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, int* s_nlen,
+                                            int* s_scan) {
+  const int B = a.B;
+  const int per_req = a.Hkv * a.row_tiles;
+  const int CH = (B + kThreads - 1) / kThreads;
+  const int t = threadIdx.x;
+  const int lo = min(B, t * CH), hi = min(B, lo + CH);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) {
+    const int nraw = a.seq_lens[b];
+    s_nlen[b] = nraw;
+    const int nb = unit_range_n(a, nraw).nblk;
+    sum += nb * per_req;
+    if (nb == 0 && b % (int)gridDim.x == (int)blockIdx.x) {
+      for (int r = b * a.Lq; r < (b + 1) * a.Lq; ++r)
+        for (int h = 0; h < a.Hq; ++h) {
+          const int rowhead = r * a.Hq + h;
+          for (int d = 0; d < a.D; ++d) a.out[(int64_t)rowhead * a.D + d] = 0;
+          if (a.lse) a.lse[rowhead] = -INFINITY;
+        }
+    }
+  }
+  s_scan[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {      // inclusive Hillis-Steele scan
+    const int v = t >= off ? s_scan[t - off] : 0;
+    __syncthreads();
+    s_scan[t] += v;
+    __syncthreads();
+  }
+  int excl = s_scan[t] - sum;
+  for (int b = lo; b < hi; ++b) {
+    s_pref[b] = excl;
+    excl += unit_range_n(a, s_nlen[b]).nblk * per_req;
+  }
+  if (t == kThreads - 1) s_pref[B] = s_scan[t];
+  __syncthreads();
+  return s_pref[B];
+}
+
+// Largest b with pref[b] <= pos (the request holding linear block pos).
+__device__ __forceinline__ int find_request(const int* s_pref, int B, int64_t pos) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// A unit's slice of one wave's range.
+struct Segment {
+  int b, kvh, tile;
+  UnitRange u;
+  int blk_begin, blk_end;    // absolute 16-key blocks [blk_begin, blk_end)
+  int64_t ustart, uend;      // the unit's linear block range
+  bool whole;                // the wave owns the entire unit
+  int side;                  // 0: first segment of the wave, 1: a later one
+};
+
+__device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
+                                          const int* s_nlen, int64_t pos, int64_t wave_lo,
+                                          int64_t wave_hi) {
+  Segment g;
+  g.b = find_request(s_pref, a.B, pos);
+  g.u = unit_range_n(a, s_nlen[g.b]);
+  const int nb = g.u.nblk;
+  const int64_t off = pos - s_pref[g.b];
+  const int uidx = (int)(off / nb);
+  g.kvh = uidx / a.row_tiles;
+  g.tile = uidx - g.kvh * a.row_tiles;
+  g.ustart = s_pref[g.b] + (int64_t)uidx * nb;
+  g.uend = g.ustart + nb;
+  const int64_t seg_end = wave_hi < g.uend ? wave_hi : g.uend;
+  g.blk_begin = g.u.first_blk + (int)(pos - g.ustart);
+  g.blk_end = g.blk_begin + (int)(seg_end - pos);
+  g.whole = pos == g.ustart && seg_end == g.uend;
+  g.side = pos == wave_lo ? 0 : 1;
+  return g;
+}
+
+}  // namespace dev
+}  // namespace pkvd

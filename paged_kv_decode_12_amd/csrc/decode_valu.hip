@@ -1,0 +1,612 @@
+// decode_valu.hip -- paged-KV decode, VALU dot-product path (rows per tile <= 8).
+//
+// Operation: flashinfer.cudnn.cudnn_batch_decode_with_kv_cache (Parameters,
+// Note / LSE convention).  A unit of work is (request b, kv head, row tile);
+// the rows of a tile are the Hq/Hkv query heads sharing the kv head times the
+// q_len_per_req query tokens, so every K/V byte a wave loads serves all of
+// them (grouped-query packing).
+//
+// Schedule (persistent, balanced): one grid of exactly the resident number of
+// waves.  Each workgroup rebuilds, from seq_lens_kv, the prefix of the linear
+// block space of all units; wave w then streams its own contiguous slice
+// [w T / NW, (w + 1) T / NW) of that space, crossing unit boundaries as
+// needed.  Every wave does the same amount of work whatever the mix of
+// lengths.  A unit wholly inside one wave is written directly; a unit cut by
+// wave boundaries leaves a partial state per piece, and the last piece to
+// arrive (atomic ticket) merges them with the base-2 LSE rule (Note / LSE
+// convention: base-2 LSE states are what the cascade merge consumes).  The
+// ranges come from device data only, so planning never reads the lengths on
+// the host.
+//
+// Inside a wave:
+//  * the page ids of the next 128 block-table columns sit in two registers
+//    (one column per lane), read with readlane / ds_bpermute; the next
+//    chunk's page ids and Q rows are fetched before the current segment's
+//    epilogue, and tickets are read only after the whole range is streamed;
+//  * 8 lanes share one key of an 8-key step: lane (kk, part) holds the
+//    16-byte pieces {c * 128 + part * 16} of key kk's row, so one wave-wide
+//    16-byte load reads eight contiguous 128-byte segments of the contiguous
+//    [page_size, D] page tile; Q sits in registers with the same dim split;
+//  * loads run PF blocks ahead of the scoring through a register ring with no
+//    branch around them (keys outside the segment are redirected to a key
+//    inside it and masked), so they stay in flight across the scoring;
+//  * q . k: v_dot2 on bf16/fp16 pairs, then a DPP all-reduce over the octet;
+//  * every octet is an independent online-softmax stream (running max m,
+//    sum l, accumulator for its dims); m rises lazily, only when a score
+//    exceeds it by more than kTau (base 2), so probabilities stay <= 2^kTau
+//    and the rescale branch is rare;
+//  * at a segment's end the 8 streams merge by DPP and lane-pair swaps.
+#include "decode_common.h"
+
+namespace pkvd {
+namespace {
+
+using namespace dev;
+
+template <int D>
+struct KeyRegs {
+  static constexpr int NP = D / 64;  // 16-byte pieces per lane per key row
+  u32x4 k[2][NP];                    // [step][piece]
+  u32x4 v[2][NP];
+};
+
+// Page ids of a chunk's block-table columns col0 .. col0 + 127, one column per
+// lane in each of two registers.
+struct PageWindow {
+  int p0, p1;   // columns col0 + lane, col0 + 64 + lane
+  int col0;
+};
+
+// Page of column col0 + c for a wave-uniform c.
+__device__ __forceinline__ int page_uniform(const PageWindow& w, int c) {
+  return __builtin_amdgcn_readlane(c < 64 ? w.p0 : w.p1, c & 63);
+}
+// Page of column col0 + c for a per-lane c.
+__device__ __forceinline__ int page_lane(const PageWindow& w, int c) {
+  const int a0 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p0);
+  const int a1 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p1);
+  return c < 64 ? a0 : a1;
+}
+
+// Loads block blk (absolute 16-key block index) of a chunk whose keys are
+// [kb, ke) and whose block-table columns sit in pw.
+template <int D, bool PAGE_POW2>
+__device__ __forceinline__ void load_block(KeyRegs<D>& x, const DecodeArgs& a, int kvh, int blk,
+                                           int kb, int ke, const PageWindow& pw, int ps_shift,
+                                           int kk, int part) {
+  constexpr int NP = D / 64;
+  const int j0 = blk * kBlockKeys;
+  int page_blk = 0;
+  if (PAGE_POW2) page_blk = page_uniform(pw, (j0 >> ps_shift) - pw.col0);  // one page per block
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int jc = min(max(j0 + t * 8 + kk, kb), ke - 1);
+    int page, slot;
+    if (PAGE_POW2) {
+      page = page_blk;
+      slot = jc & (a.ps - 1);
+    } else {
+      const int col = jc / a.ps;
+      page = page_lane(pw, col - pw.col0);
+      slot = jc - col * a.ps;
+    }
+    const uint16_t* kr = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot * D + part * 8;
+    const uint16_t* vr = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot * D + part * 8;
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      x.k[t][c] = load16_stream(kr + c * 64);
+      x.v[t][c] = load16_stream(vr + c * 64);
+    }
+  }
+}
+
+template <int D, int RT>
+struct Stream {
+  static constexpr int NP = D / 64;
+  float m[RT], msub[RT], l[RT];
+  float o[RT][NP * 8];   // this lane's dims: c * 64 + part * 8 + e
+};
+
+template <int D, int RT, bool BF16>
+__device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>& x,
+                                            const u32x4 (&qr)[RT][D / 64], float scale_log2,
+                                            bool full, int j0, int kk, const int (&lo_r)[RT],
+                                            const int (&hi_r)[RT]) {
+  using F = Fmt<BF16>;
+  constexpr int NP = D / 64;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = j0 + t * 8 + kk;
+    float s[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        acc = F::dot2(qr[r][c].x, x.k[t][c].x, acc);
+        acc = F::dot2(qr[r][c].y, x.k[t][c].y, acc);
+        acc = F::dot2(qr[r][c].z, x.k[t][c].z, acc);
+        acc = F::dot2(qr[r][c].w, x.k[t][c].w, acc);
+      }
+      s[r] = octet_sum(acc) * scale_log2;
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) s[r] = (j >= lo_r[r] && j <= hi_r[r]) ? s[r] : -INFINITY;
+    }
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) need |= s[r] > st.m[r] + kTau;
+    if (wave_any(need)) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float mn = fmaxf(st.m[r], s[r]);
+        const float alpha = rescale(st.m[r], mn);
+        st.m[r] = mn;
+        st.msub[r] = mn == -INFINITY ? 0.f : mn;
+        st.l[r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < NP * 8; ++e) st.o[r][e] *= alpha;
+      }
+    }
+    float p[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      p[r] = fast_exp2(s[r] - st.msub[r]);
+      st.l[r] += p[r];
+    }
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      const uint32_t w[4] = {x.v[t][c].x, x.v[t][c].y, x.v[t][c].z, x.v[t][c].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v0 = F::lo(w[u]), v1 = F::hi(w[u]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          st.o[r][c * 8 + 2 * u] = fmaf(p[r], v0, st.o[r][c * 8 + 2 * u]);
+          st.o[r][c * 8 + 2 * u + 1] = fmaf(p[r], v1, st.o[r][c * 8 + 2 * u + 1]);
+        }
+      }
+    }
+  }
+}
+
+// Merges the 8 octet streams of the wave (lanes differ in bits 3..5): bit 3
+// within each 16-lane row by DPP, bits 4 and 5 by lane-pair swaps.  Every
+// lane ends with the wave's state for its dims.
+template <int D, int RT>
+__device__ __forceinline__ void merge_octets(Stream<D, RT>& st) {
+  constexpr int E = (D / 64) * 8;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    {
+      const float mo = dpp<kDppRor8>(st.m[r]);
+      const float M = fmaxf(st.m[r], mo);
+      const float a0 = rescale(st.m[r], M), a1 = rescale(mo, M);
+      st.l[r] = st.l[r] * a0 + dpp<kDppRor8>(st.l[r]) * a1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.o[r][e] = st.o[r][e] * a0 + dpp<kDppRor8>(st.o[r][e]) * a1;
+      st.m[r] = M;
+    }
+    {
+      const Pair m = lane_pair<16>(st.m[r]);
+      const float M = fmaxf(m.lo, m.hi);
+      const float a0 = rescale(m.lo, M), a1 = rescale(m.hi, M);
+      const Pair l = lane_pair<16>(st.l[r]);
+      st.l[r] = l.lo * a0 + l.hi * a1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const Pair o = lane_pair<16>(st.o[r][e]);
+        st.o[r][e] = o.lo * a0 + o.hi * a1;
+      }
+      st.m[r] = M;
+    }
+    {
+      const Pair m = lane_pair<32>(st.m[r]);
+      const float M = fmaxf(m.lo, m.hi);
+      const float a0 = rescale(m.lo, M), a1 = rescale(m.hi, M);
+      const Pair l = lane_pair<32>(st.l[r]);
+      st.l[r] = l.lo * a0 + l.hi * a1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const Pair o = lane_pair<32>(st.o[r][e]);
+        st.o[r][e] = o.lo * a0 + o.hi * a1;
+      }
+      st.m[r] = M;
+    }
+  }
+}
+
+// Writes E consecutive-per-piece output values of one row (lane's dims).
+template <int D, bool BF16>
+__device__ __forceinline__ void store_row(const DecodeArgs& a, int rowhead, int qhead, int part,
+                                          float M, float L, const float* O) {
+  constexpr int NP = D / 64;
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo16 = Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, L, O[c * 8 + 2 * u]));
+      const uint32_t hi16 =
+          Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, L, O[c * 8 + 2 * u + 1]));
+      w[u] = lo16 | (hi16 << 16);
+    }
+    *reinterpret_cast<u32x4*>(a.out + (int64_t)rowhead * D + c * 64 + part * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+  if (a.lse && part == 0) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
+}
+
+// Merges the partial states of one unit's pieces (waves w_first .. w_last) for
+// the calling lane's row and dims and writes the final row.  Four pieces'
+// loads are in flight at a time; the running max is updated per group.
+template <int D, int RT, bool BF16>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t T, int NW,
+                                             int64_t ustart, int w_first, int w_last, int kk,
+                                             int part, int rowhead, int qhead) {
+  constexpr int NP = D / 64;
+  constexpr int E = NP * 8;
+  float Mx = -INFINITY, W = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int w = w_first; w <= w_last; w += 4) {
+    float l4[4], v4[4][E];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ww = min(w + u, w_last);
+      const int sl = 2 * ww + (wave_begin(T, NW, ww) >= ustart ? 0 : 1);
+      const float lv = load_coherent(a.ws_lse + (int64_t)sl * RT + kk);
+      l4[u] = w + u <= w_last ? lv : -INFINITY;
+      const float* po = a.ws_o + ((int64_t)sl * RT + kk) * D + part * 8;
+#pragma unroll
+      for (int c = 0; c < NP; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v4[u][c * 8 + e] = load_coherent(po + c * 64 + e);
+    }
+    const float Mn = fmaxf(Mx, fmaxf(fmaxf(l4[0], l4[1]), fmaxf(l4[2], l4[3])));
+    const float sc = rescale(Mx, Mn);
+    W *= sc;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wt = rescale(l4[u], Mn);
+      W += wt;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(wt, v4[u][e], acc[e]);
+    }
+    Mx = Mn;
+  }
+  // acc / W is the merged normalised output; final_value divides by W + sink
+  store_row<D, BF16>(a, rowhead, qhead, part, Mx, W, acc);
+}
+
+template <int D, int RT, bool BF16, bool PAGE_POW2, int PF, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void decode_valu(const DecodeArgs a) {
+  constexpr int NP = D / 64;
+  constexpr int E = NP * 8;
+  constexpr int NBUF = PF + 1;
+  constexpr int kWindow = 128;                        // block-table columns per chunk
+  extern __shared__ int lds[];
+  int* s_scan = lds;                                  // kThreads
+  int* s_pref = lds + kThreads;                       // B + 1
+  int* s_nlen = s_pref + a.B + 1;                     // B
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int kk = lane >> 3, part = lane & 7;
+
+  const int gw0 = (int)blockIdx.x * kWaves + wave;
+  PKVD_STAMP(a, gw0, 0);
+  const int64_t T = build_prefix<BF16>(a, s_pref, s_nlen, s_scan);
+  PKVD_STAMP(a, gw0, 1);
+  if (T == 0) return;
+  // waves that take part: at most one per min_wave_blocks blocks (and <= T)
+  int64_t nw = T / a.min_wave_blocks;
+  nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
+  const int NW = (int)nw;
+  const int gw = (int)blockIdx.x * kWaves + wave;
+  if (gw >= NW) return;
+  const int64_t lo = wave_begin(T, NW, gw), hi = wave_begin(T, NW, gw + 1);
+  const int R = a.g * a.Lq;
+  const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
+  // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
+  const int chunk_blocks = max(1, ((kWindow - 2) * a.ps + 1) / kBlockKeys);
+
+  // A chunk: blocks [cb, ce) of segment sg (a unit's slice of this wave's range).
+  struct Chunk {
+    Segment sg;
+    int cb, ce, kb, ke;
+    bool first, last;   // first / last chunk of its segment
+  };
+  auto make_chunk = [&](const Segment& sg, int cb) {
+    Chunk c;
+    c.sg = sg;
+    c.cb = cb;
+    c.ce = min(sg.blk_end, cb + chunk_blocks);
+    c.kb = max(sg.u.key_lo, cb * kBlockKeys);
+    c.ke = min(sg.u.n, c.ce * kBlockKeys);
+    c.first = cb == sg.blk_begin;
+    c.last = c.ce == sg.blk_end;
+    return c;
+  };
+  // page ids of a chunk's columns, clamped into the pool (issued early)
+  auto fetch_pages = [&](const Chunk& c) {
+    PageWindow w;
+    w.col0 = c.kb / a.ps;
+    const int ncol = (c.ke - 1) / a.ps - w.col0 + 1;
+    const int32_t* row = a.bt + (int64_t)c.sg.b * a.bt_sr + w.col0;
+    const int p0 = row[min(lane, ncol - 1)];
+    const int p1 = row[min(64 + lane, ncol - 1)];
+    w.p0 = (unsigned)p0 < (unsigned)a.P ? p0 : a.P - 1;
+    w.p1 = (unsigned)p1 < (unsigned)a.P ? p1 : a.P - 1;
+    return w;
+  };
+  // Q rows of a segment's tile: rr = tile * RT + r -> token rr / g, head rr % g
+  auto fetch_q = [&](const Segment& sg, u32x4 (&q)[RT][NP]) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int rr = sg.tile * RT + r;
+      const bool live = rr < R;
+      const int i = live ? rr / a.g : 0;
+      const int hl = live ? rr - i * a.g : 0;
+      const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
+                           (int64_t)(sg.kvh * a.g + hl) * a.q_sh + part * 8;
+#pragma unroll
+      for (int c = 0; c < NP; ++c) q[r][c] = live ? load16(qp + c * 64) : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  // pieces of units shared with other waves: at most the first and the last
+  // segment of the range; their tickets are read after the range is done
+  int pend_prev[2] = {-1, -1}, pend_unit[2] = {0, 0};
+  int64_t pend_ustart[2] = {0, 0}, pend_uend[2] = {0, 0};
+  int pend_tile[2] = {0, 0}, pend_b[2] = {0, 0}, pend_kvh[2] = {0, 0};
+
+  const Segment sg0 = locate(a, s_pref, s_nlen, lo, lo, hi);
+  Chunk ch = make_chunk(sg0, sg0.blk_begin);
+  PageWindow pw = fetch_pages(ch);
+  u32x4 qr[RT][NP];
+  fetch_q(ch.sg, qr);
+
+  Stream<D, RT> st;
+  int lo_r[RT], hi_r[RT];
+  int max_lo = 0, min_hi = 0;
+#ifdef PKVD_TRACE
+  int n_seg = 0, n_chunk = 0, n_blk = 0;
+#endif
+  PKVD_STAMP(a, gw, 2);
+  for (;;) {
+    const Segment& sg = ch.sg;
+    if (ch.first) {
+      max_lo = sg.u.key_lo;
+      min_hi = sg.u.n - 1;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int rr = sg.tile * RT + r;
+        const bool live = rr < R;
+        const int diag = sg.u.n - a.Lq + (live ? rr / a.g : 0);
+        const int rlo = max(a.window_left < 0 ? 0 : diag - a.window_left, 0);
+        lo_r[r] = live ? rlo : 1;     // dead rows see nothing
+        hi_r[r] = live ? diag : 0;
+        if (live) {
+          max_lo = max(max_lo, rlo);
+          min_hi = min(min_hi, diag);
+        }
+        st.m[r] = -INFINITY;
+        st.msub[r] = 0.f;
+        st.l[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.o[r][e] = 0.f;
+      }
+    }
+
+    // stream the chunk's blocks with loads PF ahead
+#ifdef PKVD_TRACE
+    if (n_chunk == 0) PKVD_STAMP(a, gw, 3);
+    n_chunk++;
+    n_blk += ch.ce - ch.cb;
+#endif
+    {
+      const int nb = ch.ce - ch.cb;
+      const int kb = ch.kb, ke = ch.ke, cb = ch.cb, kvh = sg.kvh;
+      KeyRegs<D> buf[NBUF];
+      auto blk_of = [&](int i) { return cb + min(i, nb - 1); };
+      auto score = [&](const KeyRegs<D>& x, int i) {
+        const int j0 = (cb + i) * kBlockKeys;
+        const bool full = j0 >= max_lo && j0 + kBlockKeys - 1 <= min_hi;
+        score_block<D, RT, BF16>(st, x, qr, a.scale_log2, full, j0, kk, lo_r, hi_r);
+      };
+#pragma unroll
+      for (int s = 0; s < PF; ++s)
+        load_block<D, PAGE_POW2>(buf[s], a, kvh, blk_of(s), kb, ke, pw, ps_shift, kk, part);
+      // full rounds: each sub-step issues the loads of the block PF ahead (the
+      // last block again near the end: a cache hit), then scores its own block
+      const int rounds = nb / NBUF;
+      for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+        for (int s = 0; s < NBUF; ++s) {
+          const int i = rd * NBUF + s;
+          load_block<D, PAGE_POW2>(buf[(s + PF) % NBUF], a, kvh, blk_of(i + PF), kb, ke, pw,
+                                   ps_shift, kk, part);
+          score(buf[s], i);
+        }
+      }
+      // tail: the remaining nb % NBUF <= PF blocks are already in flight
+      const int i0 = rounds * NBUF;
+#pragma unroll
+      for (int s = 0; s < PF; ++s)
+        if (i0 + s < nb) score(buf[s], i0 + s);
+    }
+
+#ifdef PKVD_TRACE
+    if (n_chunk == 1) PKVD_STAMP(a, gw, 4);
+#endif
+    if (!ch.last) {            // next chunk of the same segment
+      ch = make_chunk(sg, ch.ce);
+      pw = fetch_pages(ch);
+      continue;
+    }
+
+    // the segment is done: finish it
+    merge_octets<D, RT>(st);
+    float M = -INFINITY, L = 0.f, O[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) O[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      if (kk == r) {             // lanes kk < RT own row kk
+        M = st.m[r];
+        L = st.l[r];
+#pragma unroll
+        for (int e = 0; e < E; ++e) O[e] = st.o[r][e];
+      }
+    }
+    const int rr = sg.tile * RT + kk;
+    if (sg.whole) {
+      if (kk < RT && rr < R) {
+        const int i = rr / a.g, qhead = sg.kvh * a.g + (rr - i * a.g);
+        store_row<D, BF16>(a, (sg.b * a.Lq + i) * a.Hq + qhead, qhead, part, M, L, O);
+      }
+    } else {
+      // a piece of a unit shared with other waves: leave the partial state,
+      // then take a ticket (its value is read once the range is done)
+      const int slot = 2 * gw + sg.side;
+      if (kk < RT) {
+        float* po = a.ws_o + ((int64_t)slot * RT + kk) * D;
+#pragma unroll
+        for (int c = 0; c < NP; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            store_coherent(po + c * 64 + part * 8 + e, L > 0.f ? O[c * 8 + e] / L : 0.f);
+        if (part == 0)
+          store_coherent(a.ws_lse + (int64_t)slot * RT + kk, L > 0.f ? M + log2f(L) : -INFINITY);
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // partial stores complete before the ticket
+      const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
+      int prev = 0;
+      if (lane == 0) prev = atomicAdd(&a.counters[unit], 1);
+      auto remember = [&](int k) {
+        pend_prev[k] = prev;
+        pend_unit[k] = unit;
+        pend_ustart[k] = sg.ustart;
+        pend_uend[k] = sg.uend;
+        pend_tile[k] = sg.tile;
+        pend_b[k] = sg.b;
+        pend_kvh[k] = sg.kvh;
+      };
+      if (sg.side == 0) remember(0);
+      else remember(1);
+    }
+#ifdef PKVD_TRACE
+    if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
+#endif
+    const int64_t next = sg.ustart + (sg.blk_end - sg.u.first_blk);
+    if (next >= hi) break;
+    const Segment ns = locate(a, s_pref, s_nlen, next, lo, hi);
+    ch = make_chunk(ns, ns.blk_begin);
+    pw = fetch_pages(ch);
+    fetch_q(ns, qr);
+  }
+
+  PKVD_STAMP(a, gw, 6);
+#ifdef PKVD_TRACE
+  PKVD_COUNT(a, gw, 8, n_seg);
+  PKVD_COUNT(a, gw, 9, n_chunk);
+  PKVD_COUNT(a, gw, 10, n_blk);
+  {
+    uint32_t hwid = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_ID
+    uint32_t xcc = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11));    // XCC_ID
+    PKVD_COUNT(a, gw, 11, ((uint64_t)xcc << 32) | hwid);
+  }
+#endif
+  // merge the units whose last piece this wave delivered
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const int unit = pend_unit[side];
+    const bool had = uniform(pend_prev[side] >= 0 ? 1 : 0) != 0;
+    if (!had) continue;
+    const int w_first = wave_of(pend_ustart[side], T, NW);
+    const int w_last = wave_of(pend_uend[side] - 1, T, NW);
+    const int prev = uniform(pend_prev[side]);
+    if (prev != w_last - w_first) continue;
+    if (lane == 0) a.counters[unit] = 0;   // ready for the next call
+    const int rr = pend_tile[side] * RT + kk;
+    if (!(kk < RT && rr < R)) continue;
+    const int i = rr / a.g, qhead = pend_kvh[side] * a.g + (rr - i * a.g);
+    merge_pieces<D, RT, BF16>(a, T, NW, pend_ustart[side], w_first, w_last, kk, part,
+                              (pend_b[side] * a.Lq + i) * a.Hq + qhead, qhead);
+  }
+  PKVD_STAMP(a, gw, 7);
+}
+
+// blocks in flight ahead of the scoring
+#ifndef PKVD_PF4
+#define PKVD_PF4 1
+#endif
+#ifndef PKVD_PF8
+#define PKVD_PF8 1
+#endif
+
+using KernelFn = void (*)(DecodeArgs);
+
+// waves per SIMD the register budget is fitted to
+#ifndef PKVD_WPE4
+#define PKVD_WPE4 2
+#endif
+
+template <int D, int RT, bool BF16, bool POW2>
+KernelFn kernel_of() {
+  constexpr int pf = RT == 4 ? PKVD_PF4 : (D == 128 ? PKVD_PF8 : 2);
+  constexpr int wpe = RT == 4 ? (D == 128 ? PKVD_WPE4 : 3) : (D == 128 ? 1 : 2);
+  return &decode_valu<D, RT, BF16, POW2, pf, wpe>;
+}
+
+KernelFn select(int rows_per_tile, int head_dim, bool bf16, bool pow2) {
+#define PKVD_SEL(D, RT, BF, P2)                                                          \
+  if (head_dim == D && rows_per_tile == RT && bf16 == BF && pow2 == P2) \
+    return kernel_of<D, RT, BF, P2>();
+#define PKVD_SEL_P2(D, RT, BF) PKVD_SEL(D, RT, BF, true) PKVD_SEL(D, RT, BF, false)
+#define PKVD_SEL_BF(D, RT) PKVD_SEL_P2(D, RT, true) PKVD_SEL_P2(D, RT, false)
+  PKVD_SEL_BF(128, 4)
+  PKVD_SEL_BF(128, 8)
+  PKVD_SEL_BF(64, 4)
+  PKVD_SEL_BF(64, 8)
+#undef PKVD_SEL_BF
+#undef PKVD_SEL_P2
+#undef PKVD_SEL
+  return nullptr;
+}
+
+bool page_pow2(int ps) { return ps >= kBlockKeys && (ps & (ps - 1)) == 0; }
+
+}  // namespace
+
+// scan scratch, prefix, lengths
+size_t decode_lds_bytes(int B) { return sizeof(int) * ((size_t)kThreads + 2 * (size_t)B + 1); }
+
+int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
+                         size_t lds_bytes) {
+  if (path != kPathValu) return 0;
+  KernelFn k = select(rows_per_tile, head_dim, bf16, pow2);
+  if (!k) return 0;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), kThreads,
+                                                   lds_bytes) != hipSuccess)
+    return 0;
+  return n;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,
+                         hipStream_t stream) {
+  if (path != kPathValu) return hipErrorInvalidValue;
+  KernelFn k = select(rows_per_tile, a.D, bf16, page_pow2(a.ps));
+  if (!k) return hipErrorInvalidValue;
+  const dim3 grid((a.num_waves + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B), stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkvd

@@ -121,8 +121,8 @@ def test_unsupported_shapes(D, ps):
 
 
 def test_plans_of_the_workloads():
-    """Shape-only plans: the path follows rows = (Hq/Hkv) * q_len_per_req and
-    long sequences at small batch are split."""
+    """Shape-only plans: the path follows rows = (Hq/Hkv) * q_len_per_req; the
+    persistent grid and its workspace do not depend on the lengths."""
     for name, w in workloads.CONFIGS.items():
         q = torch.empty(w.B * w.q_len_per_req, w.Hq, w.D, dtype=torch.bfloat16)
         k = torch.empty(1, w.Hkv, w.page_size, w.D, dtype=torch.bfloat16)
@@ -130,8 +130,6 @@ def test_plans_of_the_workloads():
         p = pk.plan(q, k, bt, w.q_len_per_req, w.window_left)
         rows = (w.Hq // w.Hkv) * w.q_len_per_req
         assert p["rows_per_tile"] * p["row_tiles"] >= rows
-        assert p["workgroups"] == p["splits"] * w.Hkv * p["row_tiles"] * w.B
+        assert p["workgroups"] * 4 >= p["waves"] >= 1
         ws = pk.workspace_bytes(q, k, bt, w.q_len_per_req, w.window_left)
-        assert (ws > 0) == (p["splits"] > 1)
-        if name == "long_ctx":
-            assert p["splits"] > 8
+        assert ws >= 2 * p["waves"] * p["rows_per_tile"] * (w.D + 1) * 4

@@ -113,7 +113,34 @@ def test_config_poison(name):
     compare(name + "/poison", out, lse, ref_out, ref_lse)
 
 
-def test_determinism_and_split_invariance():
+SCHEDULES = {
+    "auto": {},
+    "cut7": {"PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    "cut64": {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
+}
+
+
+class schedule:
+    """Temporarily force the persistent grid's wave count (env knobs)."""
+
+    def __init__(self, name):
+        self.env = SCHEDULES[name]
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.env}
+        os.environ.update(self.env)
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def test_determinism_and_schedule_invariance():
+    """Repeat calls are bitwise identical; other wave counts (units cut at
+    other places, merged from more pieces) agree within tolerance."""
     name = "llama3_8b"
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
@@ -121,13 +148,19 @@ def test_determinism_and_split_invariance():
     b, lb = run_gpu(d)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
-    for s in ("1", "3", "16"):
-        os.environ["PKVD_NUM_SPLITS"] = s
+    for env in ({"PKVD_WAVES": "1"}, {"PKVD_WAVES": "333", "PKVD_MIN_WAVE_BLOCKS": "1"},
+                {"PKVD_WAVES": "5000", "PKVD_MIN_WAVE_BLOCKS": "1"}):
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
         try:
             o, l = run_gpu(d)
         finally:
-            del os.environ["PKVD_NUM_SPLITS"]
-        compare(f"{name}/splits={s}", o, l, ref_out, ref_lse)
+            for k, v in old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        compare(f"{name}/{env}", o, l, ref_out, ref_lse)
 
 
 # ----------------------------------------------------------------------------
@@ -156,19 +189,15 @@ def _edge_id(c):
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[_edge_id(c) for c in EDGE])
-@pytest.mark.parametrize("splits", ["auto", "4"])
-def test_edge_sweep(case, splits):
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+def test_edge_sweep(case, sched):
     kw = dict(B=len(case["seq_lens"]), Hq=4, Hkv=2, D=64, page_size=16, seed=7)
     kw.update(case)
     inp = workloads.make_case(**kw)
-    log(f"[edge] {_edge_id(case)} splits={splits}")
+    log(f"[edge] {_edge_id(case)} schedule={sched}")
     ref_out, ref_lse, _ = oracle.decode(inp)
-    if splits != "auto":
-        os.environ["PKVD_NUM_SPLITS"] = splits
-    try:
+    with schedule(sched):
         out, lse = run_gpu(to_dev(inp))
-    finally:
-        os.environ.pop("PKVD_NUM_SPLITS", None)
     # outputs far above 1 (value_std > 1) carry bf16 rounding of up to 2^-8 |out|
     atol = max(OUT_ATOL, 2.0 ** -7 * float(np.abs(ref_out).max()))
     compare(_edge_id(case), out, lse, ref_out, ref_lse, out_atol=atol)
@@ -200,7 +229,7 @@ def test_graph_replay():
     inp = workloads.make_case(B=4, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(100, 900, 33, 2000),
                               seed=9)
     d = to_dev(inp)
-    os.environ["PKVD_NUM_SPLITS"] = "4"
+    os.environ.update(SCHEDULES["cut7"])
     try:
         pk.reserve_workspace(pk.workspace_bytes(d["q"], d["k_cache"], d["block_tables"]))
         out = torch.empty_like(d["q"])
@@ -226,4 +255,5 @@ def test_graph_replay():
             assert torch.equal(out, eager_o), it
             assert torch.equal(lse, eager_l), it
     finally:
-        os.environ.pop("PKVD_NUM_SPLITS", None)
+        for k in SCHEDULES["cut7"]:
+            os.environ.pop(k, None)
