@@ -84,6 +84,11 @@ struct Fmt<true> {
   static __device__ __forceinline__ uint16_t encode(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);   // round to nearest even
   }
+  // (a, b) rounded to nearest even and packed, a in the low half
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  }
 };
 
 template <>
@@ -101,7 +106,19 @@ struct Fmt<false> {
   static __device__ __forceinline__ uint16_t encode(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
   }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+  }
 };
+
+// Low halves of w0 and w1 packed (w0's in the low half), and the high halves.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t w0, uint32_t w1) {
+  return __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t w0, uint32_t w1) {
+  return __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+}
 
 // ---------------------------------------------------------------------------
 // wavefront primitives

@@ -76,26 +76,38 @@ __device__ __forceinline__ void load_block(KeyRegs<D>& x, const DecodeArgs& a, i
                                            int kk, int part) {
   constexpr int NP = D / 64;
   const int j0 = blk * kBlockKeys;
-  int page_blk = 0;
-  if (PAGE_POW2) page_blk = page_uniform(pw, (j0 >> ps_shift) - pw.col0);  // one page per block
+  if (PAGE_POW2) {
+    // page_size is a power of two >= 16: the block lies in one page, so the
+    // tile base is wave-uniform (scalar) and each lane adds a 32-bit offset
+    const int page = page_uniform(pw, (j0 >> ps_shift) - pw.col0);
+    const int slot0 = j0 & (a.ps - 1);
+    const uint16_t* kbase = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot0 * D;
+    const uint16_t* vbase = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot0 * D;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int jc = min(max(j0 + t * 8 + kk, kb), ke - 1);
-    int page, slot;
-    if (PAGE_POW2) {
-      page = page_blk;
-      slot = jc & (a.ps - 1);
-    } else {
-      const int col = jc / a.ps;
-      page = page_lane(pw, col - pw.col0);
-      slot = jc - col * a.ps;
+    for (int t = 0; t < 2; ++t) {
+      // keys outside [kb, ke) read a key of the block inside it (masked later)
+      const uint32_t jr = (uint32_t)(min(max(j0 + t * 8 + kk, kb), ke - 1) - j0);
+      const uint32_t off = jr * D + part * 8;
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        x.k[t][c] = load16_stream(kbase + off + c * 64);
+        x.v[t][c] = load16_stream(vbase + off + c * 64);
+      }
     }
-    const uint16_t* kr = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot * D + part * 8;
-    const uint16_t* vr = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot * D + part * 8;
+  } else {
 #pragma unroll
-    for (int c = 0; c < NP; ++c) {
-      x.k[t][c] = load16_stream(kr + c * 64);
-      x.v[t][c] = load16_stream(vr + c * 64);
+    for (int t = 0; t < 2; ++t) {
+      const int jc = min(max(j0 + t * 8 + kk, kb), ke - 1);
+      const int col = jc / a.ps;
+      const int page = page_lane(pw, col - pw.col0);
+      const int slot = jc - col * a.ps;
+      const uint16_t* kr = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot * D + part * 8;
+      const uint16_t* vr = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot * D + part * 8;
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        x.k[t][c] = load16_stream(kr + c * 64);
+        x.v[t][c] = load16_stream(vr + c * 64);
+      }
     }
   }
 }
@@ -103,10 +115,14 @@ __device__ __forceinline__ void load_block(KeyRegs<D>& x, const DecodeArgs& a, i
 template <int D, int RT>
 struct Stream {
   static constexpr int NP = D / 64;
-  float m[RT], msub[RT], l[RT];
+  float m[RT], l[RT];
   float o[RT][NP * 8];   // this lane's dims: c * 64 + part * 8 + e
 };
 
+// Scores one 16-key block: the lane's octet holds key kk in step 0 and key
+// kk + 8 in step 1.  The two probabilities of a row are packed as a 16-bit
+// pair and multiplied into V with v_dot2 against (V[kk][d], V[kk + 8][d])
+// pairs built by byte permutes; the running sums l stay in fp32.
 template <int D, int RT, bool BF16>
 __device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>& x,
                                             const u32x4 (&qr)[RT][D / 64], float scale_log2,
@@ -114,10 +130,9 @@ __device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>&
                                             const int (&hi_r)[RT]) {
   using F = Fmt<BF16>;
   constexpr int NP = D / 64;
+  float s[2][RT];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int j = j0 + t * 8 + kk;
-    float s[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       float acc = 0.f;
@@ -128,44 +143,51 @@ __device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>&
         acc = F::dot2(qr[r][c].z, x.k[t][c].z, acc);
         acc = F::dot2(qr[r][c].w, x.k[t][c].w, acc);
       }
-      s[r] = octet_sum(acc) * scale_log2;
+      s[t][r] = octet_sum(acc) * scale_log2;
     }
-    if (!full) {
+  }
+  if (!full) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r) s[r] = (j >= lo_r[r] && j <= hi_r[r]) ? s[r] : -INFINITY;
+    for (int t = 0; t < 2; ++t) {
+      const int j = j0 + t * 8 + kk;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) s[t][r] = (j >= lo_r[r] && j <= hi_r[r]) ? s[t][r] : -INFINITY;
     }
-    bool need = false;
+  }
+  bool need = false;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) need |= s[r] > st.m[r] + kTau;
-    if (wave_any(need)) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float mn = fmaxf(st.m[r], s[r]);
-        const float alpha = rescale(st.m[r], mn);
-        st.m[r] = mn;
-        st.msub[r] = mn == -INFINITY ? 0.f : mn;
-        st.l[r] *= alpha;
-#pragma unroll
-        for (int e = 0; e < NP * 8; ++e) st.o[r][e] *= alpha;
-      }
-    }
-    float p[RT];
+  for (int r = 0; r < RT; ++r) need |= fmaxf(s[0][r], s[1][r]) > st.m[r] + kTau;
+  if (wave_any(need)) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      p[r] = fast_exp2(s[r] - st.msub[r]);
-      st.l[r] += p[r];
+      const float mn = fmaxf(st.m[r], fmaxf(s[0][r], s[1][r]));
+      const float alpha = rescale(st.m[r], mn);
+      st.m[r] = mn;
+      st.l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < NP * 8; ++e) st.o[r][e] *= alpha;
     }
+  }
+  uint32_t pp[RT];
 #pragma unroll
-    for (int c = 0; c < NP; ++c) {
-      const uint32_t w[4] = {x.v[t][c].x, x.v[t][c].y, x.v[t][c].z, x.v[t][c].w};
+  for (int r = 0; r < RT; ++r) {
+    // a row with no visible key yet has m = -inf and every s = -inf: p = 0
+    const float ms = st.m[r] == -INFINITY ? 0.f : st.m[r];
+    const float p0 = fast_exp2(s[0][r] - ms), p1 = fast_exp2(s[1][r] - ms);
+    st.l[r] += p0 + p1;
+    pp[r] = F::pack2(p0, p1);
+  }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float v0 = F::lo(w[u]), v1 = F::hi(w[u]);
+  for (int c = 0; c < NP; ++c) {
+    const uint32_t w0[4] = {x.v[0][c].x, x.v[0][c].y, x.v[0][c].z, x.v[0][c].w};
+    const uint32_t w1[4] = {x.v[1][c].x, x.v[1][c].y, x.v[1][c].z, x.v[1][c].w};
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          st.o[r][c * 8 + 2 * u] = fmaf(p[r], v0, st.o[r][c * 8 + 2 * u]);
-          st.o[r][c * 8 + 2 * u + 1] = fmaf(p[r], v1, st.o[r][c * 8 + 2 * u + 1]);
-        }
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t vlo = pair_lo(w0[u], w1[u]), vhi = pair_hi(w0[u], w1[u]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        st.o[r][c * 8 + 2 * u] = F::dot2(pp[r], vlo, st.o[r][c * 8 + 2 * u]);
+        st.o[r][c * 8 + 2 * u + 1] = F::dot2(pp[r], vhi, st.o[r][c * 8 + 2 * u + 1]);
       }
     }
   }
@@ -396,7 +418,6 @@ void decode_valu(const DecodeArgs a) {
           min_hi = min(min_hi, diag);
         }
         st.m[r] = -INFINITY;
-        st.msub[r] = 0.f;
         st.l[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) st.o[r][e] = 0.f;
