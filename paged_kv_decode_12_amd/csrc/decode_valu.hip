@@ -18,24 +18,29 @@
 // ranges come from device data only, so planning never reads the lengths on
 // the host.
 //
-// Inside a wave:
+// Inside a wave (LPK = D / 8 lanes per key, KPS = 64 / LPK keys per step):
+//  * lane (kq, part) holds the 16-byte piece `part` (dims part*8 .. part*8+7)
+//    of key kq of each step, so one wave-wide 16-byte load reads KPS whole
+//    contiguous key rows of the [page_size, D] page tile; Q sits in
+//    registers with the same dim split;
+//  * two steps form a group (4 KB of K and V per wave); groups are loaded PF
+//    ahead of the scoring through a register ring with no branch around the
+//    loads (keys outside the segment are redirected to a key inside it and
+//    masked), so they stay in flight across the scoring;
+//  * q . k: v_dot2 on bf16/fp16 pairs, then a DPP all-reduce over the LPK
+//    lanes of the key;
+//  * every key lane group is an independent online-softmax stream (running
+//    max m, sum l, accumulator for its 8 dims); m rises lazily, only when a
+//    score exceeds it by more than kTau (base 2), so probabilities stay
+//    <= 2^kTau and the rescale branch is rare;
+//  * P x V: the lane's two keys of a group (steps 0 and 1) give a pair of
+//    probabilities, packed to bf16/fp16 and multiplied into byte-permuted
+//    (V[k][d], V[k + KPS][d]) pairs with v_dot2; sums l stay in fp32;
 //  * the page ids of the next 128 block-table columns sit in two registers
 //    (one column per lane), read with readlane / ds_bpermute; the next
 //    chunk's page ids and Q rows are fetched before the current segment's
 //    epilogue, and tickets are read only after the whole range is streamed;
-//  * 8 lanes share one key of an 8-key step: lane (kk, part) holds the
-//    16-byte pieces {c * 128 + part * 16} of key kk's row, so one wave-wide
-//    16-byte load reads eight contiguous 128-byte segments of the contiguous
-//    [page_size, D] page tile; Q sits in registers with the same dim split;
-//  * loads run PF blocks ahead of the scoring through a register ring with no
-//    branch around them (keys outside the segment are redirected to a key
-//    inside it and masked), so they stay in flight across the scoring;
-//  * q . k: v_dot2 on bf16/fp16 pairs, then a DPP all-reduce over the octet;
-//  * every octet is an independent online-softmax stream (running max m,
-//    sum l, accumulator for its dims); m rises lazily, only when a score
-//    exceeds it by more than kTau (base 2), so probabilities stay <= 2^kTau
-//    and the rescale branch is rare;
-//  * at a segment's end the 8 streams merge by DPP and lane-pair swaps.
+//  * at a segment's end the KPS streams merge by DPP and lane-pair swaps.
 #include "decode_common.h"
 
 namespace pkvd {
@@ -44,10 +49,16 @@ namespace {
 using namespace dev;
 
 template <int D>
+struct Geo {
+  static constexpr int LPK = D / 8;           // lanes per key (one 16-byte piece each)
+  static constexpr int KPS = 64 / LPK;        // keys per step
+  static constexpr int KPG = 2 * KPS;         // keys per group (two steps)
+  static constexpr int GPB = kBlockKeys / KPG;  // groups per 16-key block
+};
+
 struct KeyRegs {
-  static constexpr int NP = D / 64;  // 16-byte pieces per lane per key row
-  u32x4 k[2][NP];                    // [step][piece]
-  u32x4 v[2][NP];
+  u32x4 k[2];   // [step]: the lane's 16-byte piece of its key of that step
+  u32x4 v[2];
 };
 
 // Page ids of a chunk's block-table columns col0 .. col0 + 127, one column per
@@ -68,88 +79,90 @@ __device__ __forceinline__ int page_lane(const PageWindow& w, int c) {
   return c < 64 ? a0 : a1;
 }
 
-// Loads block blk (absolute 16-key block index) of a chunk whose keys are
-// [kb, ke) and whose block-table columns sit in pw.
+// Loads group gi (keys gi * KPG ..) of a chunk whose keys are [kb, ke) and
+// whose block-table columns sit in pw.
 template <int D, bool PAGE_POW2>
-__device__ __forceinline__ void load_block(KeyRegs<D>& x, const DecodeArgs& a, int kvh, int blk,
+__device__ __forceinline__ void load_group(KeyRegs& x, const DecodeArgs& a, int kvh, int gi,
                                            int kb, int ke, const PageWindow& pw, int ps_shift,
-                                           int kk, int part) {
-  constexpr int NP = D / 64;
-  const int j0 = blk * kBlockKeys;
+                                           int kq, int part) {
+  using G = Geo<D>;
+  const int j0 = gi * G::KPG;
   if (PAGE_POW2) {
-    // page_size is a power of two >= 16: the block lies in one page, so the
-    // tile base is wave-uniform (scalar) and each lane adds a 32-bit offset
-    const int page = page_uniform(pw, (j0 >> ps_shift) - pw.col0);
-    const int slot0 = j0 & (a.ps - 1);
+    // page_size is a power of two >= 16: the group's 16-key block lies in one
+    // page, so the tile base is wave-uniform (scalar) and each lane adds a
+    // 32-bit offset.  A key outside [kb, ke) reads the clamped key instead
+    // (masked later); the block always holds a key of [kb, ke), so the clamped
+    // key is in the same page at a row 0..15 past the block start, even when
+    // this group itself lies wholly before kb or after ke - 1.
+    const int jb = j0 & ~(kBlockKeys - 1);
+    const int page = page_uniform(pw, (jb >> ps_shift) - pw.col0);
+    const int slot0 = jb & (a.ps - 1);
     const uint16_t* kbase = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot0 * D;
     const uint16_t* vbase = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot0 * D;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      // keys outside [kb, ke) read a key of the block inside it (masked later)
-      const uint32_t jr = (uint32_t)(min(max(j0 + t * 8 + kk, kb), ke - 1) - j0);
+      const uint32_t jr = (uint32_t)(min(max(j0 + t * G::KPS + kq, kb), ke - 1) - jb);
       const uint32_t off = jr * D + part * 8;
-#pragma unroll
-      for (int c = 0; c < NP; ++c) {
-        x.k[t][c] = load16_stream(kbase + off + c * 64);
-        x.v[t][c] = load16_stream(vbase + off + c * 64);
-      }
+      x.k[t] = load16_stream(kbase + off);
+      x.v[t] = load16_stream(vbase + off);
     }
   } else {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int jc = min(max(j0 + t * 8 + kk, kb), ke - 1);
+      const int jc = min(max(j0 + t * G::KPS + kq, kb), ke - 1);
       const int col = jc / a.ps;
       const int page = page_lane(pw, col - pw.col0);
       const int slot = jc - col * a.ps;
-      const uint16_t* kr = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + slot * D + part * 8;
-      const uint16_t* vr = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot * D + part * 8;
-#pragma unroll
-      for (int c = 0; c < NP; ++c) {
-        x.k[t][c] = load16_stream(kr + c * 64);
-        x.v[t][c] = load16_stream(vr + c * 64);
-      }
+      const int64_t off = (int64_t)slot * D + part * 8;
+      x.k[t] = load16_stream(a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh + off);
+      x.v[t] = load16_stream(a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + off);
     }
   }
 }
 
-template <int D, int RT>
+template <int RT>
 struct Stream {
-  static constexpr int NP = D / 64;
   float m[RT], l[RT];
-  float o[RT][NP * 8];   // this lane's dims: c * 64 + part * 8 + e
+  float o[RT][8];   // this lane's 8 dims: part * 8 + e
 };
 
-// Scores one 16-key block: the lane's octet holds key kk in step 0 and key
-// kk + 8 in step 1.  The two probabilities of a row are packed as a 16-bit
-// pair and multiplied into V with v_dot2 against (V[kk][d], V[kk + 8][d])
-// pairs built by byte permutes; the running sums l stay in fp32.
+// Sum over the LPK lanes of a key (aligned lane groups of 8 or 16).
+template <int LPK>
+__device__ __forceinline__ float key_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  if constexpr (LPK == 16) x += dpp<kDppRor8>(x);
+  return x;
+}
+
+// Scores one group: key kq in step 0 and key kq + KPS in step 1.  The two
+// probabilities of a row are packed as a 16-bit pair and multiplied into V
+// with v_dot2 against (V[kq][d], V[kq + KPS][d]) pairs built by byte
+// permutes; the running sums l stay in fp32.
 template <int D, int RT, bool BF16>
-__device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>& x,
-                                            const u32x4 (&qr)[RT][D / 64], float scale_log2,
-                                            bool full, int j0, int kk, const int (&lo_r)[RT],
+__device__ __forceinline__ void score_group(Stream<RT>& st, const KeyRegs& x,
+                                            const u32x4 (&qr)[RT], float scale_log2, bool full,
+                                            int j0, int kq, const int (&lo_r)[RT],
                                             const int (&hi_r)[RT]) {
   using F = Fmt<BF16>;
-  constexpr int NP = D / 64;
+  using G = Geo<D>;
   float s[2][RT];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < NP; ++c) {
-        acc = F::dot2(qr[r][c].x, x.k[t][c].x, acc);
-        acc = F::dot2(qr[r][c].y, x.k[t][c].y, acc);
-        acc = F::dot2(qr[r][c].z, x.k[t][c].z, acc);
-        acc = F::dot2(qr[r][c].w, x.k[t][c].w, acc);
-      }
-      s[t][r] = octet_sum(acc) * scale_log2;
+      float acc = F::dot2(qr[r].x, x.k[t].x, 0.f);
+      acc = F::dot2(qr[r].y, x.k[t].y, acc);
+      acc = F::dot2(qr[r].z, x.k[t].z, acc);
+      acc = F::dot2(qr[r].w, x.k[t].w, acc);
+      s[t][r] = key_sum<G::LPK>(acc) * scale_log2;
     }
   }
   if (!full) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int j = j0 + t * 8 + kk;
+      const int j = j0 + t * G::KPS + kq;
 #pragma unroll
       for (int r = 0; r < RT; ++r) s[t][r] = (j >= lo_r[r] && j <= hi_r[r]) ? s[t][r] : -INFINITY;
     }
@@ -165,7 +178,7 @@ __device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>&
       st.m[r] = mn;
       st.l[r] *= alpha;
 #pragma unroll
-      for (int e = 0; e < NP * 8; ++e) st.o[r][e] *= alpha;
+      for (int e = 0; e < 8; ++e) st.o[r][e] *= alpha;
     }
   }
   uint32_t pp[RT];
@@ -177,37 +190,33 @@ __device__ __forceinline__ void score_block(Stream<D, RT>& st, const KeyRegs<D>&
     st.l[r] += p0 + p1;
     pp[r] = F::pack2(p0, p1);
   }
+  const uint32_t w0[4] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w};
+  const uint32_t w1[4] = {x.v[1].x, x.v[1].y, x.v[1].z, x.v[1].w};
 #pragma unroll
-  for (int c = 0; c < NP; ++c) {
-    const uint32_t w0[4] = {x.v[0][c].x, x.v[0][c].y, x.v[0][c].z, x.v[0][c].w};
-    const uint32_t w1[4] = {x.v[1][c].x, x.v[1][c].y, x.v[1][c].z, x.v[1][c].w};
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t vlo = pair_lo(w0[u], w1[u]), vhi = pair_hi(w0[u], w1[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t vlo = pair_lo(w0[u], w1[u]), vhi = pair_hi(w0[u], w1[u]);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        st.o[r][c * 8 + 2 * u] = F::dot2(pp[r], vlo, st.o[r][c * 8 + 2 * u]);
-        st.o[r][c * 8 + 2 * u + 1] = F::dot2(pp[r], vhi, st.o[r][c * 8 + 2 * u + 1]);
-      }
+    for (int r = 0; r < RT; ++r) {
+      st.o[r][2 * u] = F::dot2(pp[r], vlo, st.o[r][2 * u]);
+      st.o[r][2 * u + 1] = F::dot2(pp[r], vhi, st.o[r][2 * u + 1]);
     }
   }
 }
 
-// Merges the 8 octet streams of the wave (lanes differ in bits 3..5): bit 3
-// within each 16-lane row by DPP, bits 4 and 5 by lane-pair swaps.  Every
-// lane ends with the wave's state for its dims.
+// Merges the KPS key streams of the wave into every lane (lanes of different
+// streams differ in bits log2(LPK) .. 5): bit 3 within each 16-lane row by
+// DPP (when LPK = 8), bits 4 and 5 by lane-pair swaps.
 template <int D, int RT>
-__device__ __forceinline__ void merge_octets(Stream<D, RT>& st) {
-  constexpr int E = (D / 64) * 8;
+__device__ __forceinline__ void merge_streams(Stream<RT>& st) {
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    {
+    if constexpr (Geo<D>::LPK == 8) {
       const float mo = dpp<kDppRor8>(st.m[r]);
       const float M = fmaxf(st.m[r], mo);
       const float a0 = rescale(st.m[r], M), a1 = rescale(mo, M);
       st.l[r] = st.l[r] * a0 + dpp<kDppRor8>(st.l[r]) * a1;
 #pragma unroll
-      for (int e = 0; e < E; ++e) st.o[r][e] = st.o[r][e] * a0 + dpp<kDppRor8>(st.o[r][e]) * a1;
+      for (int e = 0; e < 8; ++e) st.o[r][e] = st.o[r][e] * a0 + dpp<kDppRor8>(st.o[r][e]) * a1;
       st.m[r] = M;
     }
     {
@@ -217,7 +226,7 @@ __device__ __forceinline__ void merge_octets(Stream<D, RT>& st) {
       const Pair l = lane_pair<16>(st.l[r]);
       st.l[r] = l.lo * a0 + l.hi * a1;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const Pair o = lane_pair<16>(st.o[r][e]);
         st.o[r][e] = o.lo * a0 + o.hi * a1;
       }
@@ -230,7 +239,7 @@ __device__ __forceinline__ void merge_octets(Stream<D, RT>& st) {
       const Pair l = lane_pair<32>(st.l[r]);
       st.l[r] = l.lo * a0 + l.hi * a1;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const Pair o = lane_pair<32>(st.o[r][e]);
         st.o[r][e] = o.lo * a0 + o.hi * a1;
       }
@@ -239,64 +248,61 @@ __device__ __forceinline__ void merge_octets(Stream<D, RT>& st) {
   }
 }
 
-// Writes E consecutive-per-piece output values of one row (lane's dims).
+// Writes one row's 8 output values (dims part*8 ..) and, from part 0, its LSE.
 template <int D, bool BF16>
 __device__ __forceinline__ void store_row(const DecodeArgs& a, int rowhead, int qhead, int part,
-                                          float M, float L, const float* O) {
-  constexpr int NP = D / 64;
+                                          float M, float L, const float (&O)[8]) {
+  uint32_t w[4];
 #pragma unroll
-  for (int c = 0; c < NP; ++c) {
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t lo16 = Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, L, O[c * 8 + 2 * u]));
-      const uint32_t hi16 =
-          Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, L, O[c * 8 + 2 * u + 1]));
-      w[u] = lo16 | (hi16 << 16);
-    }
-    *reinterpret_cast<u32x4*>(a.out + (int64_t)rowhead * D + c * 64 + part * 8) =
-        u32x4{w[0], w[1], w[2], w[3]};
-  }
+  for (int u = 0; u < 4; ++u)
+    w[u] = Fmt<BF16>::pack2(final_value<BF16>(a, qhead, M, L, O[2 * u]),
+                            final_value<BF16>(a, qhead, M, L, O[2 * u + 1]));
+  *reinterpret_cast<u32x4*>(a.out + (int64_t)rowhead * D + part * 8) =
+      u32x4{w[0], w[1], w[2], w[3]};
   if (a.lse && part == 0) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
 }
 
+// Partial state layout of one slot: [row][e][part] (LPK consecutive floats per
+// store instruction and key group), then the row LSEs in ws_lse.
+template <int D, int RT>
+__device__ __forceinline__ int64_t partial_index(int slot, int r, int e, int part) {
+  return ((int64_t)slot * RT * 8 + r * 8 + e) * Geo<D>::LPK + part;
+}
+
 // Merges the partial states of one unit's pieces (waves w_first .. w_last) for
-// the calling lane's row and dims and writes the final row.  Four pieces'
-// loads are in flight at a time; the running max is updated per group.
+// row r (the calling lane's share: dims part*8 ..) and writes the final row.
+// Four pieces' loads are in flight at a time; the running max is updated per
+// group of four.
 template <int D, int RT, bool BF16>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t T, int NW,
-                                             int64_t ustart, int w_first, int w_last, int kk,
+                                             int64_t ustart, int w_first, int w_last, int r,
                                              int part, int rowhead, int qhead) {
-  constexpr int NP = D / 64;
-  constexpr int E = NP * 8;
-  float Mx = -INFINITY, W = 0.f, acc[E];
+  float Mx = -INFINITY, W = 0.f, acc[8];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int w = w_first; w <= w_last; w += 4) {
-    float l4[4], v4[4][E];
+    float l4[4], v4[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ww = min(w + u, w_last);
       const int sl = 2 * ww + (wave_begin(T, NW, ww) >= ustart ? 0 : 1);
-      const float lv = load_coherent(a.ws_lse + (int64_t)sl * RT + kk);
+      const float lv = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
       l4[u] = w + u <= w_last ? lv : -INFINITY;
-      const float* po = a.ws_o + ((int64_t)sl * RT + kk) * D + part * 8;
 #pragma unroll
-      for (int c = 0; c < NP; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v4[u][c * 8 + e] = load_coherent(po + c * 64 + e);
+      for (int e = 0; e < 8; ++e)
+        v4[u][e] = load_coherent(a.ws_o + partial_index<D, RT>(sl, r, e, part));
     }
     const float Mn = fmaxf(Mx, fmaxf(fmaxf(l4[0], l4[1]), fmaxf(l4[2], l4[3])));
     const float sc = rescale(Mx, Mn);
     W *= sc;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= sc;
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float wt = rescale(l4[u], Mn);
       W += wt;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(wt, v4[u][e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt, v4[u][e], acc[e]);
     }
     Mx = Mn;
   }
@@ -307,10 +313,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t T, int
 template <int D, int RT, bool BF16, bool PAGE_POW2, int PF, int WPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_valu(const DecodeArgs a) {
-  constexpr int NP = D / 64;
-  constexpr int E = NP * 8;
+  using G = Geo<D>;
   constexpr int NBUF = PF + 1;
   constexpr int kWindow = 128;                        // block-table columns per chunk
+  constexpr int RPG = (RT + G::KPS - 1) / G::KPS;     // output rows per key group
   extern __shared__ int lds[];
   int* s_scan = lds;                                  // kThreads
   int* s_pref = lds + kThreads;                       // B + 1
@@ -318,7 +324,7 @@ void decode_valu(const DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int kk = lane >> 3, part = lane & 7;
+  const int kq = lane / G::LPK, part = lane % G::LPK;
 
   const int gw0 = (int)blockIdx.x * kWaves + wave;
   PKVD_STAMP(a, gw0, 0);
@@ -366,8 +372,9 @@ void decode_valu(const DecodeArgs a) {
     w.p1 = (unsigned)p1 < (unsigned)a.P ? p1 : a.P - 1;
     return w;
   };
-  // Q rows of a segment's tile: rr = tile * RT + r -> token rr / g, head rr % g
-  auto fetch_q = [&](const Segment& sg, u32x4 (&q)[RT][NP]) {
+  // Q rows of a segment's tile (rr = tile * RT + r -> token rr / g, head rr % g):
+  // the lane's 16-byte piece of each row
+  auto fetch_q = [&](const Segment& sg, u32x4 (&q)[RT]) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int rr = sg.tile * RT + r;
@@ -376,8 +383,7 @@ void decode_valu(const DecodeArgs a) {
       const int hl = live ? rr - i * a.g : 0;
       const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
                            (int64_t)(sg.kvh * a.g + hl) * a.q_sh + part * 8;
-#pragma unroll
-      for (int c = 0; c < NP; ++c) q[r][c] = live ? load16(qp + c * 64) : u32x4{0, 0, 0, 0};
+      q[r] = live ? load16(qp) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -390,10 +396,10 @@ void decode_valu(const DecodeArgs a) {
   const Segment sg0 = locate(a, s_pref, s_nlen, lo, lo, hi);
   Chunk ch = make_chunk(sg0, sg0.blk_begin);
   PageWindow pw = fetch_pages(ch);
-  u32x4 qr[RT][NP];
+  u32x4 qr[RT];
   fetch_q(ch.sg, qr);
 
-  Stream<D, RT> st;
+  Stream<RT> st;
   int lo_r[RT], hi_r[RT];
   int max_lo = 0, min_hi = 0;
 #ifdef PKVD_TRACE
@@ -420,46 +426,46 @@ void decode_valu(const DecodeArgs a) {
         st.m[r] = -INFINITY;
         st.l[r] = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) st.o[r][e] = 0.f;
+        for (int e = 0; e < 8; ++e) st.o[r][e] = 0.f;
       }
     }
 
-    // stream the chunk's blocks with loads PF ahead
+    // stream the chunk's key groups with loads PF groups ahead
 #ifdef PKVD_TRACE
     if (n_chunk == 0) PKVD_STAMP(a, gw, 3);
     n_chunk++;
     n_blk += ch.ce - ch.cb;
 #endif
     {
-      const int nb = ch.ce - ch.cb;
-      const int kb = ch.kb, ke = ch.ke, cb = ch.cb, kvh = sg.kvh;
-      KeyRegs<D> buf[NBUF];
-      auto blk_of = [&](int i) { return cb + min(i, nb - 1); };
-      auto score = [&](const KeyRegs<D>& x, int i) {
-        const int j0 = (cb + i) * kBlockKeys;
-        const bool full = j0 >= max_lo && j0 + kBlockKeys - 1 <= min_hi;
-        score_block<D, RT, BF16>(st, x, qr, a.scale_log2, full, j0, kk, lo_r, hi_r);
+      const int g0 = ch.cb * G::GPB, ng = (ch.ce - ch.cb) * G::GPB;
+      const int kb = ch.kb, ke = ch.ke, kvh = sg.kvh;
+      KeyRegs buf[NBUF];
+      auto grp_of = [&](int i) { return g0 + min(i, ng - 1); };
+      auto score = [&](const KeyRegs& x, int i) {
+        const int j0 = (g0 + i) * G::KPG;
+        const bool full = j0 >= max_lo && j0 + G::KPG - 1 <= min_hi;
+        score_group<D, RT, BF16>(st, x, qr, a.scale_log2, full, j0, kq, lo_r, hi_r);
       };
 #pragma unroll
       for (int s = 0; s < PF; ++s)
-        load_block<D, PAGE_POW2>(buf[s], a, kvh, blk_of(s), kb, ke, pw, ps_shift, kk, part);
-      // full rounds: each sub-step issues the loads of the block PF ahead (the
-      // last block again near the end: a cache hit), then scores its own block
-      const int rounds = nb / NBUF;
+        load_group<D, PAGE_POW2>(buf[s], a, kvh, grp_of(s), kb, ke, pw, ps_shift, kq, part);
+      // full rounds: each sub-step issues the loads of the group PF ahead (the
+      // last group again near the end: a cache hit), then scores its own group
+      const int rounds = ng / NBUF;
       for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
           const int i = rd * NBUF + s;
-          load_block<D, PAGE_POW2>(buf[(s + PF) % NBUF], a, kvh, blk_of(i + PF), kb, ke, pw,
-                                   ps_shift, kk, part);
+          load_group<D, PAGE_POW2>(buf[(s + PF) % NBUF], a, kvh, grp_of(i + PF), kb, ke, pw,
+                                   ps_shift, kq, part);
           score(buf[s], i);
         }
       }
-      // tail: the remaining nb % NBUF <= PF blocks are already in flight
+      // tail: the remaining ng % NBUF <= PF groups are already in flight
       const int i0 = rounds * NBUF;
 #pragma unroll
       for (int s = 0; s < PF; ++s)
-        if (i0 + s < nb) score(buf[s], i0 + s);
+        if (i0 + s < ng) score(buf[s], i0 + s);
     }
 
 #ifdef PKVD_TRACE
@@ -472,38 +478,53 @@ void decode_valu(const DecodeArgs a) {
     }
 
     // the segment is done: finish it
-    merge_octets<D, RT>(st);
-    float M = -INFINITY, L = 0.f, O[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) O[e] = 0.f;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (kk == r) {             // lanes kk < RT own row kk
-        M = st.m[r];
-        L = st.l[r];
-#pragma unroll
-        for (int e = 0; e < E; ++e) O[e] = st.o[r][e];
-      }
-    }
-    const int rr = sg.tile * RT + kk;
+    merge_streams<D, RT>(st);
     if (sg.whole) {
-      if (kk < RT && rr < R) {
-        const int i = rr / a.g, qhead = sg.kvh * a.g + (rr - i * a.g);
-        store_row<D, BF16>(a, (sg.b * a.Lq + i) * a.Hq + qhead, qhead, part, M, L, O);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const int r = kq + i * G::KPS;           // rows of this key group
+        float M = -INFINITY, L = 0.f, O[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[e] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr)
+          if (rr == r) {
+            M = st.m[rr];
+            L = st.l[rr];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O[e] = st.o[rr][e];
+          }
+        const int row = sg.tile * RT + r;
+        if (r < RT && row < R) {
+          const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
+          store_row<D, BF16>(a, (sg.b * a.Lq + ti) * a.Hq + qhead, qhead, part, M, L, O);
+        }
       }
     } else {
       // a piece of a unit shared with other waves: leave the partial state,
       // then take a ticket (its value is read once the range is done)
       const int slot = 2 * gw + sg.side;
-      if (kk < RT) {
-        float* po = a.ws_o + ((int64_t)slot * RT + kk) * D;
 #pragma unroll
-        for (int c = 0; c < NP; ++c)
+      for (int i = 0; i < RPG; ++i) {
+        const int r = kq + i * G::KPS;
+        float M = -INFINITY, L = 0.f, O[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[e] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr)
+          if (rr == r) {
+            M = st.m[rr];
+            L = st.l[rr];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O[e] = st.o[rr][e];
+          }
+        if (r < RT) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            store_coherent(po + c * 64 + part * 8 + e, L > 0.f ? O[c * 8 + e] / L : 0.f);
-        if (part == 0)
-          store_coherent(a.ws_lse + (int64_t)slot * RT + kk, L > 0.f ? M + log2f(L) : -INFINITY);
+            store_coherent(a.ws_o + partial_index<D, RT>(slot, r, e, part), L > 0.f ? O[e] / L : 0.f);
+          if (part == 0)
+            store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0);   // partial stores complete before the ticket
       const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
@@ -554,11 +575,15 @@ void decode_valu(const DecodeArgs a) {
     const int prev = uniform(pend_prev[side]);
     if (prev != w_last - w_first) continue;
     if (lane == 0) a.counters[unit] = 0;   // ready for the next call
-    const int rr = pend_tile[side] * RT + kk;
-    if (!(kk < RT && rr < R)) continue;
-    const int i = rr / a.g, qhead = pend_kvh[side] * a.g + (rr - i * a.g);
-    merge_pieces<D, RT, BF16>(a, T, NW, pend_ustart[side], w_first, w_last, kk, part,
-                              (pend_b[side] * a.Lq + i) * a.Hq + qhead, qhead);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = kq + i * G::KPS;
+      const int row = pend_tile[side] * RT + r;
+      if (!(r < RT && row < R)) continue;
+      const int ti = row / a.g, qhead = pend_kvh[side] * a.g + (row - ti * a.g);
+      merge_pieces<D, RT, BF16>(a, T, NW, pend_ustart[side], w_first, w_last, r, part,
+                                (pend_b[side] * a.Lq + ti) * a.Hq + qhead, qhead);
+    }
   }
   PKVD_STAMP(a, gw, 7);
 }
@@ -575,13 +600,16 @@ using KernelFn = void (*)(DecodeArgs);
 
 // waves per SIMD the register budget is fitted to
 #ifndef PKVD_WPE4
-#define PKVD_WPE4 2
+#define PKVD_WPE4 4
+#endif
+#ifndef PKVD_WPE8
+#define PKVD_WPE8 2
 #endif
 
 template <int D, int RT, bool BF16, bool POW2>
 KernelFn kernel_of() {
-  constexpr int pf = RT == 4 ? PKVD_PF4 : (D == 128 ? PKVD_PF8 : 2);
-  constexpr int wpe = RT == 4 ? (D == 128 ? PKVD_WPE4 : 3) : (D == 128 ? 1 : 2);
+  constexpr int pf = RT == 4 ? PKVD_PF4 : PKVD_PF8;
+  constexpr int wpe = RT == 4 ? PKVD_WPE4 : PKVD_WPE8;
   return &decode_valu<D, RT, BF16, POW2, pf, wpe>;
 }
 
