@@ -142,8 +142,14 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   Plan p{};
   const int64_t g = s.Hq / s.Hkv;
   const int64_t R = g * Lq;
-  p.path = pkvd::kPathValu;
-  p.rows_per_tile = R <= 4 ? 4 : 8;
+  // Tiles of 16 rows (a group of at least 16 query rows per kv head) fill an
+  // MFMA operand; smaller groups use VALU dot products, in tiles of 4 or 8.
+  // PKVD_FORCE_PATH=0/1 overrides the choice (for measurements).
+  const int forced_path = env_int("PKVD_FORCE_PATH", -1);
+  p.path = forced_path == pkvd::kPathValu || forced_path == pkvd::kPathMfma
+               ? forced_path
+               : (R >= 16 ? pkvd::kPathMfma : pkvd::kPathValu);
+  p.rows_per_tile = p.path == pkvd::kPathMfma ? 16 : (R <= 4 ? 4 : 8);
   p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
   p.units = s.B * s.Hkv * p.row_tiles;
 

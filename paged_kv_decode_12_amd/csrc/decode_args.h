@@ -31,7 +31,7 @@ struct DecodeArgs {
   // outputs
   uint16_t* out;                   // contiguous (B * Lq, Hq, D)
   float* lse;                      // nullptr: not requested
-  float* ws_o;                     // partial states [2 * num_waves][D / 8][rows_per_tile * 8]
+  float* ws_o;                     // partial states [2 * num_waves][rows_per_tile * D], order set by the engine
   float* ws_lse;                   // [2 * num_waves][rows_per_tile]
   int32_t* counters;               // [B * Hkv * row_tiles] arrival tickets, zero between calls
   // shapes

@@ -329,5 +329,26 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
   return g;
 }
 
+// ---------------------------------------------------------------------------
+// page ids of a chunk
+// ---------------------------------------------------------------------------
+// Page ids of a chunk's block-table columns col0 .. col0 + 127, one column per
+// lane in each of two registers.
+struct PageWindow {
+  int p0, p1;   // columns col0 + lane, col0 + 64 + lane
+  int col0;
+};
+
+// Page of column col0 + c for a wave-uniform c.
+__device__ __forceinline__ int page_uniform(const PageWindow& w, int c) {
+  return __builtin_amdgcn_readlane(c < 64 ? w.p0 : w.p1, c & 63);
+}
+// Page of column col0 + c for a per-lane c.
+__device__ __forceinline__ int page_lane(const PageWindow& w, int c) {
+  const int a0 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p0);
+  const int a1 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p1);
+  return c < 64 ? a0 : a1;
+}
+
 }  // namespace dev
 }  // namespace pkvd

@@ -130,6 +130,12 @@ def test_plans_of_the_workloads():
         p = pk.plan(q, k, bt, w.q_len_per_req, w.window_left)
         rows = (w.Hq // w.Hkv) * w.q_len_per_req
         assert p["rows_per_tile"] * p["row_tiles"] >= rows
+        # MFMA exactly when the rows fill 16-row tiles; VALU tiles of 4 or 8 otherwise
+        if rows >= 16:
+            assert (p["path"], p["rows_per_tile"]) == ("mfma", 16)
+        else:
+            assert p["path"] == "valu" and p["rows_per_tile"] == (4 if rows <= 4 else 8)
+        assert p["row_tiles"] == -(-rows // p["rows_per_tile"])
         assert p["workgroups"] * 4 >= p["waves"] >= 1
         ws = pk.workspace_bytes(q, k, bt, w.q_len_per_req, w.window_left)
         assert ws >= 2 * p["waves"] * p["rows_per_tile"] * (w.D + 1) * 4

@@ -117,6 +117,9 @@ SCHEDULES = {
     "auto": {},
     "cut7": {"PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "cut64": {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    # the other engine than the planner picks (MFMA for < 16 rows, VALU for >= 16)
+    "mfma_cut7": {"PKVD_FORCE_PATH": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    "valu": {"PKVD_FORCE_PATH": "0"},
 }
 
 
@@ -136,6 +139,25 @@ class schedule:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+@pytest.mark.parametrize("name,path", [("llama3_8b", "1"), ("spec_verify", "0"),
+                                       ("sink_window", "1")])
+def test_config_other_engine(name, path):
+    """Full-size configs on the engine the planner does not pick for them."""
+    log(f"[engine] config={name} PKVD_FORCE_PATH={path}")
+    inp, (ref_out, ref_lse, _) = config_inputs(name)
+    d = to_dev(inp)
+    os.environ["PKVD_FORCE_PATH"] = path
+    try:
+        p = _pk().plan(d["q"], d["k_cache"], d["block_tables"], d["q_len_per_req"],
+                       d["window_left"])
+        log(f"[engine] plan={p}")
+        assert p["path"] == {"0": "valu", "1": "mfma"}[path]
+        out, lse = run_gpu(d, lse=True)
+    finally:
+        os.environ.pop("PKVD_FORCE_PATH", None)
+    compare(f"{name}/path{path}", out, lse, ref_out, ref_lse)
 
 
 def test_determinism_and_schedule_invariance():
