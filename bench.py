@@ -16,10 +16,18 @@ Also reported:
                 cores on the same workload, as a reported baseline only;
   cold          per-call time with the 256 MB Infinity Cache and L2 flushed
                 before every call (outside the events).
+
+roofline.traffic is the HBM bytes per launch that rocprofv3's FETCH_SIZE and
+WRITE_SIZE counters gave for this workload, scaled by what the same counters
+read for a plain device copy of known size (``--copy-calibration`` runs that
+copy).  The figures live in profiles/decode_<workload>_hbm_traffic.txt together
+with a SHA-256 of the kernel sources they were taken with; when the sources
+have changed since, traffic is null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -45,6 +53,51 @@ def kv_bytes(inp) -> int:
     return 2 * D * elt * Hkv * keys
 
 
+def kernel_source_hash() -> str:
+    """SHA-256 over the library's sources and build flags (what the counters measured)."""
+    from paged_kv_decode_12_amd import build as b
+    h = hashlib.sha256()
+    for path in b.SOURCES + b.HEADERS:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    h.update(" ".join(b.FLAGS[:-2]).encode())      # flags minus the machine-specific -I paths
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE
+    and WRITE_SIZE counters (each dispatch reads and writes exactly nbytes)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": nbytes, "dispatches": reps}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,12 +108,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU-baseline leg (0 disables it)")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this decode kernel is measured on a single "
               "MI355X; multi-GPU sharding is a design note, not a built path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -152,7 +211,7 @@ def main():
         "plan": plan,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": stored_traffic(args.config),
                      "kernel": "decode (one pkvd_decode launch)",
                      "launch_us": round(launch_ms * 1e3, 3)},
     }
