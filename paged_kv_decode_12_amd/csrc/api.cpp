@@ -132,7 +132,7 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
   }
   const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
   const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
-                                           pkvd::decode_lds_bytes((int)s.B));
+                                           pkvd::decode_lds_bytes((int)s.B, path, (int)s.D));
   if (n > 0) f.blocks_per_cu = n;
   else (void)hipGetLastError();
   return f;

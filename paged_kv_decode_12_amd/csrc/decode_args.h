@@ -50,7 +50,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,
                          hipStream_t stream);
 // Dynamic LDS bytes of a launch for B requests.
-size_t decode_lds_bytes(int B);
+size_t decode_lds_bytes(int B, int path, int head_dim);
 // Workgroups of the decode kernel that fit on one CU at once (0 on error).
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool page_pow2,
                          size_t lds_bytes);

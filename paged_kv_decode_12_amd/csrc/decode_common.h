@@ -243,6 +243,23 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t T, int NW) {
   return (int)(((x + 1) * NW - 1) / T);
 }
 
+// Dynamic LDS of a workgroup, in 32-bit words: the engine's per-wave scratch
+// (kWaves slots of eng_words), the scan scratch (kThreads), the prefix
+// (B + 1) and the raw lengths (B).  Host (launch size) and kernel (carve-up)
+// both take the offsets from here.
+struct LdsLayout {
+  int eng, scan, pref, nlen, total;
+};
+__host__ __device__ inline LdsLayout lds_layout(int eng_words, int B) {
+  LdsLayout l;
+  l.eng = 0;
+  l.scan = kWaves * eng_words;
+  l.pref = l.scan + kThreads;
+  l.nlen = l.pref + B + 1;
+  l.total = l.nlen + B;
+  return l;
+}
+
 // Builds pref[0..B] and the raw lengths nlen[0..B-1] in LDS (one workgroup,
 // ends with a barrier) and returns T = pref[B].  Requests with no visible key
 // get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
@@ -314,9 +331,11 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
   Segment g;
   g.b = find_request(s_pref, a.B, pos);
   g.u = unit_range_n(a, s_nlen[g.b]);
-  const int nb = g.u.nblk;
+  const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
   const int64_t off = pos - s_pref[g.b];
-  const int uidx = (int)(off / nb);
+  const int per_req = a.Hkv * a.row_tiles;
+  int uidx = (int)(off / nb);
+  uidx = uidx < 0 ? 0 : (uidx >= per_req ? per_req - 1 : uidx);
   g.kvh = uidx / a.row_tiles;
   g.tile = uidx - g.kvh * a.row_tiles;
   g.ustart = s_pref[g.b] + (int64_t)uidx * nb;

@@ -112,6 +112,23 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t T, int
   store_item<D, N, BF16>(a, rowhead, qhead, d0, d0 == 0, Mx, W, acc);
 }
 
+// Issue priority from a wave's progress through its own range: 3 in the first
+// quarter down to 0 in the last.  Waves sharing a SIMD are otherwise served
+// oldest first, so the youngest fall behind and finish last; dropping the
+// priority of the waves that are ahead lets the others catch up, and every
+// wave's equal share then ends at about the same time.
+#ifndef PKVD_PRIO
+#define PKVD_PRIO 0
+#endif
+__device__ __forceinline__ void progress_priority(int done, int q1, int q2, int q3) {
+#if PKVD_PRIO
+  if (done >= q3) __builtin_amdgcn_s_setprio(0);
+  else if (done >= q2) __builtin_amdgcn_s_setprio(1);
+  else if (done >= q1) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
+#endif
+}
+
 template <class Eng, int D, bool BF16, bool PAGE_POW2, int PF, int WPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_kernel(const DecodeArgs a) {
@@ -119,13 +136,15 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int NBUF = PF + 1;
   constexpr int kWindow = 128;                        // block-table columns per chunk
   extern __shared__ int lds[];
-  int* s_scan = lds;                                  // kThreads
-  int* s_pref = lds + kThreads;                       // B + 1
-  int* s_nlen = s_pref + a.B + 1;                     // B
+  constexpr int kEngWords = Eng::kLdsBytesPerWave / 4;
+  const LdsLayout L = lds_layout(kEngWords, a.B);
+  int* s_scan = lds + L.scan;
+  int* s_pref = lds + L.pref;
+  int* s_nlen = lds + L.nlen;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const typename Eng::Lane ln = Eng::lane_of(lane);
+  const typename Eng::Lane ln = Eng::lane_of(lane, lds + L.eng + wave * kEngWords);
 
   const int gw0 = (int)blockIdx.x * kWaves + wave;
   PKVD_STAMP(a, gw0, 0);
@@ -139,6 +158,10 @@ void decode_kernel(const DecodeArgs a) {
   const int gw = (int)blockIdx.x * kWaves + wave;
   if (gw >= NW) return;
   const int64_t lo = wave_begin(T, NW, gw), hi = wave_begin(T, NW, gw + 1);
+  // progress in key groups, for the issue priority
+  const int total_groups = (int)(hi - lo) * Eng::kGroupsPerBlock;
+  const int q1 = total_groups / 4, q2 = total_groups / 2, q3 = 3 * total_groups / 4;
+  int groups_done = 0;
   const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
@@ -183,7 +206,6 @@ void decode_kernel(const DecodeArgs a) {
   Chunk ch = make_chunk(sg0, sg0.blk_begin);
   PageWindow pw = fetch_pages(ch);
   typename Eng::Q qr;
-  Eng::fetch_q(a, ch.sg, R, ln, qr);
 
   typename Eng::State st;
   int max_lo = 0, min_hi = 0;
@@ -215,10 +237,13 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < PF; ++s)
         Eng::template load<PAGE_POW2>(buf[s], a, kvh, grp_of(s), kb, ke, pw, ps_shift, ln);
+      // the segment's Q rows, after the first loads so their wait overlaps them
+      if (ch.first) Eng::fetch_q(a, sg, R, ln, qr);
       // full rounds: each sub-step issues the loads of the group PF ahead (the
       // last group again near the end: a cache hit), then scores its own group
       const int rounds = ng / NBUF;
       for (int rd = 0; rd < rounds; ++rd) {
+        progress_priority(groups_done + rd * NBUF, q1, q2, q3);
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
           const int i = rd * NBUF + s;
@@ -232,6 +257,7 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < PF; ++s)
         if (i0 + s < ng) score(buf[s], i0 + s);
+      groups_done += ng;
     }
 
 #ifdef PKVD_TRACE
@@ -276,12 +302,11 @@ void decode_kernel(const DecodeArgs a) {
             store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);   // partial stores complete before the ticket
+      // the ticket is taken once the whole range is streamed, when these
+      // stores have long completed (no wait for them here)
       const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
-      int prev = 0;
-      if (lane == 0) prev = atomicAdd(&a.counters[unit], 1);
       auto remember = [&](int k) {
-        pend_prev[k] = prev;
+        pend_prev[k] = 0;
         pend_unit[k] = unit;
         pend_ustart[k] = sg.ustart;
         pend_uend[k] = sg.uend;
@@ -300,7 +325,6 @@ void decode_kernel(const DecodeArgs a) {
     const Segment ns = locate(a, s_pref, s_nlen, next, lo, hi);
     ch = make_chunk(ns, ns.blk_begin);
     pw = fetch_pages(ch);
-    Eng::fetch_q(a, ns, R, ln, qr);
   }
 
   PKVD_STAMP(a, gw, 6);
@@ -314,7 +338,16 @@ void decode_kernel(const DecodeArgs a) {
     PKVD_COUNT(a, gw, 11, ((uint64_t)xcc << 32) | hwid);
   }
 #endif
-  // merge the units whose last piece this wave delivered
+  // tickets of the pieces this wave left: partial stores complete first
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int side = 0; side < 2; ++side)
+    if (pend_prev[side] >= 0 && lane == 0) pend_prev[side] = atomicAdd(&a.counters[pend_unit[side]], 1);
+  // merge the units whose last piece this wave delivered (at the top issue
+  // priority: the kernel's end waits on these)
+#if PKVD_PRIO
+  __builtin_amdgcn_s_setprio(3);
+#endif
 #pragma unroll
   for (int side = 0; side < 2; ++side) {
     const int unit = pend_unit[side];
@@ -374,12 +407,15 @@ KernelFn valu_kernel() {
   constexpr int wpe = RT == 4 ? PKVD_WPE4 : PKVD_WPE8;
   return &decode_kernel<ValuEngine<D, RT, BF16>, D, BF16, POW2, pf, wpe>;
 }
+#ifndef PKVD_MFMA_QLDS
+#define PKVD_MFMA_QLDS 0
+#endif
 template <int D, bool BF16, bool POW2>
 KernelFn mfma_kernel() {
   // a D = 64 block takes half the registers: one more wave per SIMD fits
   constexpr int pf = D == 64 ? PKVD_PF16_D64 : PKVD_PF16;
   constexpr int wpe = D == 64 ? PKVD_WPE16_D64 : PKVD_WPE16;
-  return &decode_kernel<MfmaEngine<D, BF16>, D, BF16, POW2, pf, wpe>;
+  return &decode_kernel<MfmaEngine<D, BF16, PKVD_MFMA_QLDS>, D, BF16, POW2, pf, wpe>;
 }
 
 KernelFn select(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2) {
@@ -406,8 +442,13 @@ bool page_pow2(int ps) { return ps >= kBlockKeys && (ps & (ps - 1)) == 0; }
 
 }  // namespace
 
-// scan scratch, prefix, lengths
-size_t decode_lds_bytes(int B) { return sizeof(int) * ((size_t)kThreads + 2 * (size_t)B + 1); }
+size_t decode_lds_bytes(int B, int path, int head_dim) {
+  int eng = 0;
+  if (path == kPathMfma)
+    eng = head_dim == 128 ? MfmaEngine<128, true, PKVD_MFMA_QLDS>::kLdsBytesPerWave
+                          : MfmaEngine<64, true, PKVD_MFMA_QLDS>::kLdsBytesPerWave;
+  return sizeof(int) * (size_t)lds_layout(eng / 4, B).total;
+}
 
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
                          size_t lds_bytes) {
@@ -425,7 +466,7 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool 
   KernelFn k = select(path, rows_per_tile, a.D, bf16, page_pow2(a.ps));
   if (!k) return hipErrorInvalidValue;
   const dim3 grid((a.num_waves + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B), stream, a);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B, path, a.D), stream, a);
   return hipGetLastError();
 }
 

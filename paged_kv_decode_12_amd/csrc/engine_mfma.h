@@ -19,6 +19,8 @@
 //    rows 4q + i, dims j * DJ .. j * DJ + DJ - 1 of O, all in registers.
 #pragma once
 
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace pkvd {
@@ -36,6 +38,19 @@ __device__ __forceinline__ u32x2 load8_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 #else
   return *reinterpret_cast<const u32x2*>(p);
+#endif
+}
+
+// K rows are read 64 bytes per key per instruction (16 keys per MFMA operand),
+// so each 128-byte line is touched by two instructions in a row
+#ifndef PKVD_MFMA_K_NT
+#define PKVD_MFMA_K_NT 0
+#endif
+__device__ __forceinline__ u32x4 load16_k(const uint16_t* p) {
+#if PKVD_MFMA_K_NT
+  return load16_stream(p);
+#else
+  return *reinterpret_cast<const u32x4*>(p);
 #endif
 }
 
@@ -81,7 +96,7 @@ struct VRow<64> {
   static __device__ __forceinline__ uint32_t word(const T& v, int u) { return v[u]; }
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool QLDS>
 struct MfmaEngine {
   static constexpr int kRows = 16;
   static constexpr int kKeysPerGroup = kBlockKeys;
@@ -92,12 +107,18 @@ struct MfmaEngine {
   static constexpr int kItemDims = DJ;
   static constexpr int kItemLanes = 16;
 
+  // QLDS: the Q operand waits in LDS (4 KB per wave for D = 128) and is read
+  // per block, which frees its registers for loads in flight
+  static constexpr int kLdsBytesPerWave = QLDS ? NC * 64 * 16 : 0;
   struct Lane {
     int j, q, lane;
+    u32x4* qs;     // this wave's Q slots in LDS: [c][lane]
   };
-  struct Q {
+  struct QRegs {
     u32x4 c[NC];   // row j, dims c*32 + 8q .. +8
   };
+  struct QNone {};
+  using Q = typename std::conditional<QLDS, QNone, QRegs>::type;
   struct Buf {
     u32x4 k[NC];                      // key j, dims c*32 + 8q .. +8
     typename VRow<D>::T v[4];         // key 4q + e, dims j*DJ .. +DJ
@@ -108,7 +129,9 @@ struct MfmaEngine {
     int lo, hi;        // row j's visible keys
   };
 
-  static __device__ __forceinline__ Lane lane_of(int lane) { return {lane & 15, lane >> 4, lane}; }
+  static __device__ __forceinline__ Lane lane_of(int lane, int* wave_lds) {
+    return {lane & 15, lane >> 4, lane, reinterpret_cast<u32x4*>(wave_lds)};
+  }
 
   static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg, int R,
                                                  const Lane& ln, Q& q) {
@@ -119,7 +142,11 @@ struct MfmaEngine {
     const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
                          (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.q * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) q.c[c] = live ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 v = live ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
+      if constexpr (QLDS) ln.qs[c * 64 + ln.lane] = v;
+      else q.c[c] = v;
+    }
   }
 
   static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg, int R,
@@ -160,7 +187,7 @@ struct MfmaEngine {
       const uint16_t* vbase = a.v + (int64_t)page * a.v_sp + (int64_t)kvh * a.v_sh + slot0 * D;
       const uint32_t koff = (uint32_t)(jk - j0) * D + ln.q * 8;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) x.k[c] = load16_stream(kbase + koff + c * 32);
+      for (int c = 0; c < NC; ++c) x.k[c] = load16_k(kbase + koff + c * 32);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         x.v[e] = VRow<D>::load(vbase + (uint32_t)(jv[e] - j0) * D + ln.j * DJ);
@@ -171,7 +198,7 @@ struct MfmaEngine {
         const uint16_t* kr = a.k + (int64_t)page * a.k_sp + (int64_t)kvh * a.k_sh +
                              (int64_t)(jk - col * a.ps) * D + ln.q * 8;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) x.k[c] = load16_stream(kr + c * 32);
+        for (int c = 0; c < NC; ++c) x.k[c] = load16_k(kr + c * 32);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -190,7 +217,14 @@ struct MfmaEngine {
     using F = Fmt<BF16>;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) s = Mf::qk(x.k[c], q.c[c], s);
+    for (int c = 0; c < NC; ++c) {
+      // volatile: read per block, not hoisted into registers for the loop
+      if constexpr (QLDS) {
+        const u32x4 qc = reinterpret_cast<volatile u32x4*>(ln.qs)[c * 64 + ln.lane];
+        s = Mf::qk(x.k[c], qc, s);
+      }
+      else s = Mf::qk(x.k[c], q.c[c], s);
+    }
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -225,7 +225,10 @@ struct ValuEngine {
     int lo[RT], hi[RT];   // visible key range per row
   };
 
-  static __device__ __forceinline__ Lane lane_of(int lane) { return {lane / G::LPK, lane % G::LPK}; }
+  static constexpr int kLdsBytesPerWave = 0;
+  static __device__ __forceinline__ Lane lane_of(int lane, int*) {
+    return {lane / G::LPK, lane % G::LPK};
+  }
 
   // Q rows of a tile (rr = tile * RT + r -> token rr / g, head rr % g): the
   // lane's 16-byte piece of each row
