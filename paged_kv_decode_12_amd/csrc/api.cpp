@@ -55,8 +55,11 @@ struct Plan {
   int num_waves;        // waves of the persistent grid
   int min_wave_blocks;  // minimum 16-key blocks per participating wave
   int64_t workgroups;
-  size_t ws_bytes;      // partial states: 2 slots per wave
   int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
+  int merge_kernel;      // 1: cut units are merged by a second kernel
+  // partial-state workspace: LSE block, then (256-byte aligned) outputs and
+  // the request prefix
+  size_t ws_o, ws_pref, ws_bytes;
 };
 
 // Shape checks shared by every entry point.  Returns PKVD_OK or an error.
@@ -132,7 +135,7 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
   }
   const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
   const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
-                                           pkvd::decode_lds_bytes((int)s.B, path, (int)s.D));
+                                           pkvd::decode_lds_bytes((int)s.B));
   if (n > 0) f.blocks_per_cu = n;
   else (void)hipGetLastError();
   return f;
@@ -169,13 +172,25 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
   p.num_waves = (int)nw;
   p.workgroups = (nw + pkvd::kWaves - 1) / pkvd::kWaves;
-  p.ws_bytes = (size_t)(2 * nw * p.rows_per_tile * (s.D + 1) * 4 + 256);
+  // Where cut units leave large partial states (many pieces per unit or wide
+  // tiles: over 32 KB per unit) one wave merging a unit at the end would be
+  // slow; a second kernel merges them all in parallel instead.  Estimated
+  // from shapes only (pieces per unit ~ waves / units + 1).
+  const int64_t pieces = nw / std::max<int64_t>(p.units, 1) + 1;
+  const int64_t unit_bytes = pieces * p.rows_per_tile * s.D * 4;
+  p.merge_kernel = env_int("PKVD_MERGE_KERNEL", unit_bytes > 32768 ? 1 : 0) ? 1 : 0;
+  // two partial slots per wave
+  const size_t slots = (size_t)2 * nw;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  p.ws_o = up(slots * p.rows_per_tile * 4);
+  p.ws_pref = p.ws_o + up(slots * p.rows_per_tile * (size_t)s.D * 4);
+  p.ws_bytes = p.ws_pref + (size_t)(s.B + 1) * 4;
   return p;
 }
 
-// Library-owned split-KV workspace, one per device: fp32 partial states and
-// the per-unit arrival counters.  Counters are zeroed when allocated and every
-// call leaves them at zero (the last split of a unit resets its counter).
+// Library-owned workspace, one per device: fp32 partial states and the
+// per-unit arrival counters.  Counters are zeroed when allocated and every
+// call leaves them at zero (the last piece of a unit resets its counter).
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -294,7 +309,7 @@ int pkvd_reserve_workspace(size_t bytes) {
   g_last_error.clear();
   if (bytes == 0) return PKVD_OK;
   // counters: one per (request, kv head, row tile).  A plan whose partials
-  // fit in `bytes` has at least 2 splits of >= 65 floats per unit, so it
+  // fit in `bytes` has at least 2 slots of >= 65 floats per unit, so it
   // needs at most bytes / 520 counters.
   return ensure_workspace(bytes, (int64_t)(bytes / 512 + 1024), &p, &c);
 }
@@ -394,13 +409,12 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   st = ensure_workspace(p.ws_bytes, p.units, &ws, &a.counters);
   if (st != PKVD_OK) return st;
   a.ws_lse = static_cast<float*>(ws);
-  // partial outputs start 256-byte aligned after the LSE block
-  uintptr_t o = reinterpret_cast<uintptr_t>(a.ws_lse + (size_t)2 * p.num_waves * p.rows_per_tile);
-  o = (o + 255) & ~uintptr_t(255);
-  a.ws_o = reinterpret_cast<float*>(o);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_o);
+  a.ws_pref = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.ws_pref);
+  a.merge_kernel = p.merge_kernel;
   if (env_int("PKVD_LOG", 0))
-    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d\n", p.path,
-            p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks);
+    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d\n",
+            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

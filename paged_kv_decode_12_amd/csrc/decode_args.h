@@ -1,5 +1,5 @@
 // decode_args.h -- launch arguments shared by the host planner (api.cpp) and
-// the device kernels (decode_kernels.hip).  Internal; not part of the C ABI.
+// the device kernels (decode_kernel.hip).  Internal; not part of the C ABI.
 #pragma once
 
 #include <stdint.h>
@@ -11,7 +11,6 @@ namespace pkvd {
 constexpr int kBlockKeys = 16;   // keys per block: the unit a wave loads and scores
 constexpr int kWaves = 4;        // waves per workgroup of the decode kernels
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWavePages = 512;        // block-table columns one wave stages in LDS at a time
 constexpr int kMaxBatch = 8192;        // requests per call (the schedule keeps a prefix in LDS)
 
 enum Path : int { kPathValu = 0, kPathMfma = 1 };
@@ -31,9 +30,13 @@ struct DecodeArgs {
   // outputs
   uint16_t* out;                   // contiguous (B * Lq, Hq, D)
   float* lse;                      // nullptr: not requested
-  float* ws_o;                     // partial states [2 * num_waves][rows_per_tile * D], order set by the engine
-  float* ws_lse;                   // [2 * num_waves][rows_per_tile]
+  // workspace: pieces of units cut by slice boundaries leave a normalised
+  // partial state in slot 2 * wave + side (side 0: the slice's first segment,
+  // 1: its last); the last piece to arrive merges them
+  float* ws_o;                     // [2 * num_waves][rows_per_tile * D], engine order
+  float* ws_lse;                   // [2 * num_waves][rows_per_tile], base 2
   int32_t* counters;               // [B * Hkv * row_tiles] arrival tickets, zero between calls
+  int32_t* ws_pref;                // [B + 1] block prefix of the requests (merge kernel mode)
   // shapes
   int32_t B, Hq, Hkv, g, Lq, ps, P, C, D;
   int32_t window_left;
@@ -41,16 +44,17 @@ struct DecodeArgs {
   int32_t row_tiles;               // row tiles per (request, kv head)
   int32_t num_waves;               // waves of the persistent grid (4 per workgroup)
   int32_t min_wave_blocks;         // a wave gets at least this many blocks (fewer waves run)
+  int32_t merge_kernel;            // 1: cut units are merged by a second kernel, not in place
 #ifdef PKVD_TRACE
   uint64_t* trace;                 // instrumented builds only: [waves][16] timestamps
 #endif
 };
 
-// Launchers (decode_valu.hip).  Return the hipError_t of the launch.
+// Launcher (decode_kernel.hip).  Returns the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,
                          hipStream_t stream);
 // Dynamic LDS bytes of a launch for B requests.
-size_t decode_lds_bytes(int B, int path, int head_dim);
+size_t decode_lds_bytes(int B);
 // Workgroups of the decode kernel that fit on one CU at once (0 on error).
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool page_pow2,
                          size_t lds_bytes);

@@ -228,32 +228,22 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
 // ---------------------------------------------------------------------------
 // balanced persistent schedule
 // ---------------------------------------------------------------------------
-// The work is the linear block space of all units (request b, kv head, row
-// tile) in that order; request b owns [pref[b], pref[b + 1]) and each of its
-// Hkv * row_tiles units holds nblk(b) consecutive blocks.  With T blocks in
-// total and NW waves, wave w owns [floor(w T / NW), floor((w + 1) T / NW)),
-// so every wave streams the same number of blocks (to within one) whatever
-// the mix of sequence lengths.  NW <= T keeps every range non-empty.
+// The work is the linear block space [0, T) of all units (request b, kv head,
+// row tile) in that order: request b owns blocks [pref[b], pref[b + 1]) and
+// each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  With
+// NW waves, wave w owns the slice [w T / NW, (w + 1) T / NW), so every wave
+// streams the same number of blocks (to within one) whatever the mix of
+// sequence lengths; NW <= T keeps every slice non-empty.
 
-__device__ __forceinline__ int64_t wave_begin(int64_t T, int NW, int w) {
-  return T * w / NW;
-}
-// The wave whose range holds linear block x.
-__device__ __forceinline__ int wave_of(int64_t x, int64_t T, int NW) {
-  return (int)(((x + 1) * NW - 1) / T);
-}
-
-// Dynamic LDS of a workgroup, in 32-bit words: the engine's per-wave scratch
-// (kWaves slots of eng_words), the scan scratch (kThreads), the prefix
-// (B + 1) and the raw lengths (B).  Host (launch size) and kernel (carve-up)
-// both take the offsets from here.
+// Dynamic LDS of a workgroup, in 32-bit words: the scan scratch (kThreads),
+// the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
+// (carve-up) both take the offsets from here.
 struct LdsLayout {
-  int eng, scan, pref, nlen, total;
+  int scan, pref, nlen, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int eng_words, int B) {
+__host__ __device__ inline LdsLayout lds_layout(int B) {
   LdsLayout l;
-  l.eng = 0;
-  l.scan = kWaves * eng_words;
+  l.scan = 0;
   l.pref = l.scan + kThreads;
   l.nlen = l.pref + B + 1;
   l.total = l.nlen + B;
@@ -305,11 +295,12 @@ __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, in
 }
 
 // Largest b with pref[b] <= pos (the request holding linear block pos).
+// LDS reads here are wave-uniform (readfirstlane keeps the schedule in SGPRs).
 __device__ __forceinline__ int find_request(const int* s_pref, int B, int64_t pos) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (s_pref[mid] <= pos) lo = mid;
+    if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= pos) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -321,7 +312,7 @@ struct Segment {
   UnitRange u;
   int blk_begin, blk_end;    // absolute 16-key blocks [blk_begin, blk_end)
   int64_t ustart, uend;      // the unit's linear block range
-  bool whole;                // the wave owns the entire unit
+  int whole;                 // the range holds the entire unit (int: stays in registers)
   int side;                  // 0: first segment of the wave, 1: a later one
 };
 
@@ -330,15 +321,16 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
                                           int64_t wave_hi) {
   Segment g;
   g.b = find_request(s_pref, a.B, pos);
-  g.u = unit_range_n(a, s_nlen[g.b]);
+  g.u = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[g.b]));
+  const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[g.b]);
   const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
-  const int64_t off = pos - s_pref[g.b];
+  const int64_t off = pos - pref_b;
   const int per_req = a.Hkv * a.row_tiles;
   int uidx = (int)(off / nb);
   uidx = uidx < 0 ? 0 : (uidx >= per_req ? per_req - 1 : uidx);
   g.kvh = uidx / a.row_tiles;
   g.tile = uidx - g.kvh * a.row_tiles;
-  g.ustart = s_pref[g.b] + (int64_t)uidx * nb;
+  g.ustart = pref_b + (int64_t)uidx * nb;
   g.uend = g.ustart + nb;
   const int64_t seg_end = wave_hi < g.uend ? wave_hi : g.uend;
   g.blk_begin = g.u.first_blk + (int)(pos - g.ustart);

@@ -6,17 +6,21 @@
 // q_len_per_req query tokens, so every K/V byte a wave loads serves all of
 // them (grouped-query packing).
 //
-// Schedule (persistent, balanced): one grid of exactly the resident number of
-// waves.  Each workgroup rebuilds, from seq_lens_kv, the prefix of the linear
-// block space of all units; wave w then streams its own contiguous slice
-// [w T / NW, (w + 1) T / NW) of that space, crossing unit boundaries as
-// needed.  Every wave does the same amount of work whatever the mix of
-// lengths.  A unit wholly inside one wave is written directly; a unit cut by
-// wave boundaries leaves a partial state per piece, and the last piece to
-// arrive (atomic ticket) merges them with the base-2 LSE rule (Note / LSE
-// convention: base-2 LSE states are what the cascade merge consumes).  The
-// ranges come from device data only, so planning never reads the lengths on
-// the host.
+// Schedule (persistent, balanced): one grid of exactly the resident number
+// of waves.  Every workgroup rebuilds, from seq_lens_kv, the prefix of the
+// linear block space of all units, so planning never reads lengths on the
+// host; wave w then streams its own slice [w T / NW, (w + 1) T / NW) of that
+// space, crossing unit boundaries as needed, so every wave does the same
+// amount of work whatever the mix of lengths.  The slice is one continuous
+// stream of chunks: the last round of a chunk already issues the first loads
+// of the next one (next segment included), and the next segment's Q rows are
+// loaded before the current segment's epilogue.  A unit inside one slice is
+// written directly; a unit cut by slice boundaries leaves a normalised
+// partial state (o, base-2 LSE) per piece, and the wave whose piece arrives
+// last (atomic ticket, taken once its slice is streamed) merges the pieces
+// in slice order with the base-2 LSE rule (Note / LSE convention: base-2 LSE
+// states are what the cascade merge consumes).  The merge order is fixed,
+// so results are bitwise repeatable.
 //
 // The per-wave arithmetic comes from an engine: VALU dot products for tiles
 // of up to 8 rows (engine_valu.h), MFMA for 16-row tiles (engine_mfma.h).
@@ -40,9 +44,7 @@
 //    probabilities, packed to bf16/fp16 and multiplied into byte-permuted
 //    (V[k][d], V[k + KPS][d]) pairs with v_dot2; sums l stay in fp32;
 //  * the page ids of the next 128 block-table columns sit in two registers
-//    (one column per lane), read with readlane / ds_bpermute; the next
-//    chunk's page ids and Q rows are fetched before the current segment's
-//    epilogue, and tickets are read only after the whole range is streamed;
+//    (one column per lane), read with readlane / ds_bpermute;
 //  * at a segment's end the KPS streams merge by DPP and lane-pair swaps.
 #include "engine_mfma.h"
 #include "engine_valu.h"
@@ -55,7 +57,7 @@ using namespace dev;
 // Writes one output item (N = 8 or 4 consecutive dims from d0) and, from the
 // row's lead lane, its LSE.
 template <int D, int N, bool BF16>
-__device__ __forceinline__ void store_item(const DecodeArgs& a, int rowhead, int qhead, int d0,
+__device__ __forceinline__ void store_item(const DecodeArgs& a, int64_t rowhead, int qhead, int d0,
                                            bool lead, float M, float L, const float (&O)[8]) {
   uint32_t w[4];
 #pragma unroll
@@ -69,64 +71,87 @@ __device__ __forceinline__ void store_item(const DecodeArgs& a, int rowhead, int
   if (a.lse && lead) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
 }
 
-// Merges the partial states of one unit's pieces (waves w_first .. w_last) for
-// one output item (row r, dims d0 ..) and writes the final values.  Four
-// pieces' loads are in flight at a time; the running max is updated per group
-// of four.
-template <class Eng, int D, bool BF16>
-__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int64_t T, int NW,
-                                             int64_t ustart, int w_first, int w_last,
-                                             const typename Eng::Lane& ln, int r, int d0,
-                                             int rowhead, int qhead) {
-  constexpr int RT = Eng::kRows, N = Eng::kItemDims;
-  float Mx = -INFINITY, W = 0.f, acc[8];
+// Writes one item of a piece's partial state: the normalised output o = O / L
+// (in the engine's lane-contiguous order, with device-coherent stores so the
+// merging wave on another CU reads them after the ticket) and, from the row's
+// lead lane, its base-2 LSE.
+template <class Eng, int D>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
+                                              const typename Eng::Lane& ln, int r, int d0,
+                                              float M, float L, const float (&O)[8]) {
+  constexpr int RT = Eng::kRows;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* po = a.ws_o + (int64_t)slot * RT * D;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int w = w_first; w <= w_last; w += 4) {
-    float l4[4], v4[4][N];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ww = min(w + u, w_last);
-      const int sl = 2 * ww + (wave_begin(T, NW, ww) >= ustart ? 0 : 1);
-      const float lv = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
-      l4[u] = w + u <= w_last ? lv : -INFINITY;
-#pragma unroll
-      for (int e = 0; e < N; ++e)
-        v4[u][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
-    }
-    const float Mn = fmaxf(Mx, fmaxf(fmaxf(l4[0], l4[1]), fmaxf(l4[2], l4[3])));
-    const float sc = rescale(Mx, Mn);
-    W *= sc;
-#pragma unroll
-    for (int e = 0; e < N; ++e) acc[e] *= sc;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wt = rescale(l4[u], Mn);
-      W += wt;
-#pragma unroll
-      for (int e = 0; e < N; ++e) acc[e] = fmaf(wt, v4[u][e], acc[e]);
-    }
-    Mx = Mn;
-  }
-  // acc / W is the merged normalised output; final_value divides by W + sink
-  store_item<D, N, BF16>(a, rowhead, qhead, d0, d0 == 0, Mx, W, acc);
+  for (int e = 0; e < Eng::kItemDims; ++e) store_coherent(po + Eng::pidx(ln, r, e), O[e] * inv);
+  if (d0 == 0) store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
 }
 
-// Issue priority from a wave's progress through its own range: 3 in the first
-// quarter down to 0 in the last.  Waves sharing a SIMD are otherwise served
-// oldest first, so the youngest fall behind and finish last; dropping the
-// priority of the waves that are ahead lets the others catch up, and every
-// wave's equal share then ends at about the same time.
-#ifndef PKVD_PRIO
-#define PKVD_PRIO 0
-#endif
-__device__ __forceinline__ void progress_priority(int done, int q1, int q2, int q3) {
-#if PKVD_PRIO
-  if (done >= q3) __builtin_amdgcn_s_setprio(0);
-  else if (done >= q2) __builtin_amdgcn_s_setprio(1);
-  else if (done >= q1) __builtin_amdgcn_s_setprio(2);
-  else __builtin_amdgcn_s_setprio(3);
-#endif
+// Merges the partial states of one unit's pieces (slices of waves w_first ..
+// w_last, in that order) for all output items of the lane and writes the
+// final values.  kDepth pieces' loads (every item's) are in flight at a time;
+// the running maximum is raised once per group of kDepth pieces.
+template <class Eng, int D, bool BF16>
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, int T, int NW, int64_t ustart,
+                                           int w_first, int w_last, const typename Eng::Lane& ln,
+                                           int tile, int b, int kvh, int R) {
+  constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
+  constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
+  int rr[NI], dd[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) Eng::item_pos(ln, it, rr[it], dd[it]);
+  float Mx[NI], W[NI], acc[NI][8];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    Mx[it] = -INFINITY;
+    W[it] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[it][e] = 0.f;
+  }
+  for (int w = w_first; w <= w_last; w += kDepth) {
+    float lv[kDepth][NI], ov[kDepth][NI][N];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int ww = min(w + u, w_last);
+      const int sl = 2 * ww + ((int64_t)T * ww / NW >= ustart ? 0 : 1);
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int r = rr[it] < RT ? rr[it] : 0;
+        const float l = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
+        lv[u][it] = w + u <= w_last ? l : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+          ov[u][it][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      float Mn = Mx[it];
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, lv[u][it]);
+      const float sc = rescale(Mx[it], Mn);
+      W[it] *= sc;
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[it][e] *= sc;
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const float wt = rescale(lv[u][it], Mn);
+        W[it] += wt;
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[it][e] = fmaf(wt, ov[u][it][e], acc[it][e]);
+      }
+      Mx[it] = Mn;
+    }
+  }
+  // acc / W is the merged normalised output; final_value divides by W + sink
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int r = rr[it], row = tile * RT + r;
+    if (!(r < RT && row < R)) continue;
+    const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
+    store_item<D, N, BF16>(a, ((int64_t)b * a.Lq + ti) * a.Hq + qhead, qhead, dd[it], dd[it] == 0,
+                           Mx[it], W[it], acc[it]);
+  }
 }
 
 template <class Eng, int D, bool BF16, bool PAGE_POW2, int PF, int WPE>
@@ -135,43 +160,46 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int RT = Eng::kRows;
   constexpr int NBUF = PF + 1;
   constexpr int kWindow = 128;                        // block-table columns per chunk
+  constexpr int GPB = Eng::kGroupsPerBlock, KPG = Eng::kKeysPerGroup;
   extern __shared__ int lds[];
-  constexpr int kEngWords = Eng::kLdsBytesPerWave / 4;
-  const LdsLayout L = lds_layout(kEngWords, a.B);
+  const LdsLayout L = lds_layout(a.B);
   int* s_scan = lds + L.scan;
   int* s_pref = lds + L.pref;
   int* s_nlen = lds + L.nlen;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const typename Eng::Lane ln = Eng::lane_of(lane, lds + L.eng + wave * kEngWords);
+  const typename Eng::Lane ln = Eng::lane_of(lane);
+  const int gw = (int)blockIdx.x * kWaves + wave;
 
-  const int gw0 = (int)blockIdx.x * kWaves + wave;
-  PKVD_STAMP(a, gw0, 0);
-  const int64_t T = build_prefix<BF16>(a, s_pref, s_nlen, s_scan);
-  PKVD_STAMP(a, gw0, 1);
+  PKVD_STAMP(a, gw, 0);
+  const int T = uniform(build_prefix<BF16>(a, s_pref, s_nlen, s_scan));
+  PKVD_STAMP(a, gw, 1);
+  if (a.merge_kernel && blockIdx.x == 0)   // the prefix, for the merge kernel
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) a.ws_pref[i] = s_pref[i];
   if (T == 0) return;
   // waves that take part: at most one per min_wave_blocks blocks (and <= T)
-  int64_t nw = T / a.min_wave_blocks;
+  int nw = T / a.min_wave_blocks;
   nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
-  const int NW = (int)nw;
-  const int gw = (int)blockIdx.x * kWaves + wave;
+  const int NW = nw;
   if (gw >= NW) return;
-  const int64_t lo = wave_begin(T, NW, gw), hi = wave_begin(T, NW, gw + 1);
-  // progress in key groups, for the issue priority
-  const int total_groups = (int)(hi - lo) * Eng::kGroupsPerBlock;
-  const int q1 = total_groups / 4, q2 = total_groups / 2, q3 = 3 * total_groups / 4;
-  int groups_done = 0;
+  const int lo = (int)((int64_t)T * gw / NW), hi = (int)((int64_t)T * (gw + 1) / NW);
   const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
   const int chunk_blocks = max(1, ((kWindow - 2) * a.ps + 1) / kBlockKeys);
 
-  // A chunk: blocks [cb, ce) of segment sg (a unit's slice of this wave's range).
+  // The slice is one stream of chunks: blocks [cb, ce) of a segment (a unit's
+  // part of the slice), at most chunk_blocks long so its page ids fit the
+  // 128-column window.  Each chunk is padded to a whole number of rounds of
+  // NBUF groups (the padding groups are loaded again from the chunk and not
+  // scored), so group g of every chunk lives in buf[g % NBUF] and the last
+  // round of a chunk issues the first loads of the next one.
   struct Chunk {
     Segment sg;
-    int cb, ce, kb, ke;
-    bool first, last;   // first / last chunk of its segment
+    int cb, ce, kb, ke;   // blocks and keys
+    int ng, ngp;          // groups, and groups padded to rounds
+    int first, last, valid;   // ints, not bools: copies of the struct stay in registers
   };
   auto make_chunk = [&](const Segment& sg, int cb) {
     Chunk c;
@@ -180,9 +208,24 @@ void decode_kernel(const DecodeArgs a) {
     c.ce = min(sg.blk_end, cb + chunk_blocks);
     c.kb = max(sg.u.key_lo, cb * kBlockKeys);
     c.ke = min(sg.u.n, c.ce * kBlockKeys);
+    c.ng = (c.ce - c.cb) * GPB;
+    c.ngp = (c.ng + NBUF - 1) / NBUF * NBUF;
     c.first = cb == sg.blk_begin;
     c.last = c.ce == sg.blk_end;
+    c.valid = 1;
     return c;
+  };
+  // the chunk after c: the same segment's next one, or the next segment's first
+  auto next_chunk = [&](const Chunk& c) {
+    if (!c.last) return make_chunk(c.sg, c.ce);
+    const int64_t pos = c.sg.ustart + (c.sg.blk_end - c.sg.u.first_blk);
+    if (pos >= hi) {
+      Chunk n = c;
+      n.valid = 0;
+      return n;
+    }
+    const Segment sg = locate(a, s_pref, s_nlen, pos, lo, hi);
+    return make_chunk(sg, sg.blk_begin);
   };
   // page ids of a chunk's columns, clamped into the pool (issued early)
   auto fetch_pages = [&](const Chunk& c) {
@@ -196,135 +239,115 @@ void decode_kernel(const DecodeArgs a) {
     w.p1 = (unsigned)p1 < (unsigned)a.P ? p1 : a.P - 1;
     return w;
   };
-  // pieces of units shared with other waves: at most the first and the last
-  // segment of the range; their tickets are read after the range is done
-  int pend_prev[2] = {-1, -1}, pend_unit[2] = {0, 0};
+  // pieces of units shared with other waves: at most the slice's first and
+  // last segments; their tickets are taken after the slice is streamed
+  int pend_unit[2] = {-1, -1}, pend_b[2] = {0, 0}, pend_kvh[2] = {0, 0}, pend_tile[2] = {0, 0};
   int64_t pend_ustart[2] = {0, 0}, pend_uend[2] = {0, 0};
-  int pend_tile[2] = {0, 0}, pend_b[2] = {0, 0}, pend_kvh[2] = {0, 0};
 
-  const Segment sg0 = locate(a, s_pref, s_nlen, lo, lo, hi);
-  Chunk ch = make_chunk(sg0, sg0.blk_begin);
-  PageWindow pw = fetch_pages(ch);
-  typename Eng::Q qr;
-
-  typename Eng::State st;
-  int max_lo = 0, min_hi = 0;
 #ifdef PKVD_TRACE
   int n_seg = 0, n_chunk = 0, n_blk = 0;
 #endif
+  Chunk cur;
+  {
+    const Segment sg = locate(a, s_pref, s_nlen, lo, lo, hi);
+    cur = make_chunk(sg, sg.blk_begin);
+  }
+  PageWindow pw = fetch_pages(cur);
+  Chunk nxt = next_chunk(cur);
+  PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
+  typename Eng::Q qr;
+  typename Eng::State st;
+  int max_lo = 0, min_hi = 0;
+  typename Eng::Buf buf[NBUF];
+  // loads of group g of chunk c (clamped to its last group)
+  auto load_group = [&](typename Eng::Buf& x, const Chunk& c, const PageWindow& w, int g) {
+    Eng::template load<PAGE_POW2>(x, a, c.sg.kvh, c.cb * GPB + min(g, c.ng - 1), c.kb, c.ke, w,
+                                  ps_shift, ln);
+  };
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
+  Eng::fetch_q(a, cur.sg, R, ln, qr);
+  Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
   PKVD_STAMP(a, gw, 2);
-  for (;;) {
-    const Segment& sg = ch.sg;
-    if (ch.first) Eng::reset(a, sg, R, ln, st, max_lo, min_hi);
 
-    // stream the chunk's key groups with loads PF groups ahead
+  for (;;) {
 #ifdef PKVD_TRACE
-    if (n_chunk == 0) PKVD_STAMP(a, gw, 3);
     n_chunk++;
-    n_blk += ch.ce - ch.cb;
+    n_blk += cur.ce - cur.cb;
 #endif
     {
-      constexpr int GPB = Eng::kGroupsPerBlock, KPG = Eng::kKeysPerGroup;
-      const int g0 = ch.cb * GPB, ng = (ch.ce - ch.cb) * GPB;
-      const int kb = ch.kb, ke = ch.ke, kvh = sg.kvh;
-      typename Eng::Buf buf[NBUF];
-      auto grp_of = [&](int i) { return g0 + min(i, ng - 1); };
-      auto score = [&](const typename Eng::Buf& x, int i) {
-        const int j0 = (g0 + i) * KPG;
-        const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
-        Eng::score(st, x, qr, a.scale_log2, full, j0, ln);
+      const int g0 = cur.cb * GPB;
+      const int rounds = cur.ngp / NBUF;
+      auto score = [&](int s, int i) {
+        if (i < cur.ng) {   // padding groups are not scored
+          const int j0 = (g0 + i) * KPG;
+          const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
+          Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
+        }
       };
-#pragma unroll
-      for (int s = 0; s < PF; ++s)
-        Eng::template load<PAGE_POW2>(buf[s], a, kvh, grp_of(s), kb, ke, pw, ps_shift, ln);
-      // the segment's Q rows, after the first loads so their wait overlaps them
-      if (ch.first) Eng::fetch_q(a, sg, R, ln, qr);
-      // full rounds: each sub-step issues the loads of the group PF ahead (the
-      // last group again near the end: a cache hit), then scores its own group
-      const int rounds = ng / NBUF;
-      for (int rd = 0; rd < rounds; ++rd) {
-        progress_priority(groups_done + rd * NBUF, q1, q2, q3);
+      // each sub-step issues the loads of the group PF ahead, then scores its own
+      for (int rd = 0; rd + 1 < rounds; ++rd) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
-          const int i = rd * NBUF + s;
-          Eng::template load<PAGE_POW2>(buf[(s + PF) % NBUF], a, kvh, grp_of(i + PF), kb, ke,
-                                        pw, ps_shift, ln);
-          score(buf[s], i);
+          load_group(buf[(s + PF) % NBUF], cur, pw, rd * NBUF + s + PF);
+          score(s, rd * NBUF + s);
         }
       }
-      // tail: the remaining ng % NBUF <= PF groups are already in flight
-      const int i0 = rounds * NBUF;
+      // last round: sub-steps s >= NBUF - PF load groups s + PF - NBUF of the
+      // next chunk (at the end of the slice: this chunk's last group again)
+      const Chunk& lc = nxt.valid ? nxt : cur;
+      const PageWindow lw = nxt.valid ? pwn : pw;
+      const int i0 = (rounds - 1) * NBUF;
 #pragma unroll
-      for (int s = 0; s < PF; ++s)
-        if (i0 + s < ng) score(buf[s], i0 + s);
-      groups_done += ng;
-    }
-
-#ifdef PKVD_TRACE
-    if (n_chunk == 1) PKVD_STAMP(a, gw, 4);
-#endif
-    if (!ch.last) {            // next chunk of the same segment
-      ch = make_chunk(sg, ch.ce);
-      pw = fetch_pages(ch);
-      continue;
-    }
-
-    // the segment is done: finish it
-    Eng::finish(st, ln);
-    if (sg.whole) {
-#pragma unroll
-      for (int k = 0; k < Eng::kItems; ++k) {
-        int r, d0;
-        float M, L, O[8];
-        const bool ok = Eng::item(st, ln, k, r, d0, M, L, O);
-        const int row = sg.tile * RT + r;
-        if (ok && row < R) {
-          const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
-          store_item<D, Eng::kItemDims, BF16>(a, (sg.b * a.Lq + ti) * a.Hq + qhead, qhead, d0,
-                                              d0 == 0, M, L, O);
-        }
+      for (int s = 0; s < NBUF; ++s) {
+        if (s + PF < NBUF) load_group(buf[(s + PF) % NBUF], cur, pw, i0 + s + PF);
+        else load_group(buf[(s + PF) % NBUF], lc, lw, nxt.valid ? s + PF - NBUF : cur.ng - 1);
+        score(s, i0 + s);
       }
-    } else {
-      // a piece of a unit shared with other waves: leave the partial state,
-      // then take a ticket (its value is read once the range is done)
+    }
+    if (cur.last) {
+      // the segment is done.  The next segment's Q rows are loaded first, so
+      // their latency overlaps this epilogue (its first groups are in flight)
+      if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
+      // the whole unit's output, or this piece's partial
+      const Segment& sg = cur.sg;
+      Eng::finish(st, ln);
       const int slot = 2 * gw + sg.side;
 #pragma unroll
-      for (int k = 0; k < Eng::kItems; ++k) {
+      for (int it = 0; it < Eng::kItems; ++it) {
         int r, d0;
-        float M, L, O[8];
-        const bool ok = Eng::item(st, ln, k, r, d0, M, L, O);
-        if (ok) {
-          float* po = a.ws_o + (int64_t)slot * RT * D;
-#pragma unroll
-          for (int e = 0; e < Eng::kItemDims; ++e)
-            store_coherent(po + Eng::pidx(ln, r, e), L > 0.f ? O[e] / L : 0.f);
-          if (d0 == 0)
-            store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
+        float M, Lsum, O[8];
+        const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
+        if (sg.whole) {
+          const int row = sg.tile * RT + r;
+          if (ok && row < R) {
+            const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
+            store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
+                                                qhead, d0, d0 == 0, M, Lsum, O);
+          }
+        } else if (ok) {
+          store_partial<Eng, D>(a, slot, ln, r, d0, M, Lsum, O);
         }
       }
-      // the ticket is taken once the whole range is streamed, when these
-      // stores have long completed (no wait for them here)
-      const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
-      auto remember = [&](int k) {
-        pend_prev[k] = 0;
-        pend_unit[k] = unit;
-        pend_ustart[k] = sg.ustart;
-        pend_uend[k] = sg.uend;
-        pend_tile[k] = sg.tile;
+      if (!sg.whole) {
+        const int k = sg.side;
+        pend_unit[k] = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
         pend_b[k] = sg.b;
         pend_kvh[k] = sg.kvh;
-      };
-      if (sg.side == 0) remember(0);
-      else remember(1);
-    }
+        pend_tile[k] = sg.tile;
+        pend_ustart[k] = sg.ustart;
+        pend_uend[k] = sg.uend;
+      }
 #ifdef PKVD_TRACE
-    if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
+      if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
 #endif
-    const int64_t next = sg.ustart + (sg.blk_end - sg.u.first_blk);
-    if (next >= hi) break;
-    const Segment ns = locate(a, s_pref, s_nlen, next, lo, hi);
-    ch = make_chunk(ns, ns.blk_begin);
-    pw = fetch_pages(ch);
+    }
+    if (!nxt.valid) break;
+    cur = nxt;
+    pw = pwn;
+    if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+    nxt = next_chunk(cur);
+    if (nxt.valid) pwn = fetch_pages(nxt);
   }
 
   PKVD_STAMP(a, gw, 6);
@@ -338,44 +361,127 @@ void decode_kernel(const DecodeArgs a) {
     PKVD_COUNT(a, gw, 11, ((uint64_t)xcc << 32) | hwid);
   }
 #endif
-  // tickets of the pieces this wave left: partial stores complete first
+  if (a.merge_kernel) return;   // the merge kernel takes the pieces
+  // tickets of the pieces this wave left: its partial stores complete first
   __builtin_amdgcn_s_waitcnt(0);
+  int prev[2] = {0, 0};
 #pragma unroll
-  for (int side = 0; side < 2; ++side)
-    if (pend_prev[side] >= 0 && lane == 0) pend_prev[side] = atomicAdd(&a.counters[pend_unit[side]], 1);
-  // merge the units whose last piece this wave delivered (at the top issue
-  // priority: the kernel's end waits on these)
-#if PKVD_PRIO
-  __builtin_amdgcn_s_setprio(3);
-#endif
+  for (int k = 0; k < 2; ++k)
+    if (pend_unit[k] >= 0 && lane == 0) prev[k] = atomicAdd(&a.counters[pend_unit[k]], 1);
+  // merge the units whose last piece this wave delivered
 #pragma unroll
-  for (int side = 0; side < 2; ++side) {
-    const int unit = pend_unit[side];
-    const bool had = uniform(pend_prev[side] >= 0 ? 1 : 0) != 0;
-    if (!had) continue;
-    const int w_first = wave_of(pend_ustart[side], T, NW);
-    const int w_last = wave_of(pend_uend[side] - 1, T, NW);
-    const int prev = uniform(pend_prev[side]);
-    if (prev != w_last - w_first) continue;
-    if (lane == 0) a.counters[unit] = 0;   // ready for the next call
-#pragma unroll
-    for (int k = 0; k < Eng::kItems; ++k) {
-      int r, d0;
-      Eng::item_pos(ln, k, r, d0);
-      const int row = pend_tile[side] * RT + r;
-      if (!(r < RT && row < R)) continue;
-      const int ti = row / a.g, qhead = pend_kvh[side] * a.g + (row - ti * a.g);
-      merge_pieces<Eng, D, BF16>(a, T, NW, pend_ustart[side], w_first, w_last, ln, r, d0,
-                                 (pend_b[side] * a.Lq + ti) * a.Hq + qhead, qhead);
-    }
+  for (int k = 0; k < 2; ++k) {
+    if (pend_unit[k] < 0) continue;
+    const int w_first = (int)(((pend_ustart[k] + 1) * NW - 1) / T);
+    const int w_last = (int)((pend_uend[k] * NW - 1) / T);
+    if (uniform(prev[k]) != w_last - w_first) continue;
+    if (lane == 0) a.counters[pend_unit[k]] = 0;   // ready for the next call
+    merge_unit<Eng, D, BF16>(a, T, NW, pend_ustart[k], w_first, w_last, ln, pend_tile[k],
+                             pend_b[k], pend_kvh[k], R);
   }
   PKVD_STAMP(a, gw, 7);
+}
+
+// Merge kernel (for plans whose cut units leave large partial states): one
+// wave per (unit, row of its tile), launched after the decode kernel.  Lane p
+// reads piece p's LSE (64 pieces at a time), the batch maximum and the weights
+// 2^(lse - max) come from wave reductions, and every lane accumulates its
+// D / 64 output dims over the pieces in slice order, eight pieces' loads in
+// flight.  Each lane owns its dims, so every sum has a fixed order and the
+// result is the same in every run.  Writes out (sink in the denominator) and
+// the base-2 LSE.
+constexpr int kMergeWaves = 4;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <class Eng, int D, bool BF16>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a) {
+  constexpr int RT = Eng::kRows, NDL = D / 64;   // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int pair = (int)blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
+  const int per_req = a.Hkv * a.row_tiles;
+  const int unit = pair / RT, r = pair - unit * RT;
+  const int b = unit / per_req, uidx = unit - b * per_req;
+  if (b >= a.B) return;
+  const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
+  const int row = tile * RT + r;
+  if (row >= a.g * a.Lq) return;
+  const UnitRange u = unit_range(a, b);
+  if (u.nblk == 0) return;
+  const int T = a.ws_pref[a.B];
+  int nw = T / a.min_wave_blocks;
+  nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
+  const int NW = nw;
+  const int us = a.ws_pref[b] + uidx * u.nblk, ue = us + u.nblk;
+  const int w_first = (int)(((int64_t)(us + 1) * NW - 1) / T);
+  const int w_last = (int)(((int64_t)ue * NW - 1) / T);
+  if (ue > T || w_first == w_last) return;   // whole: the decode kernel wrote it
+  const int n = w_last - w_first + 1;
+  float M = -INFINITY, W = 0.f, acc[NDL];
+#pragma unroll
+  for (int e = 0; e < NDL; ++e) acc[e] = 0.f;
+  int pos[NDL];
+#pragma unroll
+  for (int e = 0; e < NDL; ++e) pos[e] = Eng::ppos(r, lane * NDL + e);
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int nb = min(64, n - p0);
+    int slot = 0;
+    float l = -INFINITY;
+    if (lane < nb) {
+      const int w = w_first + p0 + lane;
+      slot = 2 * w + ((int64_t)T * w / NW >= us ? 0 : 1);
+      l = a.ws_lse[(int64_t)slot * RT + r];
+    }
+    const float Mn = fmaxf(M, wave_max(l));
+    const float wt = lane < nb ? rescale(l, Mn) : 0.f;
+    const float sc = rescale(M, Mn);
+    W = W * sc + wave_sum(wt);
+#pragma unroll
+    for (int e = 0; e < NDL; ++e) acc[e] *= sc;
+    M = Mn;
+    constexpr int kDepth = 8;
+    for (int q0 = 0; q0 < nb; q0 += kDepth) {   // uniform: every lane shuffles
+      float wq[kDepth], oq[kDepth][NDL];
+#pragma unroll
+      for (int e = 0; e < kDepth; ++e) {
+        const int q = q0 + e < nb ? q0 + e : 0;
+        wq[e] = q0 + e < nb ? __shfl(wt, q) : 0.f;
+        const float* po = a.ws_o + (int64_t)__shfl(slot, q) * RT * D;
+#pragma unroll
+        for (int x = 0; x < NDL; ++x) oq[e][x] = po[pos[x]];
+      }
+#pragma unroll
+      for (int e = 0; e < kDepth; ++e)
+#pragma unroll
+        for (int x = 0; x < NDL; ++x) acc[x] = fmaf(wq[e], oq[e][x], acc[x]);
+    }
+  }
+  const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
+  const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
+  // acc / W is the merged normalised output; final_value divides by W + sink
+  if constexpr (NDL == 2) {
+    *reinterpret_cast<uint32_t*>(a.out + rowhead * D + 2 * lane) =
+        Fmt<BF16>::pack2(final_value<BF16>(a, qhead, M, W, acc[0]),
+                         final_value<BF16>(a, qhead, M, W, acc[1]));
+  } else {
+    a.out[rowhead * D + lane] = Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, W, acc[0]));
+  }
+  if (a.lse && lane == 0) a.lse[rowhead] = W > 0.f ? M + log2f(W) : -INFINITY;
 }
 
 // blocks in flight ahead of the scoring, and waves per SIMD the register
 // budget is fitted to, per engine
 #ifndef PKVD_PF4
-#define PKVD_PF4 2
+#define PKVD_PF4 1
 #endif
 #ifndef PKVD_WPE4
 #define PKVD_WPE4 3
@@ -407,15 +513,12 @@ KernelFn valu_kernel() {
   constexpr int wpe = RT == 4 ? PKVD_WPE4 : PKVD_WPE8;
   return &decode_kernel<ValuEngine<D, RT, BF16>, D, BF16, POW2, pf, wpe>;
 }
-#ifndef PKVD_MFMA_QLDS
-#define PKVD_MFMA_QLDS 0
-#endif
 template <int D, bool BF16, bool POW2>
 KernelFn mfma_kernel() {
   // a D = 64 block takes half the registers: one more wave per SIMD fits
   constexpr int pf = D == 64 ? PKVD_PF16_D64 : PKVD_PF16;
   constexpr int wpe = D == 64 ? PKVD_WPE16_D64 : PKVD_WPE16;
-  return &decode_kernel<MfmaEngine<D, BF16, PKVD_MFMA_QLDS>, D, BF16, POW2, pf, wpe>;
+  return &decode_kernel<MfmaEngine<D, BF16>, D, BF16, POW2, pf, wpe>;
 }
 
 KernelFn select(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2) {
@@ -438,17 +541,29 @@ KernelFn select(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2)
   return nullptr;
 }
 
+using MergeFn = void (*)(DecodeArgs);
+
+MergeFn select_merge(int path, int rows_per_tile, int head_dim, bool bf16) {
+#define PKVD_SELM(D, BF)                                                               \
+  if (head_dim == D && bf16 == BF) {                                                  \
+    if (path == kPathMfma) return rows_per_tile == 16 ? &merge_kernel<MfmaEngine<D, BF>, D, BF> : nullptr; \
+    if (rows_per_tile == 4) return &merge_kernel<ValuEngine<D, 4, BF>, D, BF>;        \
+    if (rows_per_tile == 8) return &merge_kernel<ValuEngine<D, 8, BF>, D, BF>;        \
+    return nullptr;                                                                   \
+  }
+  PKVD_SELM(128, true)
+  PKVD_SELM(128, false)
+  PKVD_SELM(64, true)
+  PKVD_SELM(64, false)
+#undef PKVD_SELM
+  return nullptr;
+}
+
 bool page_pow2(int ps) { return ps >= kBlockKeys && (ps & (ps - 1)) == 0; }
 
 }  // namespace
 
-size_t decode_lds_bytes(int B, int path, int head_dim) {
-  int eng = 0;
-  if (path == kPathMfma)
-    eng = head_dim == 128 ? MfmaEngine<128, true, PKVD_MFMA_QLDS>::kLdsBytesPerWave
-                          : MfmaEngine<64, true, PKVD_MFMA_QLDS>::kLdsBytesPerWave;
-  return sizeof(int) * (size_t)lds_layout(eng / 4, B).total;
-}
+size_t decode_lds_bytes(int B) { return sizeof(int) * (size_t)lds_layout(B).total; }
 
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
                          size_t lds_bytes) {
@@ -466,7 +581,15 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool 
   KernelFn k = select(path, rows_per_tile, a.D, bf16, page_pow2(a.ps));
   if (!k) return hipErrorInvalidValue;
   const dim3 grid((a.num_waves + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B, path, a.D), stream, a);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B), stream, a);
+  if (!a.merge_kernel) return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeFn m = select_merge(path, rows_per_tile, a.D, bf16);
+  if (!m) return hipErrorInvalidValue;
+  const int pairs = a.B * a.Hkv * a.row_tiles * rows_per_tile;   // (unit, row) pairs
+  hipLaunchKernelGGL(m, dim3((pairs + kMergeWaves - 1) / kMergeWaves), dim3(64 * kMergeWaves), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

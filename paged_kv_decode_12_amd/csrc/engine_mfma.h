@@ -19,8 +19,6 @@
 //    rows 4q + i, dims j * DJ .. j * DJ + DJ - 1 of O, all in registers.
 #pragma once
 
-#include <type_traits>
-
 #include "decode_common.h"
 
 namespace pkvd {
@@ -96,7 +94,7 @@ struct VRow<64> {
   static __device__ __forceinline__ uint32_t word(const T& v, int u) { return v[u]; }
 };
 
-template <int D, bool BF16, bool QLDS>
+template <int D, bool BF16>
 struct MfmaEngine {
   static constexpr int kRows = 16;
   static constexpr int kKeysPerGroup = kBlockKeys;
@@ -107,18 +105,12 @@ struct MfmaEngine {
   static constexpr int kItemDims = DJ;
   static constexpr int kItemLanes = 16;
 
-  // QLDS: the Q operand waits in LDS (4 KB per wave for D = 128) and is read
-  // per block, which frees its registers for loads in flight
-  static constexpr int kLdsBytesPerWave = QLDS ? NC * 64 * 16 : 0;
   struct Lane {
     int j, q, lane;
-    u32x4* qs;     // this wave's Q slots in LDS: [c][lane]
   };
-  struct QRegs {
+  struct Q {
     u32x4 c[NC];   // row j, dims c*32 + 8q .. +8
   };
-  struct QNone {};
-  using Q = typename std::conditional<QLDS, QNone, QRegs>::type;
   struct Buf {
     u32x4 k[NC];                      // key j, dims c*32 + 8q .. +8
     typename VRow<D>::T v[4];         // key 4q + e, dims j*DJ .. +DJ
@@ -129,9 +121,7 @@ struct MfmaEngine {
     int lo, hi;        // row j's visible keys
   };
 
-  static __device__ __forceinline__ Lane lane_of(int lane, int* wave_lds) {
-    return {lane & 15, lane >> 4, lane, reinterpret_cast<u32x4*>(wave_lds)};
-  }
+  static __device__ __forceinline__ Lane lane_of(int lane) { return {lane & 15, lane >> 4, lane}; }
 
   static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg, int R,
                                                  const Lane& ln, Q& q) {
@@ -142,11 +132,7 @@ struct MfmaEngine {
     const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
                          (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.q * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x4 v = live ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
-      if constexpr (QLDS) ln.qs[c * 64 + ln.lane] = v;
-      else q.c[c] = v;
-    }
+    for (int c = 0; c < NC; ++c) q.c[c] = live ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
   }
 
   static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg, int R,
@@ -217,14 +203,7 @@ struct MfmaEngine {
     using F = Fmt<BF16>;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      // volatile: read per block, not hoisted into registers for the loop
-      if constexpr (QLDS) {
-        const u32x4 qc = reinterpret_cast<volatile u32x4*>(ln.qs)[c * 64 + ln.lane];
-        s = Mf::qk(x.k[c], qc, s);
-      }
-      else s = Mf::qk(x.k[c], q.c[c], s);
-    }
+    for (int c = 0; c < NC; ++c) s = Mf::qk(x.k[c], q.c[c], s);
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,6 +282,8 @@ struct MfmaEngine {
   static __device__ __forceinline__ int pidx(const Lane& ln, int r, int e) {
     return (r * DJ + e) * 16 + ln.j;
   }
+  // The same index for element (row r, dim d): d = j * DJ + e
+  static __device__ __forceinline__ int ppos(int r, int d) { return (r * DJ + d % DJ) * 16 + d / DJ; }
 };
 
 }  // namespace dev

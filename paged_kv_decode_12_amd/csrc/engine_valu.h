@@ -225,10 +225,7 @@ struct ValuEngine {
     int lo[RT], hi[RT];   // visible key range per row
   };
 
-  static constexpr int kLdsBytesPerWave = 0;
-  static __device__ __forceinline__ Lane lane_of(int lane, int*) {
-    return {lane / G::LPK, lane % G::LPK};
-  }
+  static __device__ __forceinline__ Lane lane_of(int lane) { return {lane / G::LPK, lane % G::LPK}; }
 
   // Q rows of a tile (rr = tile * RT + r -> token rr / g, head rr % g): the
   // lane's 16-byte piece of each row
@@ -314,6 +311,8 @@ struct ValuEngine {
   static __device__ __forceinline__ int pidx(const Lane& ln, int r, int e) {
     return (r * 8 + e) * G::LPK + ln.part;
   }
+  // The same index for element (row r, dim d): d = part * 8 + e
+  static __device__ __forceinline__ int ppos(int r, int d) { return (r * 8 + (d & 7)) * G::LPK + (d >> 3); }
 };
 
 }  // namespace dev

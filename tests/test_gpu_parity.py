@@ -120,6 +120,10 @@ SCHEDULES = {
     # the other engine than the planner picks (MFMA for < 16 rows, VALU for >= 16)
     "mfma_cut7": {"PKVD_FORCE_PATH": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "valu": {"PKVD_FORCE_PATH": "0"},
+    # cut units merged by the second kernel instead of by their last piece
+    "mk_cut7": {"PKVD_MERGE_KERNEL": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    "mk_mfma_cut64": {"PKVD_MERGE_KERNEL": "1", "PKVD_FORCE_PATH": "1", "PKVD_WAVES": "64",
+                      "PKVD_MIN_WAVE_BLOCKS": "1"},
 }
 
 
@@ -158,6 +162,24 @@ def test_config_other_engine(name, path):
     finally:
         os.environ.pop("PKVD_FORCE_PATH", None)
     compare(f"{name}/path{path}", out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("name,mode", [("llama3_8b", "1"), ("long_ctx", "0"), ("spec_verify", "0"),
+                                       ("sink_window", "1")])
+def test_config_other_merge(name, mode):
+    """Full-size configs with the merge mode the planner does not pick for them."""
+    log(f"[merge] config={name} PKVD_MERGE_KERNEL={mode}")
+    inp, (ref_out, ref_lse, _) = config_inputs(name)
+    d = to_dev(inp)
+    os.environ["PKVD_MERGE_KERNEL"] = mode
+    try:
+        out, lse = run_gpu(d, lse=True)
+        out2, lse2 = run_gpu(d, lse=True)
+    finally:
+        os.environ.pop("PKVD_MERGE_KERNEL", None)
+    compare(f"{name}/merge{mode}", out, lse, ref_out, ref_lse)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
 
 
 def test_determinism_and_schedule_invariance():
