@@ -235,6 +235,14 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
 // streams the same number of blocks (to within one) whatever the mix of
 // sequence lengths; NW <= T keeps every slice non-empty.
 
+// First block of wave w's slice, and the wave whose slice holds block x.
+__device__ __forceinline__ int slice_begin(int T, int NW, int w) {
+  return (int)((int64_t)T * w / NW);
+}
+__device__ __forceinline__ int slice_of(int T, int NW, int64_t x) {
+  return (int)(((x + 1) * NW - 1) / T);
+}
+
 // Dynamic LDS of a workgroup, in 32-bit words: the scan scratch (kThreads),
 // the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
 // (carve-up) both take the offsets from here.

@@ -113,7 +113,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int T, int NW, i
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int ww = min(w + u, w_last);
-      const int sl = 2 * ww + ((int64_t)T * ww / NW >= ustart ? 0 : 1);
+      const int sl = 2 * ww + (slice_begin(T, NW, ww) >= ustart ? 0 : 1);
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         const int r = rr[it] < RT ? rr[it] : 0;
@@ -183,7 +183,7 @@ void decode_kernel(const DecodeArgs a) {
   nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
   const int NW = nw;
   if (gw >= NW) return;
-  const int lo = (int)((int64_t)T * gw / NW), hi = (int)((int64_t)T * (gw + 1) / NW);
+  const int lo = slice_begin(T, NW, gw), hi = slice_begin(T, NW, gw + 1);
   const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
@@ -245,7 +245,8 @@ void decode_kernel(const DecodeArgs a) {
   int64_t pend_ustart[2] = {0, 0}, pend_uend[2] = {0, 0};
 
 #ifdef PKVD_TRACE
-  int n_seg = 0, n_chunk = 0, n_blk = 0;
+  int n_seg = 0, n_chunk = 0, n_blk = 0, g_done = 0, quart = 1;
+  const int g_total = (hi - lo) * GPB;
 #endif
   Chunk cur;
   {
@@ -283,6 +284,13 @@ void decode_kernel(const DecodeArgs a) {
           const int j0 = (g0 + i) * KPG;
           const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
           Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
+#ifdef PKVD_TRACE
+          // progress stamps at 1/4, 1/2, 3/4 of the slice (trace slots 13..15)
+          if (++g_done * 4 >= quart * g_total && quart < 4) {
+            PKVD_STAMP(a, gw, 12 + quart);
+            quart++;
+          }
+#endif
         }
       };
       // each sub-step issues the loads of the group PF ahead, then scores its own
@@ -372,8 +380,8 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     if (pend_unit[k] < 0) continue;
-    const int w_first = (int)(((pend_ustart[k] + 1) * NW - 1) / T);
-    const int w_last = (int)((pend_uend[k] * NW - 1) / T);
+    const int w_first = slice_of(T, NW, pend_ustart[k]);
+    const int w_last = slice_of(T, NW, pend_uend[k] - 1);
     if (uniform(prev[k]) != w_last - w_first) continue;
     if (lane == 0) a.counters[pend_unit[k]] = 0;   // ready for the next call
     merge_unit<Eng, D, BF16>(a, T, NW, pend_ustart[k], w_first, w_last, ln, pend_tile[k],
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
   const int NW = nw;
   const int us = a.ws_pref[b] + uidx * u.nblk, ue = us + u.nblk;
-  const int w_first = (int)(((int64_t)(us + 1) * NW - 1) / T);
-  const int w_last = (int)(((int64_t)ue * NW - 1) / T);
+  const int w_first = slice_of(T, NW, us);
+  const int w_last = slice_of(T, NW, ue - 1);
   if (ue > T || w_first == w_last) return;   // whole: the decode kernel wrote it
   const int n = w_last - w_first + 1;
   float M = -INFINITY, W = 0.f, acc[NDL];
@@ -438,7 +446,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     float l = -INFINITY;
     if (lane < nb) {
       const int w = w_first + p0 + lane;
-      slot = 2 * w + ((int64_t)T * w / NW >= us ? 0 : 1);
+      slot = 2 * w + (slice_begin(T, NW, w) >= us ? 0 : 1);
       l = a.ws_lse[(int64_t)slot * RT + r];
     }
     const float Mn = fmaxf(M, wave_max(l));
