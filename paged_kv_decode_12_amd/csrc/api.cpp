@@ -57,10 +57,26 @@ struct Plan {
   int64_t workgroups;
   int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
   int merge_kernel;      // 1: cut units are merged by a second kernel
-  // partial-state workspace: LSE block, then (256-byte aligned) outputs and
-  // the request prefix
-  size_t ws_o, ws_pref, ws_bytes;
+  int tail_tasks;        // tail tasks per slice shared with the partner wave (0: none)
+  int tail_q;            // the tail's share of a slice, in sixteenths
+  int tail_owner_max;    // tail tasks a wave may claim for itself
+  int rank_waves;        // waves per dispatch rank
+  int rank_w[4];         // slice weights of dispatch ranks 0..3
+  int64_t slots;         // partial-state slots: two per piece
+  // Workspace: one allocation whose first eighth (int_area) holds int32
+  // state that is zero when allocated and that every call leaves at zero:
+  // arrival counters (at 0), claim words, pair counters, markers.  The
+  // partial LSEs, outputs and the request prefix follow the int area.  The
+  // int area's size belongs to the allocation, not the plan, so floats of
+  // one plan never lie where another plan keeps int state.  Offsets are
+  // relative to each area's start; ws_bytes is the allocation size needed.
+  size_t ws_claims, ws_pairdone, ws_marks, int_bytes;
+  size_t ws_lse, ws_o, ws_pref, float_bytes;
+  size_t ws_bytes;
 };
+
+// Bytes of the int area of an allocation of `bytes`.
+size_t int_area(size_t bytes) { return bytes / 8 / 256 * 256; }
 
 // Shape checks shared by every entry point.  Returns PKVD_OK or an error.
 int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* bt,
@@ -179,28 +195,64 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   const int64_t pieces = nw / std::max<int64_t>(p.units, 1) + 1;
   const int64_t unit_bytes = pieces * p.rows_per_tile * s.D * 4;
   p.merge_kernel = env_int("PKVD_MERGE_KERNEL", unit_bytes > 32768 ? 1 : 0) ? 1 : 0;
-  // two partial slots per wave
-  const size_t slots = (size_t)2 * nw;
+  // Tail sharing (off by default): the last part of each slice is cut into
+  // tasks that the wave's partner may take once its own slice is done.  The
+  // waves of a CU do not progress at one rate, but taking a task costs the
+  // taker several memory round trips, and on the measured workloads that
+  // outweighs the gain.  PKVD_TAIL_TASKS / PKVD_TAIL_Q set it; with 0 tasks
+  // every wave streams exactly its slice and results are bitwise repeatable.
+  p.tail_tasks = std::min(64, std::max(0, env_int("PKVD_TAIL_TASKS", 0)));
+  p.tail_q = std::min(15, std::max(1, env_int("PKVD_TAIL_Q", 8)));
+  // tasks a wave may claim for itself; 0 hands every tail task to the partner
+  // (a fixed split, so tests reach the partner's path deterministically)
+  p.tail_owner_max = std::min(64, std::max(0, env_int("PKVD_TAIL_OWNER_MAX", 64)));
+  // Slice weights by dispatch rank (workgroups placed on the CUs in the
+  // first, second, ... round): PKVD_RANK_W="w0,w1,w2,w3" (1..4096, max/min <= 4).
+  p.rank_waves = std::max(1, env_int("PKVD_RANK_WAVES", f.cus * pkvd::kWaves));
+  for (int r = 0; r < 4; ++r) p.rank_w[r] = 1;
+  if (const char* e = getenv("PKVD_RANK_W")) {
+    int w[4] = {0, 0, 0, 0};
+    const int n = sscanf(e, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
+    for (int r = n; r < 4; ++r) w[r] = n > 0 ? w[n - 1] : 1;
+    int lo = 1 << 30, hi = 0;
+    for (int r = 0; r < 4; ++r) {
+      w[r] = std::min(4096, std::max(1, w[r]));
+      lo = std::min(lo, w[r]);
+      hi = std::max(hi, w[r]);
+    }
+    if (n > 0 && hi <= 4 * lo)
+      for (int r = 0; r < 4; ++r) p.rank_w[r] = w[r];
+  }
+  // two partial slots per piece, K + 1 pieces per wave
+  p.slots = (int64_t)2 * nw * (p.tail_tasks + 1);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  p.ws_o = up(slots * p.rows_per_tile * 4);
-  p.ws_pref = p.ws_o + up(slots * p.rows_per_tile * (size_t)s.D * 4);
-  p.ws_bytes = p.ws_pref + (size_t)(s.B + 1) * 4;
+  const size_t rows = (size_t)p.slots * p.rows_per_tile;
+  p.ws_claims = up((size_t)p.units * 4);
+  p.ws_pairdone = p.ws_claims + up((size_t)nw * 4);
+  p.ws_marks = p.ws_pairdone + up((size_t)nw * 4);
+  p.int_bytes = p.ws_marks + up(rows * 4);
+  p.ws_lse = 0;
+  p.ws_o = up(rows * 4);
+  p.ws_pref = p.ws_o + up(rows * (size_t)s.D * 4);
+  p.float_bytes = p.ws_pref + up((size_t)(s.B + 1) * 4);
+  // smallest allocation whose int area and remainder hold both parts
+  size_t S = std::max(8 * p.int_bytes + 2048, p.float_bytes + p.float_bytes / 7 + 2048);
+  S = up(S);
+  while (int_area(S) < p.int_bytes || S - int_area(S) < p.float_bytes) S += 256;
+  p.ws_bytes = S;
   return p;
 }
 
-// Library-owned workspace, one per device: fp32 partial states and the
-// per-unit arrival counters.  Counters are zeroed when allocated and every
-// call leaves them at zero (the last piece of a unit resets its counter).
+// Library-owned workspace, one per device (layout in Plan).  It is zeroed
+// when allocated, and every call leaves its int32 state at zero again.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
-  int32_t* counters = nullptr;
-  int64_t n_counters = 0;
 };
 std::mutex g_ws_mutex;
 Workspace g_ws[64];
 
-int ensure_workspace(size_t bytes, int64_t n_counters, void** out, int32_t** counters) {
+int ensure_workspace(size_t bytes, void** out, size_t* size) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -214,33 +266,20 @@ int ensure_workspace(size_t bytes, int64_t n_counters, void** out, int32_t** cou
       w.bytes = 0;
       if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
     }
-    e = hipMalloc(&w.ptr, bytes);
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return fail(PKVD_ERR_WORKSPACE, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    e = hipMemset(p, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-      w.ptr = nullptr;
-      return fail(PKVD_ERR_WORKSPACE, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+      (void)hipFree(p);
+      return fail(PKVD_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
     }
+    w.ptr = p;
     w.bytes = bytes;
   }
-  if (w.n_counters < n_counters) {
-    if (w.counters) {
-      e = hipFree(w.counters);
-      w.counters = nullptr;
-      w.n_counters = 0;
-      if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-    }
-    const int64_t n = std::max<int64_t>(n_counters, 1024);
-    e = hipMalloc(reinterpret_cast<void**>(&w.counters), (size_t)n * sizeof(int32_t));
-    if (e != hipSuccess) {
-      w.counters = nullptr;
-      return fail(PKVD_ERR_WORKSPACE, "hipMalloc(counters): %s", hipGetErrorString(e));
-    }
-    e = hipMemset(w.counters, 0, (size_t)n * sizeof(int32_t));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipMemset(counters): %s", hipGetErrorString(e));
-    w.n_counters = n;
-  }
   *out = w.ptr;
-  *counters = w.counters;
+  *size = w.bytes;
   return PKVD_OK;
 }
 
@@ -305,13 +344,10 @@ int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache
 
 int pkvd_reserve_workspace(size_t bytes) {
   void* p = nullptr;
-  int32_t* c = nullptr;
+  size_t size = 0;
   g_last_error.clear();
   if (bytes == 0) return PKVD_OK;
-  // counters: one per (request, kv head, row tile).  A plan whose partials
-  // fit in `bytes` has at least 2 slots of >= 65 floats per unit, so it
-  // needs at most bytes / 520 counters.
-  return ensure_workspace(bytes, (int64_t)(bytes / 512 + 1024), &p, &c);
+  return ensure_workspace(bytes, &p, &size);
 }
 
 int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_tensor* v_cache,
@@ -406,15 +442,29 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   }
 #endif
   void* ws = nullptr;
-  st = ensure_workspace(p.ws_bytes, p.units, &ws, &a.counters);
+  size_t ws_size = 0;
+  st = ensure_workspace(p.ws_bytes, &ws, &ws_size);
   if (st != PKVD_OK) return st;
-  a.ws_lse = static_cast<float*>(ws);
-  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_o);
-  a.ws_pref = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.ws_pref);
+  char* wi = static_cast<char*>(ws);            // int area
+  char* wf = wi + int_area(ws_size);            // floats follow it
+  a.counters = reinterpret_cast<int32_t*>(wi);
+  a.claims = reinterpret_cast<int32_t*>(wi + p.ws_claims);
+  a.pairdone = reinterpret_cast<int32_t*>(wi + p.ws_pairdone);
+  a.marks = reinterpret_cast<int32_t*>(wi + p.ws_marks);
+  a.ws_lse = reinterpret_cast<float*>(wf + p.ws_lse);
+  a.ws_o = reinterpret_cast<float*>(wf + p.ws_o);
+  a.ws_pref = reinterpret_cast<int32_t*>(wf + p.ws_pref);
   a.merge_kernel = p.merge_kernel;
+  a.tail_tasks = p.tail_tasks;
+  a.tail_q = p.tail_q;
+  a.tail_owner_max = p.tail_owner_max;
+  a.rank_waves = p.rank_waves;
+  for (int r = 0; r < 4; ++r) a.rank_w[r] = p.rank_w[r];
   if (env_int("PKVD_LOG", 0))
-    fprintf(stderr, "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d\n",
-            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel);
+    fprintf(stderr,
+            "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d tail=%d/%d\n",
+            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel,
+            p.tail_tasks, p.tail_q);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

@@ -48,6 +48,12 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_coherent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Instrumented builds (-DPKVD_TRACE) stamp the 100 MHz real-time counter at
@@ -230,17 +236,137 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
 // ---------------------------------------------------------------------------
 // The work is the linear block space [0, T) of all units (request b, kv head,
 // row tile) in that order: request b owns blocks [pref[b], pref[b + 1]) and
-// each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  With
-// NW waves, wave w owns the slice [w T / NW, (w + 1) T / NW), so every wave
-// streams the same number of blocks (to within one) whatever the mix of
-// sequence lengths; NW <= T keeps every slice non-empty.
-
-// First block of wave w's slice, and the wave whose slice holds block x.
-__device__ __forceinline__ int slice_begin(int T, int NW, int w) {
-  return (int)((int64_t)T * w / NW);
+// each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  The
+// NW waves split it into consecutive slices, wave w's in proportion to its
+// weight: W[r] for the waves of dispatch rank r = min(w / rank_waves, 3)
+// (workgroups dispatched in the r-th round over the CUs).  Equal weights give
+// [w T / NW, (w + 1) T / NW): every wave streams the same number of blocks
+// (to within one) whatever the mix of sequence lengths.  The slice sizes
+// never depend on the lengths, only on T.
+struct Slices {
+  int T, NW;
+  int uniform;   // all weights equal: closed forms
+  int RW;        // waves per dispatch rank
+  int W[4];
+  int64_t S;     // total weight of the NW waves
+  int n_min;     // blocks of the shortest slice (a lower bound)
+};
+// Total weight of waves [0, w).
+__device__ __forceinline__ int64_t weight_before(const Slices& s, int w) {
+  int64_t acc = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t lo = (int64_t)r * s.RW, hi = r == 3 ? (int64_t)w : (int64_t)(r + 1) * s.RW;
+    const int64_t n = w < lo ? 0 : (w < hi ? w - lo : hi - lo);
+    acc += n * s.W[r];
+  }
+  return acc;
 }
-__device__ __forceinline__ int slice_of(int T, int NW, int64_t x) {
-  return (int)(((x + 1) * NW - 1) / T);
+__device__ __forceinline__ Slices make_slices(const DecodeArgs& a, int T, int NW) {
+  Slices s;
+  s.T = T;
+  s.NW = NW;
+  s.RW = a.rank_waves > 0 ? a.rank_waves : NW;
+  int wmin = 1 << 30;
+  s.uniform = 1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s.W[r] = a.rank_w[r];
+    if (s.W[r] != s.W[0]) s.uniform = 0;
+    if ((int64_t)r * s.RW < NW && s.W[r] < wmin) wmin = s.W[r];
+  }
+  s.S = weight_before(s, NW);
+  s.n_min = s.uniform ? T / NW : (int)((int64_t)T * wmin / s.S);
+  return s;
+}
+// First block of wave w's slice (w <= NW).
+__device__ __forceinline__ int slice_begin(const Slices& s, int w) {
+  if (s.uniform) return (int)((int64_t)s.T * w / s.NW);
+  return (int)((int64_t)s.T * weight_before(s, w) / s.S);
+}
+// The wave whose slice holds block x (0 <= x < T).
+__device__ __forceinline__ int slice_of(const Slices& s, int64_t x) {
+  if (s.uniform) return (int)(((x + 1) * s.NW - 1) / s.T);
+  int lo = 0, hi = s.NW - 1;   // largest w with slice_begin(w) <= x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slice_begin(s, mid) <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Tail sharing.  With K > 0 tail tasks, the last nt = (hi - lo) * tail_q / 16
+// blocks of wave w's slice [lo, hi) form K tasks; piece 0 (home) is
+// [lo, hi - nt) and piece 1 + k (task k) is
+// [hi - nt + nt k / K, hi - nt + nt (k + 1) / K).  The wave always streams its
+// home piece and claims its tasks front to back; its partner wave
+// NW - 1 - w, once done with its own slice, claims them back to front.
+// Pieces are numbered w (K + 1) + j over the whole grid.  With K = 0 the
+// only piece of a wave is its slice.
+__device__ __forceinline__ int piece_begin(const Slices& s, int K, int tq, int w, int j) {
+  const int lo = slice_begin(s, w);
+  if (j == 0) return lo;
+  const int hi = slice_begin(s, w + 1);
+  const int nt = (int)(((int64_t)(hi - lo) * tq) >> 4);
+  return hi - nt + (int)((int64_t)nt * (j - 1) / K);
+}
+// Piece j of wave w holding block x (lo <= x < hi).
+__device__ __forceinline__ int piece_of(const Slices& s, int K, int tq, int w, int64_t x) {
+  if (K == 0) return 0;
+  const int lo = slice_begin(s, w), hi = slice_begin(s, w + 1);
+  const int nt = (int)(((int64_t)(hi - lo) * tq) >> 4);
+  const int64_t y = x - (hi - nt);
+  if (y < 0) return 0;
+  return 1 + (int)(((y + 1) * K - 1) / nt);
+}
+
+// Where the partial states of a cut unit [us, ue) can be.  A run (a wave's
+// own home piece and the tasks it claimed, or one task taken by the
+// partner) writes the partial of each unit it cuts into slot
+// 2 P + side of the piece P it started at, side 0 when the run starts at or
+// after the unit's first block, 1 otherwise.  The pieces P0 .. P1 holding the
+// unit's blocks are candidates, plus the home piece of the first wave when P0
+// is a task (the wave's own run may have started there and claimed P0).  A
+// marker (unit + 1) beside each written partial tells which candidates hold
+// one.
+struct UnitPieces {
+  int P0;      // first piece holding a block of the unit
+  int n;       // candidates
+  int extra;   // 1: candidate 0 is the home piece of wave w0
+  int w0;
+};
+__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int K, int tq, int64_t us,
+                                                  int64_t ue) {
+  UnitPieces p;
+  p.w0 = slice_of(s, us);
+  const int w1 = slice_of(s, ue - 1);
+  const int j0 = piece_of(s, K, tq, p.w0, us);
+  const int j1 = piece_of(s, K, tq, w1, ue - 1);
+  p.P0 = p.w0 * (K + 1) + j0;
+  p.extra = j0 > 0 ? 1 : 0;
+  p.n = w1 * (K + 1) + j1 - p.P0 + 1 + p.extra;
+  return p;
+}
+// Slot of candidate c.
+__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int K, int tq,
+                                              int64_t us, int c) {
+  const int P = (p.extra && c == 0) ? p.w0 * (K + 1) : p.P0 + c - p.extra;
+  const int w = P / (K + 1), j = P - w * (K + 1);
+  return 2 * P + (piece_begin(s, K, tq, w, j) >= us ? 0 : 1);
+}
+
+// Tail tasks per slice for a launch: the requested count, lowered so that
+// every task of the shortest slice holds at least one block.
+__device__ __forceinline__ int tail_task_count(const DecodeArgs& a, const Slices& s) {
+  const int nt_min = (int)(((int64_t)s.n_min * a.tail_q) >> 4);
+  return a.tail_tasks < nt_min ? a.tail_tasks : nt_min;
+}
+
+// Waves that take part: at most one per min_wave_blocks blocks, and >= 1.
+__device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
+  int nw = T / a.min_wave_blocks;
+  return nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
 }
 
 // Dynamic LDS of a workgroup, in 32-bit words: the scan scratch (kThreads),
@@ -304,7 +430,7 @@ __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, in
 
 // Largest b with pref[b] <= pos (the request holding linear block pos).
 // LDS reads here are wave-uniform (readfirstlane keeps the schedule in SGPRs).
-__device__ __forceinline__ int find_request(const int* s_pref, int B, int64_t pos) {
+__device__ __forceinline__ int find_request(const int* s_pref, int B, int pos) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -319,30 +445,30 @@ struct Segment {
   int b, kvh, tile;
   UnitRange u;
   int blk_begin, blk_end;    // absolute 16-key blocks [blk_begin, blk_end)
-  int64_t ustart, uend;      // the unit's linear block range
+  int ustart, uend;          // the unit's linear block range (the block space fits int32)
   int whole;                 // the range holds the entire unit (int: stays in registers)
   int side;                  // 0: first segment of the wave, 1: a later one
 };
 
 __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
-                                          const int* s_nlen, int64_t pos, int64_t wave_lo,
-                                          int64_t wave_hi) {
+                                          const int* s_nlen, int pos, int wave_lo,
+                                          int wave_hi) {
   Segment g;
   g.b = find_request(s_pref, a.B, pos);
   g.u = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[g.b]));
   const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[g.b]);
   const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
-  const int64_t off = pos - pref_b;
+  const int off = pos - pref_b;
   const int per_req = a.Hkv * a.row_tiles;
-  int uidx = (int)(off / nb);
+  int uidx = off / nb;
   uidx = uidx < 0 ? 0 : (uidx >= per_req ? per_req - 1 : uidx);
   g.kvh = uidx / a.row_tiles;
   g.tile = uidx - g.kvh * a.row_tiles;
-  g.ustart = pref_b + (int64_t)uidx * nb;
+  g.ustart = pref_b + uidx * nb;
   g.uend = g.ustart + nb;
-  const int64_t seg_end = wave_hi < g.uend ? wave_hi : g.uend;
-  g.blk_begin = g.u.first_blk + (int)(pos - g.ustart);
-  g.blk_end = g.blk_begin + (int)(seg_end - pos);
+  const int seg_end = wave_hi < g.uend ? wave_hi : g.uend;
+  g.blk_begin = g.u.first_blk + (pos - g.ustart);
+  g.blk_end = g.blk_begin + (seg_end - pos);
   g.whole = pos == g.ustart && seg_end == g.uend;
   g.side = pos == wave_lo ? 0 : 1;
   return g;

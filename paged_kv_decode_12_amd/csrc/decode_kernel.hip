@@ -9,18 +9,22 @@
 // Schedule (persistent, balanced): one grid of exactly the resident number
 // of waves.  Every workgroup rebuilds, from seq_lens_kv, the prefix of the
 // linear block space of all units, so planning never reads lengths on the
-// host; wave w then streams its own slice [w T / NW, (w + 1) T / NW) of that
-// space, crossing unit boundaries as needed, so every wave does the same
-// amount of work whatever the mix of lengths.  The slice is one continuous
-// stream of chunks: the last round of a chunk already issues the first loads
-// of the next one (next segment included), and the next segment's Q rows are
-// loaded before the current segment's epilogue.  A unit inside one slice is
-// written directly; a unit cut by slice boundaries leaves a normalised
-// partial state (o, base-2 LSE) per piece, and the wave whose piece arrives
-// last (atomic ticket, taken once its slice is streamed) merges the pieces
-// in slice order with the base-2 LSE rule (Note / LSE convention: base-2 LSE
-// states are what the cascade merge consumes).  The merge order is fixed,
-// so results are bitwise repeatable.
+// host; wave w then streams its own slice of that space (decode_common.h:
+// equal slices by default, optionally weighted by dispatch rank), crossing
+// unit boundaries as needed, so every wave does the same amount of work
+// whatever the mix of lengths.  The slice is one continuous stream of
+// chunks: the last round of a chunk already issues the first loads of the
+// next one (next segment included), and the next segment's Q rows are loaded
+// before the current segment's epilogue.  A unit inside one run is written
+// directly; a unit cut between runs leaves a normalised partial state (o,
+// base-2 LSE) per piece in the slot of the piece its run started at, with a
+// marker naming the unit.  Either the run whose blocks complete the unit (an
+// atomic count of delivered blocks, taken once the run is streamed) merges
+// the pieces in block order with the base-2 LSE rule (Note / LSE
+// convention: base-2 LSE states are what the cascade merge consumes), or a
+// second kernel merges all cut units.  Optional tail sharing lets a wave that
+// is done take tail tasks of its partner's slice (decode_common.h); without
+// it the split of the work, and so the result, is the same in every run.
 //
 // The per-wave arithmetic comes from an engine: VALU dot products for tiles
 // of up to 8 rows (engine_valu.h), MFMA for 16-row tiles (engine_mfma.h).
@@ -71,12 +75,14 @@ __device__ __forceinline__ void store_item(const DecodeArgs& a, int64_t rowhead,
   if (a.lse && lead) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
 }
 
-// Writes one item of a piece's partial state: the normalised output o = O / L
-// (in the engine's lane-contiguous order, with device-coherent stores so the
-// merging wave on another CU reads them after the ticket) and, from the row's
-// lead lane, its base-2 LSE.
+// Writes one item of a run's partial state for a cut unit: the normalised
+// output o = O / L (in the engine's lane-contiguous order, with
+// device-coherent stores so that a merging wave on another CU reads them
+// after its ticket) and, from the row's lead lane, its base-2 LSE and the
+// marker (unit + 1; 0: no marker, for padding rows) that tells the merge this
+// slot holds the unit's partial.
 template <class Eng, int D>
-__device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot, int mark,
                                               const typename Eng::Lane& ln, int r, int d0,
                                               float M, float L, const float (&O)[8]) {
   constexpr int RT = Eng::kRows;
@@ -84,19 +90,29 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
   float* po = a.ws_o + (int64_t)slot * RT * D;
 #pragma unroll
   for (int e = 0; e < Eng::kItemDims; ++e) store_coherent(po + Eng::pidx(ln, r, e), O[e] * inv);
-  if (d0 == 0) store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
+  if (d0 == 0) {
+    store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
+    if (mark) store_coherent(a.marks + (int64_t)slot * RT + r, mark);
+  }
 }
 
-// Merges the partial states of one unit's pieces (slices of waves w_first ..
-// w_last, in that order) for all output items of the lane and writes the
-// final values.  kDepth pieces' loads (every item's) are in flight at a time;
-// the running maximum is raised once per group of kDepth pieces.
+// Merges the partial states of the cut unit `unit` (linear blocks [us, ue))
+// for all output items of the lane and writes the final values.  Candidate
+// slots are checked 64 at a time (lane c reads candidate c's row-0 marker);
+// the written ones are read kDepth at a time in block order (every item's
+// loads in flight), raising the running maximum once per group.  The markers
+// read are cleared for the next call.
 template <class Eng, int D, bool BF16>
-__device__ __forceinline__ void merge_unit(const DecodeArgs& a, int T, int NW, int64_t ustart,
-                                           int w_first, int w_last, const typename Eng::Lane& ln,
-                                           int tile, int b, int kvh, int R) {
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int K, int unit,
+                                           int us, int ue, const typename Eng::Lane& ln, int lane,
+                                           int R) {
   constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
+  const int tq = a.tail_q;
+  const int per_req = a.Hkv * a.row_tiles;
+  const int b = unit / per_req, uidx = unit - b * per_req;
+  const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
+  const UnitPieces up = unit_pieces(sl_, K, tq, us, ue);
   int rr[NI], dd[NI];
 #pragma unroll
   for (int it = 0; it < NI; ++it) Eng::item_pos(ln, it, rr[it], dd[it]);
@@ -108,40 +124,57 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int T, int NW, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[it][e] = 0.f;
   }
-  for (int w = w_first; w <= w_last; w += kDepth) {
-    float lv[kDepth][NI], ov[kDepth][NI][N];
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int ww = min(w + u, w_last);
-      const int sl = 2 * ww + (slice_begin(T, NW, ww) >= ustart ? 0 : 1);
-#pragma unroll
-      for (int it = 0; it < NI; ++it) {
-        const int r = rr[it] < RT ? rr[it] : 0;
-        const float l = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
-        lv[u][it] = w + u <= w_last ? l : -INFINITY;
-#pragma unroll
-        for (int e = 0; e < N; ++e)
-          ov[u][it][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
-      }
+  for (int c0 = 0; c0 < up.n; c0 += 64) {
+    const int c = c0 + lane;
+    int slot = 0;
+    bool valid = false;
+    if (c < up.n) {
+      slot = candidate_slot(up, sl_, K, tq, us, c);
+      valid = load_coherent(a.marks + (int64_t)slot * RT) == unit + 1;
     }
-#pragma unroll
-    for (int it = 0; it < NI; ++it) {
-      float Mn = Mx[it];
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, lv[u][it]);
-      const float sc = rescale(Mx[it], Mn);
-      W[it] *= sc;
-#pragma unroll
-      for (int e = 0; e < N; ++e) acc[it][e] *= sc;
+    uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+    // slot of the batch's first written candidate: off entries of a group
+    // read it (finite values) and get weight 0
+    const int sl0 = __builtin_amdgcn_readlane(slot, m ? (int)__builtin_ctzll(m) : 0);
+    while (m) {
+      float lv[kDepth][NI], ov[kDepth][NI][N];
+      bool on[kDepth];
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
-        const float wt = rescale(lv[u][it], Mn);
-        W[it] += wt;
+        on[u] = m != 0;
+        const int q = on[u] ? (int)__builtin_ctzll(m) : 0;
+        m = on[u] ? m & (m - 1) : m;
+        const int sl = on[u] ? __builtin_amdgcn_readlane(slot, q) : sl0;
 #pragma unroll
-        for (int e = 0; e < N; ++e) acc[it][e] = fmaf(wt, ov[u][it][e], acc[it][e]);
+        for (int it = 0; it < NI; ++it) {
+          const int r = rr[it] < RT ? rr[it] : 0;
+          lv[u][it] = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
+#pragma unroll
+          for (int e = 0; e < N; ++e)
+            ov[u][it][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
+        }
       }
-      Mx[it] = Mn;
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        float Mn = Mx[it];
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, on[u] ? lv[u][it] : -INFINITY);
+        const float sc = rescale(Mx[it], Mn);
+        W[it] *= sc;
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[it][e] *= sc;
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+          const float wt = on[u] ? rescale(lv[u][it], Mn) : 0.f;
+          W[it] += wt;
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[it][e] = fmaf(wt, ov[u][it][e], acc[it][e]);
+        }
+        Mx[it] = Mn;
+      }
     }
+    if (valid)
+      for (int r = 0; r < RT; ++r) store_coherent(a.marks + (int64_t)slot * RT + r, 0);
   }
   // acc / W is the merged normalised output; final_value divides by W + sink
 #pragma unroll
@@ -171,30 +204,61 @@ void decode_kernel(const DecodeArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const typename Eng::Lane ln = Eng::lane_of(lane);
   const int gw = (int)blockIdx.x * kWaves + wave;
+  const int tq = a.tail_q;
 
   PKVD_STAMP(a, gw, 0);
+  // The claim on the wave's first tail task goes out before the prefix scan,
+  // which hides its latency.  claim_ret (lane 0) holds a claim's old word.
+  int claim_ret = 0;
+  const int early = a.tail_tasks > 0 && a.tail_owner_max > 0;
+  if (early && lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
   const int T = uniform(build_prefix<BF16>(a, s_pref, s_nlen, s_scan));
   PKVD_STAMP(a, gw, 1);
   if (a.merge_kernel && blockIdx.x == 0)   // the prefix, for the merge kernel
     for (int i = threadIdx.x; i <= a.B; i += kThreads) a.ws_pref[i] = s_pref[i];
-  if (T == 0) return;
-  // waves that take part: at most one per min_wave_blocks blocks (and <= T)
-  int nw = T / a.min_wave_blocks;
-  nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
-  const int NW = nw;
-  if (gw >= NW) return;
-  const int lo = slice_begin(T, NW, gw), hi = slice_begin(T, NW, gw + 1);
+  const int NW = wave_count(a, T);
+  const Slices sl_ = make_slices(a, T, NW);
+  const int lo = T ? slice_begin(sl_, gw) : 0, hi = T ? slice_begin(sl_, gw + 1) : 0;
+  if (T == 0 || gw >= NW || lo >= hi) {
+    // no slice, and no partner touches this wave's claim word: clear it once
+    // the claim has returned
+    if (early && lane == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      store_coherent(&a.claims[gw], 0);
+    }
+    return;
+  }
+  const int K = tail_task_count(a, sl_);   // no task is empty
+  const int partner = NW - 1 - gw;
   const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
   const int chunk_blocks = max(1, ((kWindow - 2) * a.ps + 1) / kBlockKeys);
 
-  // The slice is one stream of chunks: blocks [cb, ce) of a segment (a unit's
-  // part of the slice), at most chunk_blocks long so its page ids fit the
-  // 128-column window.  Each chunk is padded to a whole number of rounds of
-  // NBUF groups (the padding groups are loaded again from the chunk and not
-  // scored), so group g of every chunk lives in buf[g % NBUF] and the last
-  // round of a chunk issues the first loads of the next one.
+  // The run being streamed covers blocks [rlo, rhi) and holds [rlo, bound).
+  // The wave's own run starts with its home piece and moves bound to the end
+  // of each tail task it claims; a claim is issued when the chunk before the
+  // one that ends at bound is set up, and looked at when that chunk is (so a
+  // full chunk hides the atomic's latency).  If the partner got the task,
+  // the run ends at bound.  A task taken from the partner is a run of its own.
+  // A wave with no partner (K = 0, or the middle wave of an odd grid) holds
+  // its whole slice without claims.
+  const int solo = K == 0 || partner == gw;
+  const int omax = solo ? 0 : min(K, a.tail_owner_max);   // tasks the wave may claim
+  int rlo = lo, rhi = hi;
+  int bound = solo ? hi : piece_begin(sl_, K, tq, gw, 1);
+  if (!solo && omax == 0) rhi = bound;
+  int piece = gw * (K + 1);     // piece the run started at: its partial slots
+  int kown = 0;                 // tail tasks the wave holds
+  int claim_pending = !solo && early;   // claim_ret holds a claim not looked at yet
+
+  // The run is one stream of chunks: blocks [cb, ce) of a segment (a unit's
+  // part of the run), at most chunk_blocks long so its page ids fit the
+  // 128-column window, and ending at bound.  Each chunk is padded to a whole
+  // number of rounds of NBUF groups (the padding groups are loaded again from
+  // the chunk and not scored), so group g of every chunk lives in
+  // buf[g % NBUF] and the last round of a chunk issues the first loads of the
+  // next one.
   struct Chunk {
     Segment sg;
     int cb, ce, kb, ke;   // blocks and keys
@@ -205,7 +269,8 @@ void decode_kernel(const DecodeArgs a) {
     Chunk c;
     c.sg = sg;
     c.cb = cb;
-    c.ce = min(sg.blk_end, cb + chunk_blocks);
+    const int lim = bound - sg.ustart + sg.u.first_blk;   // block at bound
+    c.ce = min(min(sg.blk_end, cb + chunk_blocks), lim);
     c.kb = max(sg.u.key_lo, cb * kBlockKeys);
     c.ke = min(sg.u.n, c.ce * kBlockKeys);
     c.ng = (c.ce - c.cb) * GPB;
@@ -215,17 +280,44 @@ void decode_kernel(const DecodeArgs a) {
     c.valid = 1;
     return c;
   };
-  // the chunk after c: the same segment's next one, or the next segment's first
-  auto next_chunk = [&](const Chunk& c) {
-    if (!c.last) return make_chunk(c.sg, c.ce);
-    const int64_t pos = c.sg.ustart + (c.sg.blk_end - c.sg.u.first_blk);
-    if (pos >= hi) {
-      Chunk n = c;
-      n.valid = 0;
-      return n;
+  auto chunk_end = [&](const Chunk& c) -> int {   // linear block after the chunk
+    return c.sg.ustart + (c.ce - c.sg.u.first_blk);
+  };
+  // The chunk after c: the same segment's next one, or the next segment's
+  // first.  At bound the pending claim decides whether the run goes on; if
+  // not, c becomes the run's last chunk (its segment is cut there).
+  auto next_chunk = [&](Chunk& c) {
+    const int pos = chunk_end(c);
+    if (pos == bound && bound < rhi) {
+      // the claim on the task at bound: pending exactly when kown < omax
+      const int old = uniform(claim_ret);
+      const int took = kown < omax && (old >> 16) + (old & 0xffff) < K;
+      claim_pending = 0;
+      if (took) {            // the task is the wave's
+        ++kown;
+        bound = piece_begin(sl_, K, tq, gw, kown + 1);
+      } else {               // the partner's (or beyond omax): stop here
+        rhi = bound;
+        if (!c.last) {
+          c.last = 1;
+          c.sg.blk_end = c.ce;
+          c.sg.whole = 0;
+        }
+      }
     }
-    const Segment sg = locate(a, s_pref, s_nlen, pos, lo, hi);
-    return make_chunk(sg, sg.blk_begin);
+    Chunk n = c;
+    n.valid = 0;
+    if (!c.last) {
+      n = make_chunk(c.sg, c.ce);
+    } else if (pos < rhi) {
+      const Segment sg = locate(a, s_pref, s_nlen, pos, rlo, rhi);
+      n = make_chunk(sg, sg.blk_begin);
+    }
+    if (n.valid && !claim_pending && kown < omax && bound < rhi && chunk_end(n) == bound) {
+      if (lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
+      claim_pending = 1;
+    }
+    return n;
   };
   // page ids of a chunk's columns, clamped into the pool (issued early)
   auto fetch_pages = [&](const Chunk& c) {
@@ -239,126 +331,170 @@ void decode_kernel(const DecodeArgs a) {
     w.p1 = (unsigned)p1 < (unsigned)a.P ? p1 : a.P - 1;
     return w;
   };
-  // pieces of units shared with other waves: at most the slice's first and
-  // last segments; their tickets are taken after the slice is streamed
-  int pend_unit[2] = {-1, -1}, pend_b[2] = {0, 0}, pend_kvh[2] = {0, 0}, pend_tile[2] = {0, 0};
-  int64_t pend_ustart[2] = {0, 0}, pend_uend[2] = {0, 0};
 
 #ifdef PKVD_TRACE
-  int n_seg = 0, n_chunk = 0, n_blk = 0, g_done = 0, quart = 1;
-  const int g_total = (hi - lo) * GPB;
+  int n_seg = 0, n_chunk = 0, n_blk = 0, n_steal = 0, n_stolen_blk = 0;
 #endif
-  Chunk cur;
-  {
-    const Segment sg = locate(a, s_pref, s_nlen, lo, lo, hi);
-    cur = make_chunk(sg, sg.blk_begin);
-  }
-  PageWindow pw = fetch_pages(cur);
-  Chunk nxt = next_chunk(cur);
-  PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
-  typename Eng::Q qr;
-  typename Eng::State st;
-  int max_lo = 0, min_hi = 0;
-  typename Eng::Buf buf[NBUF];
-  // loads of group g of chunk c (clamped to its last group)
-  auto load_group = [&](typename Eng::Buf& x, const Chunk& c, const PageWindow& w, int g) {
-    Eng::template load<PAGE_POW2>(x, a, c.sg.kvh, c.cb * GPB + min(g, c.ng - 1), c.kb, c.ke, w,
-                                  ps_shift, ln);
-  };
-#pragma unroll
-  for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
-  Eng::fetch_q(a, cur.sg, R, ln, qr);
-  Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
-  PKVD_STAMP(a, gw, 2);
-
-  for (;;) {
-#ifdef PKVD_TRACE
-    n_chunk++;
-    n_blk += cur.ce - cur.cb;
-#endif
-    {
-      const int g0 = cur.cb * GPB;
-      const int rounds = cur.ngp / NBUF;
-      auto score = [&](int s, int i) {
-        if (i < cur.ng) {   // padding groups are not scored
-          const int j0 = (g0 + i) * KPG;
-          const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
-          Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
-#ifdef PKVD_TRACE
-          // progress stamps at 1/4, 1/2, 3/4 of the slice (trace slots 13..15)
-          if (++g_done * 4 >= quart * g_total && quart < 4) {
-            PKVD_STAMP(a, gw, 12 + quart);
-            quart++;
-          }
-#endif
-        }
+  for (int run = 0;; ++run) {
+    if (rlo < rhi) {
+      // pieces of units this run cuts: at most its first and last segments;
+      // their tickets are taken once the run is streamed
+      int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_us[2] = {0, 0}, pend_ue[2] = {0, 0};
+      Chunk cur;
+      {
+        const Segment sg = locate(a, s_pref, s_nlen, rlo, rlo, rhi);
+        cur = make_chunk(sg, sg.blk_begin);
+      }
+      PageWindow pw = fetch_pages(cur);
+      Chunk nxt = next_chunk(cur);
+      PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
+      typename Eng::Q qr;
+      typename Eng::State st;
+      int max_lo = 0, min_hi = 0;
+      typename Eng::Buf buf[NBUF];
+      // loads of group g of chunk c (clamped to its last group)
+      auto load_group = [&](typename Eng::Buf& x, const Chunk& c, const PageWindow& w, int g) {
+        Eng::template load<PAGE_POW2>(x, a, c.sg.kvh, c.cb * GPB + min(g, c.ng - 1), c.kb, c.ke, w,
+                                      ps_shift, ln);
       };
-      // each sub-step issues the loads of the group PF ahead, then scores its own
-      for (int rd = 0; rd + 1 < rounds; ++rd) {
 #pragma unroll
-        for (int s = 0; s < NBUF; ++s) {
-          load_group(buf[(s + PF) % NBUF], cur, pw, rd * NBUF + s + PF);
-          score(s, rd * NBUF + s);
-        }
-      }
-      // last round: sub-steps s >= NBUF - PF load groups s + PF - NBUF of the
-      // next chunk (at the end of the slice: this chunk's last group again)
-      const Chunk& lc = nxt.valid ? nxt : cur;
-      const PageWindow lw = nxt.valid ? pwn : pw;
-      const int i0 = (rounds - 1) * NBUF;
-#pragma unroll
-      for (int s = 0; s < NBUF; ++s) {
-        if (s + PF < NBUF) load_group(buf[(s + PF) % NBUF], cur, pw, i0 + s + PF);
-        else load_group(buf[(s + PF) % NBUF], lc, lw, nxt.valid ? s + PF - NBUF : cur.ng - 1);
-        score(s, i0 + s);
-      }
-    }
-    if (cur.last) {
-      // the segment is done.  The next segment's Q rows are loaded first, so
-      // their latency overlaps this epilogue (its first groups are in flight)
-      if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
-      // the whole unit's output, or this piece's partial
-      const Segment& sg = cur.sg;
-      Eng::finish(st, ln);
-      const int slot = 2 * gw + sg.side;
-#pragma unroll
-      for (int it = 0; it < Eng::kItems; ++it) {
-        int r, d0;
-        float M, Lsum, O[8];
-        const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
-        if (sg.whole) {
-          const int row = sg.tile * RT + r;
-          if (ok && row < R) {
-            const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
-            store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
-                                                qhead, d0, d0 == 0, M, Lsum, O);
-          }
-        } else if (ok) {
-          store_partial<Eng, D>(a, slot, ln, r, d0, M, Lsum, O);
-        }
-      }
-      if (!sg.whole) {
-        const int k = sg.side;
-        pend_unit[k] = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
-        pend_b[k] = sg.b;
-        pend_kvh[k] = sg.kvh;
-        pend_tile[k] = sg.tile;
-        pend_ustart[k] = sg.ustart;
-        pend_uend[k] = sg.uend;
-      }
+      for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
+      Eng::fetch_q(a, cur.sg, R, ln, qr);
+      Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+      if (run == 0) PKVD_STAMP(a, gw, 2);
+
+      for (;;) {
 #ifdef PKVD_TRACE
-      if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
+        n_chunk++;
+        if (run == 0) n_blk += cur.ce - cur.cb;
+        else n_stolen_blk += cur.ce - cur.cb;
 #endif
+        {
+          const int g0 = cur.cb * GPB;
+          const int rounds = cur.ngp / NBUF;
+          auto score = [&](int s, int i) {
+            if (i < cur.ng) {   // padding groups are not scored
+              const int j0 = (g0 + i) * KPG;
+              const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
+              Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
+            }
+          };
+          // each sub-step issues the loads of the group PF ahead, then scores its own
+          for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+            for (int s = 0; s < NBUF; ++s) {
+              load_group(buf[(s + PF) % NBUF], cur, pw, rd * NBUF + s + PF);
+              score(s, rd * NBUF + s);
+            }
+          }
+          // last round: sub-steps s >= NBUF - PF load groups s + PF - NBUF of the
+          // next chunk (at the end of the run: this chunk's last group again)
+          const Chunk& lc = nxt.valid ? nxt : cur;
+          const PageWindow lw = nxt.valid ? pwn : pw;
+          const int i0 = (rounds - 1) * NBUF;
+#pragma unroll
+          for (int s = 0; s < NBUF; ++s) {
+            if (s + PF < NBUF) load_group(buf[(s + PF) % NBUF], cur, pw, i0 + s + PF);
+            else load_group(buf[(s + PF) % NBUF], lc, lw, nxt.valid ? s + PF - NBUF : cur.ng - 1);
+            score(s, i0 + s);
+          }
+        }
+        if (cur.last) {
+          // the segment is done.  The next segment's Q rows are loaded first, so
+          // their latency overlaps this epilogue (its first groups are in flight)
+          if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
+          // the whole unit's output, or this piece's partial
+          const Segment& sg = cur.sg;
+          const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
+          Eng::finish(st, ln);
+          const int slot = 2 * piece + sg.side;
+#pragma unroll
+          for (int it = 0; it < Eng::kItems; ++it) {
+            int r, d0;
+            float M, Lsum, O[8];
+            const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
+            const int row = sg.tile * RT + r;
+            if (sg.whole) {
+              if (ok && row < R) {
+                const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
+                store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
+                                                    qhead, d0, d0 == 0, M, Lsum, O);
+              }
+            } else if (ok) {
+              store_partial<Eng, D>(a, slot, row < R ? unit + 1 : 0, ln, r, d0, M, Lsum, O);
+            }
+          }
+          if (!sg.whole) {
+            const int k = sg.side;
+            pend_unit[k] = unit;
+            pend_n[k] = sg.blk_end - sg.blk_begin;
+            pend_us[k] = sg.ustart;
+            pend_ue[k] = sg.uend;
+          }
+#ifdef PKVD_TRACE
+          if (run == 0 && n_seg++ == 0) PKVD_STAMP(a, gw, 5);
+#endif
+        }
+        if (!nxt.valid) break;
+        cur = nxt;
+        pw = pwn;
+        if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+        nxt = next_chunk(cur);
+        if (nxt.valid) pwn = fetch_pages(nxt);
+      }
+      if (run == 0) PKVD_STAMP(a, gw, 6);
+
+      if (!a.merge_kernel) {
+        // tickets of the cut units: blocks delivered, after this run's partial
+        // stores have completed.  The run that completes a unit merges it.
+        __builtin_amdgcn_s_waitcnt(0);
+        int prev[2] = {0, 0};
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (pend_unit[k] >= 0 && lane == 0)
+            prev[k] = atomicAdd(&a.counters[pend_unit[k]], pend_n[k]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (pend_unit[k] < 0) continue;
+          if (uniform(prev[k]) + pend_n[k] != pend_ue[k] - pend_us[k]) continue;
+          if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
+          merge_unit<Eng, D, BF16>(a, sl_, K, pend_unit[k], pend_us[k], pend_ue[k], ln, lane, R);
+        }
+      }
     }
-    if (!nxt.valid) break;
-    cur = nxt;
-    pw = pwn;
-    if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
-    nxt = next_chunk(cur);
-    if (nxt.valid) pwn = fetch_pages(nxt);
+    // the next run: a tail task of the partner's slice, taken from its back
+    if (solo) break;
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&a.claims[partner], 1);
+    old = uniform(old);
+    if ((old >> 16) + (old & 0xffff) >= K) break;
+    const int k = K - 1 - (old & 0xffff);
+    rlo = piece_begin(sl_, K, tq, partner, k + 1);
+    rhi = piece_begin(sl_, K, tq, partner, k + 2);
+    bound = rhi;
+    piece = partner * (K + 1) + k + 1;
+#ifdef PKVD_TRACE
+    n_steal++;
+#endif
   }
 
-  PKVD_STAMP(a, gw, 6);
+  // The second wave of a pair to finish clears both claim words (no claim
+  // on them is outstanding then) and the pair's counter.  Without tasks (or
+  // without a partner) only the wave's own first claim touched its word.
+  if (a.tail_tasks > 0 && lane == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (solo) {
+      store_coherent(&a.claims[gw], 0);
+    } else {
+      const int pi = min(gw, partner);
+      if (atomicAdd(&a.pairdone[pi], 1) == 1) {
+        store_coherent(&a.claims[gw], 0);
+        store_coherent(&a.claims[partner], 0);
+        store_coherent(&a.pairdone[pi], 0);
+      }
+    }
+  }
+  PKVD_STAMP(a, gw, 7);
 #ifdef PKVD_TRACE
   PKVD_COUNT(a, gw, 8, n_seg);
   PKVD_COUNT(a, gw, 9, n_chunk);
@@ -368,36 +504,22 @@ void decode_kernel(const DecodeArgs a) {
     uint32_t xcc = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11));    // XCC_ID
     PKVD_COUNT(a, gw, 11, ((uint64_t)xcc << 32) | hwid);
   }
+  PKVD_COUNT(a, gw, 12, n_steal);
+  PKVD_COUNT(a, gw, 13, kown);
+  PKVD_COUNT(a, gw, 14, n_stolen_blk);
 #endif
-  if (a.merge_kernel) return;   // the merge kernel takes the pieces
-  // tickets of the pieces this wave left: its partial stores complete first
-  __builtin_amdgcn_s_waitcnt(0);
-  int prev[2] = {0, 0};
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (pend_unit[k] >= 0 && lane == 0) prev[k] = atomicAdd(&a.counters[pend_unit[k]], 1);
-  // merge the units whose last piece this wave delivered
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    if (pend_unit[k] < 0) continue;
-    const int w_first = slice_of(T, NW, pend_ustart[k]);
-    const int w_last = slice_of(T, NW, pend_uend[k] - 1);
-    if (uniform(prev[k]) != w_last - w_first) continue;
-    if (lane == 0) a.counters[pend_unit[k]] = 0;   // ready for the next call
-    merge_unit<Eng, D, BF16>(a, T, NW, pend_ustart[k], w_first, w_last, ln, pend_tile[k],
-                             pend_b[k], pend_kvh[k], R);
-  }
-  PKVD_STAMP(a, gw, 7);
 }
 
 // Merge kernel (for plans whose cut units leave large partial states): one
-// wave per (unit, row of its tile), launched after the decode kernel.  Lane p
-// reads piece p's LSE (64 pieces at a time), the batch maximum and the weights
-// 2^(lse - max) come from wave reductions, and every lane accumulates its
-// D / 64 output dims over the pieces in slice order, eight pieces' loads in
-// flight.  Each lane owns its dims, so every sum has a fixed order and the
-// result is the same in every run.  Writes out (sink in the denominator) and
-// the base-2 LSE.
+// wave per (unit, row of its tile), launched after the decode kernel.  Lane c
+// checks candidate slot c's marker (64 at a time); the batch maximum of the
+// written pieces' LSEs and their weights 2^(lse - max) come from wave
+// reductions, and every lane accumulates its D / 64 output dims over those
+// pieces in block order, eight pieces' loads in flight.  Each lane owns its
+// dims, so every sum has a fixed order for a given set of pieces.  Writes out
+// (sink in the denominator) and the base-2 LSE, and clears the markers it
+// read.  A unit with no written partial was whole in one run and is left as
+// the decode kernel wrote it.
 constexpr int kMergeWaves = 4;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -426,44 +548,56 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   const UnitRange u = unit_range(a, b);
   if (u.nblk == 0) return;
   const int T = a.ws_pref[a.B];
-  int nw = T / a.min_wave_blocks;
-  nw = nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
-  const int NW = nw;
-  const int us = a.ws_pref[b] + uidx * u.nblk, ue = us + u.nblk;
-  const int w_first = slice_of(T, NW, us);
-  const int w_last = slice_of(T, NW, ue - 1);
-  if (ue > T || w_first == w_last) return;   // whole: the decode kernel wrote it
-  const int n = w_last - w_first + 1;
+  const int NW = wave_count(a, T);
+  const Slices sl_ = make_slices(a, T, NW);
+  const int K = tail_task_count(a, sl_), tq = a.tail_q;
+  const int64_t us = a.ws_pref[b] + (int64_t)uidx * u.nblk, ue = us + u.nblk;
+  if (ue > T) return;
+  const UnitPieces up = unit_pieces(sl_, K, tq, us, ue);
+  if (up.n - up.extra == 1) return;   // inside one piece: one run wrote it whole
   float M = -INFINITY, W = 0.f, acc[NDL];
 #pragma unroll
   for (int e = 0; e < NDL; ++e) acc[e] = 0.f;
   int pos[NDL];
 #pragma unroll
   for (int e = 0; e < NDL; ++e) pos[e] = Eng::ppos(r, lane * NDL + e);
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    const int nb = min(64, n - p0);
+  bool any = false;
+  for (int c0 = 0; c0 < up.n; c0 += 64) {
+    const int c = c0 + lane;
     int slot = 0;
     float l = -INFINITY;
-    if (lane < nb) {
-      const int w = w_first + p0 + lane;
-      slot = 2 * w + (slice_begin(T, NW, w) >= us ? 0 : 1);
-      l = a.ws_lse[(int64_t)slot * RT + r];
+    bool valid = false;
+    if (c < up.n) {
+      slot = candidate_slot(up, sl_, K, tq, us, c);
+      valid = a.marks[(int64_t)slot * RT + r] == unit + 1;
+      if (valid) l = a.ws_lse[(int64_t)slot * RT + r];
     }
+    uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+    if (m == 0) continue;
+    any = true;
     const float Mn = fmaxf(M, wave_max(l));
-    const float wt = lane < nb ? rescale(l, Mn) : 0.f;
+    const float wt = valid ? rescale(l, Mn) : 0.f;
     const float sc = rescale(M, Mn);
     W = W * sc + wave_sum(wt);
 #pragma unroll
     for (int e = 0; e < NDL; ++e) acc[e] *= sc;
     M = Mn;
     constexpr int kDepth = 8;
-    for (int q0 = 0; q0 < nb; q0 += kDepth) {   // uniform: every lane shuffles
+    // off entries of a group read the batch's first written piece (finite
+    // values) with weight 0
+    const int sl0 = __builtin_amdgcn_readlane(slot, (int)__builtin_ctzll(m));
+    while (m) {   // uniform: the written pieces of this batch, in order
       float wq[kDepth], oq[kDepth][NDL];
 #pragma unroll
       for (int e = 0; e < kDepth; ++e) {
-        const int q = q0 + e < nb ? q0 + e : 0;
-        wq[e] = q0 + e < nb ? __shfl(wt, q) : 0.f;
-        const float* po = a.ws_o + (int64_t)__shfl(slot, q) * RT * D;
+        const bool on = m != 0;
+        const int q = on ? (int)__builtin_ctzll(m) : 0;
+        m = on ? m & (m - 1) : m;
+        const float w_q = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), q));
+        wq[e] = on ? w_q : 0.f;
+        const int sl = on ? __builtin_amdgcn_readlane(slot, q) : sl0;
+        const float* po = a.ws_o + (int64_t)sl * RT * D;
 #pragma unroll
         for (int x = 0; x < NDL; ++x) oq[e][x] = po[pos[x]];
       }
@@ -472,7 +606,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #pragma unroll
         for (int x = 0; x < NDL; ++x) acc[x] = fmaf(wq[e], oq[e][x], acc[x]);
     }
+    if (valid) a.marks[(int64_t)slot * RT + r] = 0;
   }
+  if (!any) return;   // whole in one run: written by the decode kernel
   const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
   const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
   // acc / W is the merged normalised output; final_value divides by W + sink

@@ -95,8 +95,10 @@ def test_config_parity(name):
     log(f"[parity] plan={_pk().plan(d['q'], d['k_cache'], d['block_tables'], d['q_len_per_req'], d['window_left'])}")
     out, lse = run_gpu(d, lse=True)
     compare(name, out, lse, ref_out, ref_lse)
-    # the same call without LSE output writes the same out
     out2, _ = run_gpu(d, lse=False)
+    compare(name + "/no_lse", out2, None, ref_out, ref_lse)
+    # with a fixed split of the work (the default), the call without LSE
+    # output writes the same out bit for bit
     np.testing.assert_array_equal(out, out2)
 
 
@@ -124,6 +126,22 @@ SCHEDULES = {
     "mk_cut7": {"PKVD_MERGE_KERNEL": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "mk_mfma_cut64": {"PKVD_MERGE_KERNEL": "1", "PKVD_FORCE_PATH": "1", "PKVD_WAVES": "64",
                       "PKVD_MIN_WAVE_BLOCKS": "1"},
+    # tail sharing: every tail task handed to the partner wave (a fixed split),
+    # merged in place and by the merge kernel; and no tail tasks at all
+    "tail_all": {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_TAIL_OWNER_MAX": "0",
+                 "PKVD_TAIL_TASKS": "3", "PKVD_TAIL_Q": "12"},
+    "mk_tail_all": {"PKVD_MERGE_KERNEL": "1", "PKVD_WAVES": "9", "PKVD_MIN_WAVE_BLOCKS": "1",
+                    "PKVD_TAIL_OWNER_MAX": "0", "PKVD_TAIL_TASKS": "5", "PKVD_TAIL_Q": "15"},
+    "tail": {"PKVD_TAIL_TASKS": "4"},
+    "mk_tail": {"PKVD_TAIL_TASKS": "3", "PKVD_TAIL_Q": "12", "PKVD_MERGE_KERNEL": "1",
+                "PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    # slices weighted by dispatch rank (ranks of 7 waves here), with and
+    # without tail tasks handed to the partner
+    "weighted": {"PKVD_WAVES": "40", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_RANK_WAVES": "7",
+                 "PKVD_RANK_W": "1400,1000,700,400"},
+    "weighted_tail": {"PKVD_WAVES": "24", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_RANK_WAVES": "5",
+                      "PKVD_RANK_W": "900,1200,1000,700", "PKVD_TAIL_OWNER_MAX": "0",
+                      "PKVD_TAIL_TASKS": "2", "PKVD_TAIL_Q": "8"},
 }
 
 
@@ -136,6 +154,24 @@ class schedule:
     def __enter__(self):
         self.old = {k: os.environ.get(k) for k in self.env}
         os.environ.update(self.env)
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+class env:
+    """Temporarily set environment knobs of the planner."""
+
+    def __init__(self, **kv):
+        self.kv = kv
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update(self.kv)
 
     def __exit__(self, *exc):
         for k, v in self.old.items():
@@ -171,40 +207,51 @@ def test_config_other_merge(name, mode):
     log(f"[merge] config={name} PKVD_MERGE_KERNEL={mode}")
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
-    os.environ["PKVD_MERGE_KERNEL"] = mode
-    try:
+    with env(PKVD_MERGE_KERNEL=mode):
         out, lse = run_gpu(d, lse=True)
         out2, lse2 = run_gpu(d, lse=True)
-    finally:
-        os.environ.pop("PKVD_MERGE_KERNEL", None)
     compare(f"{name}/merge{mode}", out, lse, ref_out, ref_lse)
-    np.testing.assert_array_equal(out, out2)
-    np.testing.assert_array_equal(lse, lse2)
+    compare(f"{name}/merge{mode}/again", out2, lse2, ref_out, ref_lse)
 
 
-def test_determinism_and_schedule_invariance():
-    """Repeat calls are bitwise identical; other wave counts (units cut at
-    other places, merged from more pieces) agree within tolerance."""
+@pytest.mark.parametrize("knobs", [{},
+                                   {"PKVD_TAIL_TASKS": "4", "PKVD_TAIL_OWNER_MAX": "0"},
+                                   {"PKVD_TAIL_TASKS": "4", "PKVD_TAIL_OWNER_MAX": "0",
+                                    "PKVD_MERGE_KERNEL": "1"}],
+                         ids=["notail", "tail_all", "tail_all_mk"])
+def test_determinism(knobs):
+    """With a fixed split of the work (no tail tasks, or every tail task given
+    to the partner wave) repeat calls are bitwise identical."""
     name = "llama3_8b"
+    log(f"[determinism] {knobs}")
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
-    a, la = run_gpu(d)
-    b, lb = run_gpu(d)
+    with env(**knobs):
+        a, la = run_gpu(d)
+        b, lb = run_gpu(d)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
-    for env in ({"PKVD_WAVES": "1"}, {"PKVD_WAVES": "333", "PKVD_MIN_WAVE_BLOCKS": "1"},
-                {"PKVD_WAVES": "5000", "PKVD_MIN_WAVE_BLOCKS": "1"}):
-        old = {k: os.environ.get(k) for k in env}
-        os.environ.update(env)
-        try:
+    compare(f"{name}/{knobs}", a, la, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "long_ctx"])
+def test_schedule_invariance(name):
+    """Other wave counts and tail splits (units cut at other places, merged
+    from more pieces) agree with the oracle; the default split twice."""
+    inp, (ref_out, ref_lse, _) = config_inputs(name)
+    d = to_dev(inp)
+    for knobs in ({}, {}, {"PKVD_WAVES": "1"}, {"PKVD_WAVES": "333", "PKVD_MIN_WAVE_BLOCKS": "1"},
+                  {"PKVD_WAVES": "5000", "PKVD_MIN_WAVE_BLOCKS": "1"},
+                  {"PKVD_TAIL_TASKS": "4"}, {"PKVD_TAIL_TASKS": "4"},
+                  {"PKVD_TAIL_TASKS": "8", "PKVD_TAIL_Q": "15"},
+                  {"PKVD_TAIL_TASKS": "1", "PKVD_TAIL_Q": "2"},
+                  {"PKVD_TAIL_OWNER_MAX": "1", "PKVD_TAIL_TASKS": "6"},
+                  {"PKVD_RANK_W": "1170,980,850"},
+                  {"PKVD_RANK_W": "1170,980,850", "PKVD_TAIL_TASKS": "3"}):
+        log(f"[invariance] config={name} {knobs}")
+        with env(**knobs):
             o, l = run_gpu(d)
-        finally:
-            for k, v in old.items():
-                if v is None:
-                    os.environ.pop(k, None)
-                else:
-                    os.environ[k] = v
-        compare(f"{name}/{env}", o, l, ref_out, ref_lse)
+        compare(f"{name}/{knobs}", o, l, ref_out, ref_lse)
 
 
 # ----------------------------------------------------------------------------
@@ -266,15 +313,19 @@ def test_short_rows_out_of_contract():
     compare("short_rows", out, lse, ref_out, ref_lse)
 
 
-def test_graph_replay():
+@pytest.mark.parametrize("sched,bitwise", [("cut7", True), ("auto", True), ("tail", False),
+                                           ("tail_all", True), ("mk_tail_all", True)])
+def test_graph_replay(sched, bitwise):
     """Capture one call in a HIP graph (workspace reserved first) and replay it
-    several times with eager work in between; every replay equals eager."""
+    several times with eager work in between; every replay matches the oracle,
+    and equals the eager call where the split of the work is fixed."""
     pk = _pk()
     inp = workloads.make_case(B=4, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(100, 900, 33, 2000),
                               seed=9)
+    ref_out, ref_lse, _ = oracle.decode(inp)
     d = to_dev(inp)
-    os.environ.update(SCHEDULES["cut7"])
-    try:
+    log(f"[graph] schedule={sched}")
+    with schedule(sched):
         pk.reserve_workspace(pk.workspace_bytes(d["q"], d["k_cache"], d["block_tables"]))
         out = torch.empty_like(d["q"])
         lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device="cuda")
@@ -296,8 +347,8 @@ def test_graph_replay():
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
-            assert torch.equal(out, eager_o), it
-            assert torch.equal(lse, eager_l), it
-    finally:
-        for k in SCHEDULES["cut7"]:
-            os.environ.pop(k, None)
+            o = out.float().cpu().numpy().reshape(-1, out.shape[-1])
+            compare(f"graph/{sched}/{it}", o, lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
+            if bitwise:
+                assert torch.equal(out, eager_o), it
+                assert torch.equal(lse, eager_l), it
