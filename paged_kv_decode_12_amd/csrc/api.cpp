@@ -121,11 +121,13 @@ int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* 
   return PKVD_OK;
 }
 
-// CUs of the current device and resident workgroups per CU for a kernel; an
-// MI355X (256 CUs, 2 workgroups per CU) is assumed when no device answers.
+// CUs of the current device, waves per workgroup and resident workgroups per
+// CU for a kernel; an MI355X (256 CUs, one workgroup per CU) is assumed when
+// no device answers.
 struct DeviceFit {
   int cus = 256;
-  int blocks_per_cu = 2;
+  int group_waves = 8;
+  int blocks_per_cu = 1;
 };
 
 DeviceFit device_fit(int path, int rt, const Shapes& s) {
@@ -150,8 +152,10 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
     if (cached_cus[dev]) f.cus = cached_cus[dev];
   }
   const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
+  const int gw = pkvd::decode_group_waves(path, rt, (int)s.D);
+  if (gw > 0) f.group_waves = gw;
   const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
-                                           pkvd::decode_lds_bytes((int)s.B));
+                                           pkvd::decode_lds_bytes((int)s.B, 64 * f.group_waves));
   if (n > 0) f.blocks_per_cu = n;
   else (void)hipGetLastError();
   return f;
@@ -179,7 +183,7 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   if (p.units * max_blocks >= INT32_MAX) return Plan{-1};
 
   const DeviceFit f = device_fit(p.path, p.rows_per_tile, s);
-  int64_t nw = (int64_t)f.cus * f.blocks_per_cu * pkvd::kWaves;
+  int64_t nw = (int64_t)f.cus * f.blocks_per_cu * f.group_waves;
   const int forced = env_int("PKVD_WAVES", 0);
   if (forced > 0) nw = forced;
   p.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 8));
@@ -187,7 +191,10 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   nw = std::min<int64_t>(nw, (p.units * max_blocks + p.min_wave_blocks - 1) / p.min_wave_blocks);
   nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
   p.num_waves = (int)nw;
-  p.workgroups = (nw + pkvd::kWaves - 1) / pkvd::kWaves;
+  // one workgroup per resident slot (one per CU) even when waves are few,
+  // so that they spread over the CUs; more if the waves need more
+  p.workgroups = std::max<int64_t>((nw + f.group_waves - 1) / f.group_waves,
+                                   std::min<int64_t>((int64_t)f.cus * f.blocks_per_cu, nw));
   // Where cut units leave large partial states (many pieces per unit or wide
   // tiles: over 32 KB per unit) one wave merging a unit at the end would be
   // slow; a second kernel merges them all in parallel instead.  Estimated
@@ -206,9 +213,10 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   // tasks a wave may claim for itself; 0 hands every tail task to the partner
   // (a fixed split, so tests reach the partner's path deterministically)
   p.tail_owner_max = std::min(64, std::max(0, env_int("PKVD_TAIL_OWNER_MAX", 64)));
-  // Slice weights by dispatch rank (workgroups placed on the CUs in the
-  // first, second, ... round): PKVD_RANK_W="w0,w1,w2,w3" (1..4096, max/min <= 4).
-  p.rank_waves = std::max(1, env_int("PKVD_RANK_WAVES", f.cus * pkvd::kWaves));
+  // Slice weights by age rank: with waves numbered across workgroups, rank r
+  // holds the waves at position r within their SIMD (the r-th oldest on it).
+  // PKVD_RANK_W="w0,w1,w2,w3" (1..4096, max/min <= 4); equal by default.
+  p.rank_waves = std::max(1, env_int("PKVD_RANK_WAVES", f.cus * f.blocks_per_cu * pkvd::kSimdsPerCu));
   for (int r = 0; r < 4; ++r) p.rank_w[r] = 1;
   if (const char* e = getenv("PKVD_RANK_W")) {
     int w[4] = {0, 0, 0, 0};
@@ -434,6 +442,7 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   a.D = (int32_t)s.D;
   a.row_tiles = p.row_tiles;
   a.num_waves = p.num_waves;
+  a.groups = (int32_t)p.workgroups;
   a.min_wave_blocks = p.min_wave_blocks;
 #ifdef PKVD_TRACE
   {

@@ -9,8 +9,7 @@
 namespace pkvd {
 
 constexpr int kBlockKeys = 16;   // keys per block: the unit a wave loads and scores
-constexpr int kWaves = 4;        // waves per workgroup of the decode kernels
-constexpr int kThreads = 64 * kWaves;
+constexpr int kSimdsPerCu = 4;   // a decode workgroup holds WPE waves on each SIMD of a CU
 constexpr int kMaxBatch = 8192;        // requests per call (the schedule keeps a prefix in LDS)
 
 enum Path : int { kPathValu = 0, kPathMfma = 1 };
@@ -46,14 +45,15 @@ struct DecodeArgs {
   int32_t window_left;
   float scale_log2;                // scale * log2(e): scores are kept in base 2
   int32_t row_tiles;               // row tiles per (request, kv head)
-  int32_t num_waves;               // waves of the persistent grid (4 per workgroup)
+  int32_t num_waves;               // waves of the persistent grid
+  int32_t groups;                  // workgroups launched (groups * waves per group >= num_waves)
   int32_t min_wave_blocks;         // a wave gets at least this many blocks (fewer waves run)
   int32_t merge_kernel;            // 1: cut units are merged by a second kernel, not in place
   int32_t tail_tasks;              // K: tail tasks per slice (0: no sharing)
   int32_t tail_q;                  // the tail's share of a slice, in sixteenths
   int32_t tail_owner_max;          // tail tasks a wave may claim for itself (tests: 0)
-  int32_t rank_waves;              // waves per dispatch rank (workgroups on all CUs once)
-  int32_t rank_w[4];               // slice weight of the waves of dispatch rank 0, 1, 2, >= 3
+  int32_t rank_waves;              // waves per age rank (one wave per SIMD of every group)
+  int32_t rank_w[4];               // slice weight of the waves of age rank 0, 1, 2, >= 3
 #ifdef PKVD_TRACE
   uint64_t* trace;                 // instrumented builds only: [waves][16] timestamps
 #endif
@@ -62,8 +62,12 @@ struct DecodeArgs {
 // Launcher (decode_kernel.hip).  Returns the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,
                          hipStream_t stream);
-// Dynamic LDS bytes of a launch for B requests.
-size_t decode_lds_bytes(int B);
+// Waves per workgroup of the decode kernel for a path (0 on error): all the
+// waves one CU holds at the kernel's register budget, so one workgroup fills
+// a CU and every wave of a CU starts together.
+int decode_group_waves(int path, int rows_per_tile, int head_dim);
+// Dynamic LDS bytes of a launch for B requests, `threads` per workgroup.
+size_t decode_lds_bytes(int B, int threads);
 // Workgroups of the decode kernel that fit on one CU at once (0 on error).
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool page_pow2,
                          size_t lds_bytes);

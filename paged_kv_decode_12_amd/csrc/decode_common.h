@@ -238,15 +238,16 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
 // row tile) in that order: request b owns blocks [pref[b], pref[b + 1]) and
 // each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  The
 // NW waves split it into consecutive slices, wave w's in proportion to its
-// weight: W[r] for the waves of dispatch rank r = min(w / rank_waves, 3)
-// (workgroups dispatched in the r-th round over the CUs).  Equal weights give
+// weight: W[r] for the waves of age rank r = min(w / rank_waves, 3) (waves
+// are numbered across workgroups first, so rank r holds the r-th oldest wave
+// of every SIMD).  Equal weights give
 // [w T / NW, (w + 1) T / NW): every wave streams the same number of blocks
 // (to within one) whatever the mix of sequence lengths.  The slice sizes
 // never depend on the lengths, only on T.
 struct Slices {
   int T, NW;
   int uniform;   // all weights equal: closed forms
-  int RW;        // waves per dispatch rank
+  int RW;        // waves per age rank
   int W[4];
   int64_t S;     // total weight of the NW waves
   int n_min;     // blocks of the shortest slice (a lower bound)
@@ -369,16 +370,16 @@ __device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
   return nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
 }
 
-// Dynamic LDS of a workgroup, in 32-bit words: the scan scratch (kThreads),
+// Dynamic LDS of a workgroup of NT threads, in 32-bit words: the scan scratch (NT),
 // the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
 // (carve-up) both take the offsets from here.
 struct LdsLayout {
   int scan, pref, nlen, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int B) {
+__host__ __device__ inline LdsLayout lds_layout(int B, int NT) {
   LdsLayout l;
   l.scan = 0;
-  l.pref = l.scan + kThreads;
+  l.pref = l.scan + NT;
   l.nlen = l.pref + B + 1;
   l.total = l.nlen + B;
   return l;
@@ -387,12 +388,12 @@ __host__ __device__ inline LdsLayout lds_layout(int B) {
 // Builds pref[0..B] and the raw lengths nlen[0..B-1] in LDS (one workgroup,
 // ends with a barrier) and returns T = pref[B].  Requests with no visible key
 // get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
-template <bool BF16>
+template <bool BF16, int NT>
 __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, int* s_nlen,
                                             int* s_scan) {
   const int B = a.B;
   const int per_req = a.Hkv * a.row_tiles;
-  const int CH = (B + kThreads - 1) / kThreads;
+  const int CH = (B + NT - 1) / NT;
   const int t = threadIdx.x;
   const int lo = min(B, t * CH), hi = min(B, lo + CH);
   int sum = 0;
@@ -412,7 +413,7 @@ __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, in
   }
   s_scan[t] = sum;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {      // inclusive Hillis-Steele scan
+  for (int off = 1; off < NT; off <<= 1) {      // inclusive Hillis-Steele scan
     const int v = t >= off ? s_scan[t - off] : 0;
     __syncthreads();
     s_scan[t] += v;
@@ -423,7 +424,7 @@ __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, in
     s_pref[b] = excl;
     excl += unit_range_n(a, s_nlen[b]).nblk * per_req;
   }
-  if (t == kThreads - 1) s_pref[B] = s_scan[t];
+  if (t == NT - 1) s_pref[B] = s_scan[t];
   __syncthreads();
   return s_pref[B];
 }

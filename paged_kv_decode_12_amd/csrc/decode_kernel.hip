@@ -10,7 +10,7 @@
 // of waves.  Every workgroup rebuilds, from seq_lens_kv, the prefix of the
 // linear block space of all units, so planning never reads lengths on the
 // host; wave w then streams its own slice of that space (decode_common.h:
-// equal slices by default, optionally weighted by dispatch rank), crossing
+// equal slices by default, optionally weighted by age rank), crossing
 // unit boundaries as needed, so every wave does the same amount of work
 // whatever the mix of lengths.  The slice is one continuous stream of
 // chunks: the last round of a chunk already issues the first loads of the
@@ -188,14 +188,16 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
 }
 
 template <class Eng, int D, bool BF16, bool PAGE_POW2, int PF, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+__global__ __launch_bounds__(64 * kSimdsPerCu * WPE) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_kernel(const DecodeArgs a) {
+  // one workgroup per CU: WPE waves on each of its SIMDs
+  constexpr int kWaves = kSimdsPerCu * WPE, kThreads = 64 * kWaves;
   constexpr int RT = Eng::kRows;
   constexpr int NBUF = PF + 1;
   constexpr int kWindow = 128;                        // block-table columns per chunk
   constexpr int GPB = Eng::kGroupsPerBlock, KPG = Eng::kKeysPerGroup;
   extern __shared__ int lds[];
-  const LdsLayout L = lds_layout(a.B);
+  const LdsLayout L = lds_layout(a.B, kThreads);
   int* s_scan = lds + L.scan;
   int* s_pref = lds + L.pref;
   int* s_nlen = lds + L.nlen;
@@ -203,31 +205,28 @@ void decode_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const typename Eng::Lane ln = Eng::lane_of(lane);
-  const int gw = (int)blockIdx.x * kWaves + wave;
   const int tq = a.tail_q;
 
-  PKVD_STAMP(a, gw, 0);
-  // The claim on the wave's first tail task goes out before the prefix scan,
-  // which hides its latency.  claim_ret (lane 0) holds a claim's old word.
-  int claim_ret = 0;
-  const int early = a.tail_tasks > 0 && a.tail_owner_max > 0;
-  if (early && lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
-  const int T = uniform(build_prefix<BF16>(a, s_pref, s_nlen, s_scan));
-  PKVD_STAMP(a, gw, 1);
+#ifdef PKVD_TRACE
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+#endif
+  const int T = uniform(build_prefix<BF16, kThreads>(a, s_pref, s_nlen, s_scan));
+#ifdef PKVD_TRACE
+  const uint64_t t_prefix = __builtin_amdgcn_s_memrealtime();
+#endif
   if (a.merge_kernel && blockIdx.x == 0)   // the prefix, for the merge kernel
     for (int i = threadIdx.x; i <= a.B; i += kThreads) a.ws_pref[i] = s_pref[i];
   const int NW = wave_count(a, T);
+  // Each workgroup takes a run of consecutive slices (its CU then streams
+  // neighbouring kv heads of the same requests): ceil(NW / groups) waves of
+  // each group are active, so a short grid still spreads over all groups.
+  const int active = (NW + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
   const Slices sl_ = make_slices(a, T, NW);
   const int lo = T ? slice_begin(sl_, gw) : 0, hi = T ? slice_begin(sl_, gw + 1) : 0;
-  if (T == 0 || gw >= NW || lo >= hi) {
-    // no slice, and no partner touches this wave's claim word: clear it once
-    // the claim has returned
-    if (early && lane == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      store_coherent(&a.claims[gw], 0);
-    }
-    return;
-  }
+  if (T == 0 || gw >= NW || lo >= hi) return;   // no slice
+  PKVD_COUNT(a, gw, 0, t_start);
+  PKVD_COUNT(a, gw, 1, t_prefix);
   const int K = tail_task_count(a, sl_);   // no task is empty
   const int partner = NW - 1 - gw;
   const int R = a.g * a.Lq;
@@ -250,7 +249,11 @@ void decode_kernel(const DecodeArgs a) {
   if (!solo && omax == 0) rhi = bound;
   int piece = gw * (K + 1);     // piece the run started at: its partial slots
   int kown = 0;                 // tail tasks the wave holds
-  int claim_pending = !solo && early;   // claim_ret holds a claim not looked at yet
+  // the claim on the first tail task goes out now; claim_ret (lane 0) holds
+  // a claim's old word until it is looked at
+  int claim_ret = 0;
+  int claim_pending = omax > 0;
+  if (claim_pending && lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
 
   // The run is one stream of chunks: blocks [cb, ce) of a segment (a unit's
   // part of the run), at most chunk_blocks long so its page ids fit the
@@ -479,19 +482,15 @@ void decode_kernel(const DecodeArgs a) {
   }
 
   // The second wave of a pair to finish clears both claim words (no claim
-  // on them is outstanding then) and the pair's counter.  Without tasks (or
-  // without a partner) only the wave's own first claim touched its word.
-  if (a.tail_tasks > 0 && lane == 0) {
+  // on them is outstanding then) and the pair's counter.  A wave with no
+  // partner touched no claim word.
+  if (!solo && lane == 0) {
     __builtin_amdgcn_s_waitcnt(0);
-    if (solo) {
+    const int pi = min(gw, partner);
+    if (atomicAdd(&a.pairdone[pi], 1) == 1) {
       store_coherent(&a.claims[gw], 0);
-    } else {
-      const int pi = min(gw, partner);
-      if (atomicAdd(&a.pairdone[pi], 1) == 1) {
-        store_coherent(&a.claims[gw], 0);
-        store_coherent(&a.claims[partner], 0);
-        store_coherent(&a.pairdone[pi], 0);
-      }
+      store_coherent(&a.claims[partner], 0);
+      store_coherent(&a.pairdone[pi], 0);
     }
   }
   PKVD_STAMP(a, gw, 7);
@@ -625,10 +624,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 // blocks in flight ahead of the scoring, and waves per SIMD the register
 // budget is fitted to, per engine
 #ifndef PKVD_PF4
-#define PKVD_PF4 1
+#define PKVD_PF4 3
 #endif
 #ifndef PKVD_WPE4
-#define PKVD_WPE4 3
+#define PKVD_WPE4 2
 #endif
 #ifndef PKVD_PF8
 #define PKVD_PF8 1
@@ -651,18 +650,23 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 
 using KernelFn = void (*)(DecodeArgs);
 
+template <int RT>
+constexpr int valu_pf() { return RT == 4 ? PKVD_PF4 : PKVD_PF8; }
+template <int RT>
+constexpr int valu_wpe() { return RT == 4 ? PKVD_WPE4 : PKVD_WPE8; }
+template <int D>
+constexpr int mfma_pf() { return D == 64 ? PKVD_PF16_D64 : PKVD_PF16; }
+// a D = 64 block takes half the registers: one more wave per SIMD fits
+template <int D>
+constexpr int mfma_wpe() { return D == 64 ? PKVD_WPE16_D64 : PKVD_WPE16; }
+
 template <int D, int RT, bool BF16, bool POW2>
 KernelFn valu_kernel() {
-  constexpr int pf = RT == 4 ? PKVD_PF4 : PKVD_PF8;
-  constexpr int wpe = RT == 4 ? PKVD_WPE4 : PKVD_WPE8;
-  return &decode_kernel<ValuEngine<D, RT, BF16>, D, BF16, POW2, pf, wpe>;
+  return &decode_kernel<ValuEngine<D, RT, BF16>, D, BF16, POW2, valu_pf<RT>(), valu_wpe<RT>()>;
 }
 template <int D, bool BF16, bool POW2>
 KernelFn mfma_kernel() {
-  // a D = 64 block takes half the registers: one more wave per SIMD fits
-  constexpr int pf = D == 64 ? PKVD_PF16_D64 : PKVD_PF16;
-  constexpr int wpe = D == 64 ? PKVD_WPE16_D64 : PKVD_WPE16;
-  return &decode_kernel<MfmaEngine<D, BF16>, D, BF16, POW2, pf, wpe>;
+  return &decode_kernel<MfmaEngine<D, BF16>, D, BF16, POW2, mfma_pf<D>(), mfma_wpe<D>()>;
 }
 
 KernelFn select(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2) {
@@ -707,14 +711,25 @@ bool page_pow2(int ps) { return ps >= kBlockKeys && (ps & (ps - 1)) == 0; }
 
 }  // namespace
 
-size_t decode_lds_bytes(int B) { return sizeof(int) * (size_t)lds_layout(B).total; }
+int decode_group_waves(int path, int rows_per_tile, int head_dim) {
+  int wpe = 0;
+  if (path == kPathMfma) wpe = rows_per_tile != 16 ? 0 : (head_dim == 64 ? mfma_wpe<64>() : mfma_wpe<128>());
+  else if (rows_per_tile == 4) wpe = valu_wpe<4>();
+  else if (rows_per_tile == 8) wpe = valu_wpe<8>();
+  return kSimdsPerCu * wpe;
+}
+
+size_t decode_lds_bytes(int B, int threads) {
+  return sizeof(int) * (size_t)lds_layout(B, threads).total;
+}
 
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
                          size_t lds_bytes) {
   KernelFn k = select(path, rows_per_tile, head_dim, bf16, pow2);
-  if (!k) return 0;
+  const int threads = 64 * decode_group_waves(path, rows_per_tile, head_dim);
+  if (!k || !threads) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads,
                                                    lds_bytes) != hipSuccess)
     return 0;
   return n;
@@ -724,8 +739,10 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool 
                          hipStream_t stream) {
   KernelFn k = select(path, rows_per_tile, a.D, bf16, page_pow2(a.ps));
   if (!k) return hipErrorInvalidValue;
-  const dim3 grid((a.num_waves + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), decode_lds_bytes(a.B), stream, a);
+  const int waves = decode_group_waves(path, rows_per_tile, a.D);
+  if (!waves || (int64_t)a.groups * waves < a.num_waves) return hipErrorInvalidValue;
+  const dim3 grid(a.groups);
+  hipLaunchKernelGGL(k, grid, dim3(64 * waves), decode_lds_bytes(a.B, 64 * waves), stream, a);
   if (!a.merge_kernel) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
