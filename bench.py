@@ -55,7 +55,11 @@ def kv_bytes(inp) -> int:
 
 def kernel_source_hash() -> str:
     """SHA-256 over the library's sources and build flags (what the counters measured)."""
-    from paged_kv_decode_12_amd import build as b
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_pkvd_build", os.path.join(ROOT, "paged_kv_decode_12_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
     h = hashlib.sha256()
     for path in b.SOURCES + b.HEADERS:
         with open(path, "rb") as f:

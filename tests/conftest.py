@@ -13,5 +13,15 @@ def pytest_configure(config):
     oracle.build(force=False)
     lib = os.path.join(ROOT, "paged_kv_decode_12_amd", "libpkvd.so")
     if not os.path.exists(lib):
-        from paged_kv_decode_12_amd import build as _b
-        _b.build(force=True)
+        _build_module().build(force=True)
+
+
+def _build_module():
+    """The package's build script, loaded by path (importing the package loads
+    libpkvd.so, which is what is missing here)."""
+    import importlib.util
+    path = os.path.join(ROOT, "paged_kv_decode_12_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("_pkvd_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
