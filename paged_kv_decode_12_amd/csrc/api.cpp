@@ -57,20 +57,16 @@ struct Plan {
   int64_t workgroups;
   int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
   int merge_kernel;      // 1: cut units are merged by a second kernel
-  int tail_tasks;        // tail tasks per slice shared with the partner wave (0: none)
-  int tail_q;            // the tail's share of a slice, in sixteenths
-  int tail_owner_max;    // tail tasks a wave may claim for itself
-  int rank_waves;        // waves per dispatch rank
-  int rank_w[4];         // slice weights of dispatch ranks 0..3
-  int64_t slots;         // partial-state slots: two per piece
+  int slot_w[4];         // slice weights of the waves at position 0..3 on their SIMD
+  int64_t slots;         // partial-state slots: two per wave
   // Workspace: one allocation whose first eighth (int_area) holds int32
   // state that is zero when allocated and that every call leaves at zero:
-  // arrival counters (at 0), claim words, pair counters, markers.  The
+  // arrival counters (at 0) and markers.  The
   // partial LSEs, outputs and the request prefix follow the int area.  The
   // int area's size belongs to the allocation, not the plan, so floats of
   // one plan never lie where another plan keeps int state.  Offsets are
   // relative to each area's start; ws_bytes is the allocation size needed.
-  size_t ws_claims, ws_pairdone, ws_marks, int_bytes;
+  size_t ws_marks, int_bytes;
   size_t ws_lse, ws_o, ws_pref, float_bytes;
   size_t ws_bytes;
 };
@@ -154,24 +150,48 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
   const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
   const int gw = pkvd::decode_group_waves(path, rt, (int)s.D);
   if (gw > 0) f.group_waves = gw;
+  // One workgroup per CU, holding the WPE waves per SIMD the kernel's
+  // register budget was fitted to.  The occupancy query can report room for
+  // a second workgroup when the kernel needs fewer registers than that
+  // budget, but on MI355X the second one did not become resident alongside
+  // (per-wave start stamps: half the waves began only when the first half
+  // was done), so the grid is never sized for more than one.
   const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
                                            pkvd::decode_lds_bytes((int)s.B, 64 * f.group_waves));
-  if (n > 0) f.blocks_per_cu = n;
-  else (void)hipGetLastError();
+  if (n <= 0) (void)hipGetLastError();
+  f.blocks_per_cu = 1;
   return f;
+}
+
+// Default slice weight of the waves at position `slot` on their SIMD.  Equal
+// weights measured fastest for the default engines on MI355X (the MFMA
+// engine at D = 128 runs one wave per SIMD; for the others the second wave
+// finishes last with equal slices, but a CU's waves share one memory pipe,
+// so moving blocks to the first wave did not shorten the call).
+int default_slot_weight(int path, int rows_per_tile, int slot) {
+  (void)path;
+  (void)rows_per_tile;
+  (void)slot;
+  return 100;
 }
 
 Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   Plan p{};
   const int64_t g = s.Hq / s.Hkv;
   const int64_t R = g * Lq;
-  // Tiles of 16 rows (a group of at least 16 query rows per kv head) fill an
-  // MFMA operand; smaller groups use VALU dot products, in tiles of 4 or 8.
-  // PKVD_FORCE_PATH=0/1 overrides the choice (for measurements).
+  // Groups of more than 4 query rows per kv head run on MFMA in 16-row tiles
+  // (a group of 8 leaves half of each tile as padding rows); groups of up to
+  // 4 use VALU dot products.  The VALU engine issues about 27 vector
+  // instructions per (key, kv head) at 4 rows and more at 8, so past 4 rows
+  // the vector units, not HBM, set the pace, while the matrix cores are idle.
+  // Measured on MI355X: 8 rows, D = 128 (131k-key requests) 248 -> 217 us;
+  // 8 rows, D = 64 (window of 128) 50 -> 36 us; 4 rows, D = 128 (2k keys)
+  // 118 us VALU vs 135 us MFMA.
+  // PKVD_FORCE_PATH=0/1 overrides the choice (for measurements and tests).
   const int forced_path = env_int("PKVD_FORCE_PATH", -1);
   p.path = forced_path == pkvd::kPathValu || forced_path == pkvd::kPathMfma
                ? forced_path
-               : (R >= 16 ? pkvd::kPathMfma : pkvd::kPathValu);
+               : (R > 4 ? pkvd::kPathMfma : pkvd::kPathValu);
   p.rows_per_tile = p.path == pkvd::kPathMfma ? 16 : (R <= 4 ? 4 : 8);
   p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
   p.units = s.B * s.Hkv * p.row_tiles;
@@ -195,6 +215,11 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   // so that they spread over the CUs; more if the waves need more
   p.workgroups = std::max<int64_t>((nw + f.group_waves - 1) / f.group_waves,
                                    std::min<int64_t>((int64_t)f.cus * f.blocks_per_cu, nw));
+  // PKVD_GROUPS forces fewer, fuller workgroups (tests reach several waves
+  // per SIMD, and so the slot weights, with small grids)
+  const int forced_groups = env_int("PKVD_GROUPS", 0);
+  if (forced_groups > 0)
+    p.workgroups = std::max<int64_t>(forced_groups, (nw + f.group_waves - 1) / f.group_waves);
   // Where cut units leave large partial states (many pieces per unit or wide
   // tiles: over 32 KB per unit) one wave merging a unit at the end would be
   // slow; a second kernel merges them all in parallel instead.  Estimated
@@ -202,42 +227,31 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   const int64_t pieces = nw / std::max<int64_t>(p.units, 1) + 1;
   const int64_t unit_bytes = pieces * p.rows_per_tile * s.D * 4;
   p.merge_kernel = env_int("PKVD_MERGE_KERNEL", unit_bytes > 32768 ? 1 : 0) ? 1 : 0;
-  // Tail sharing (off by default): the last part of each slice is cut into
-  // tasks that the wave's partner may take once its own slice is done.  The
-  // waves of a CU do not progress at one rate, but taking a task costs the
-  // taker several memory round trips, and on the measured workloads that
-  // outweighs the gain.  PKVD_TAIL_TASKS / PKVD_TAIL_Q set it; with 0 tasks
-  // every wave streams exactly its slice and results are bitwise repeatable.
-  p.tail_tasks = std::min(64, std::max(0, env_int("PKVD_TAIL_TASKS", 0)));
-  p.tail_q = std::min(15, std::max(1, env_int("PKVD_TAIL_Q", 8)));
-  // tasks a wave may claim for itself; 0 hands every tail task to the partner
-  // (a fixed split, so tests reach the partner's path deterministically)
-  p.tail_owner_max = std::min(64, std::max(0, env_int("PKVD_TAIL_OWNER_MAX", 64)));
-  // Slice weights by age rank: with waves numbered across workgroups, rank r
-  // holds the waves at position r within their SIMD (the r-th oldest on it).
-  // PKVD_RANK_W="w0,w1,w2,w3" (1..4096, max/min <= 4); equal by default.
-  p.rank_waves = std::max(1, env_int("PKVD_RANK_WAVES", f.cus * f.blocks_per_cu * pkvd::kSimdsPerCu));
-  for (int r = 0; r < 4; ++r) p.rank_w[r] = 1;
-  if (const char* e = getenv("PKVD_RANK_W")) {
+  // Slice weights by position on the SIMD: of the two waves a SIMD holds,
+  // the first issues ahead of the second and streams faster (per-wave
+  // timestamps: about 1.2x the blocks per microsecond, and it starts
+  // earlier), so with equal slices the second waves finish last.  Weight
+  // W[s] goes to the waves at position s on their SIMD.
+  // PKVD_SLOT_W="w0,w1,w2,w3" (1..1024, max/min <= 4) overrides the default.
+  for (int r = 0; r < 4; ++r) p.slot_w[r] = default_slot_weight(p.path, p.rows_per_tile, r);
+  if (const char* e = getenv("PKVD_SLOT_W")) {
     int w[4] = {0, 0, 0, 0};
     const int n = sscanf(e, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
     for (int r = n; r < 4; ++r) w[r] = n > 0 ? w[n - 1] : 1;
     int lo = 1 << 30, hi = 0;
     for (int r = 0; r < 4; ++r) {
-      w[r] = std::min(4096, std::max(1, w[r]));
+      w[r] = std::min(1024, std::max(1, w[r]));
       lo = std::min(lo, w[r]);
       hi = std::max(hi, w[r]);
     }
     if (n > 0 && hi <= 4 * lo)
-      for (int r = 0; r < 4; ++r) p.rank_w[r] = w[r];
+      for (int r = 0; r < 4; ++r) p.slot_w[r] = w[r];
   }
-  // two partial slots per piece, K + 1 pieces per wave
-  p.slots = (int64_t)2 * nw * (p.tail_tasks + 1);
+  // two partial slots per wave (its slice's first and last segments)
+  p.slots = (int64_t)2 * nw;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t rows = (size_t)p.slots * p.rows_per_tile;
-  p.ws_claims = up((size_t)p.units * 4);
-  p.ws_pairdone = p.ws_claims + up((size_t)nw * 4);
-  p.ws_marks = p.ws_pairdone + up((size_t)nw * 4);
+  p.ws_marks = up((size_t)p.units * 4);   // the arrival counters come first
   p.int_bytes = p.ws_marks + up(rows * 4);
   p.ws_lse = 0;
   p.ws_o = up(rows * 4);
@@ -457,23 +471,16 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   char* wi = static_cast<char*>(ws);            // int area
   char* wf = wi + int_area(ws_size);            // floats follow it
   a.counters = reinterpret_cast<int32_t*>(wi);
-  a.claims = reinterpret_cast<int32_t*>(wi + p.ws_claims);
-  a.pairdone = reinterpret_cast<int32_t*>(wi + p.ws_pairdone);
   a.marks = reinterpret_cast<int32_t*>(wi + p.ws_marks);
   a.ws_lse = reinterpret_cast<float*>(wf + p.ws_lse);
   a.ws_o = reinterpret_cast<float*>(wf + p.ws_o);
   a.ws_pref = reinterpret_cast<int32_t*>(wf + p.ws_pref);
   a.merge_kernel = p.merge_kernel;
-  a.tail_tasks = p.tail_tasks;
-  a.tail_q = p.tail_q;
-  a.tail_owner_max = p.tail_owner_max;
-  a.rank_waves = p.rank_waves;
-  for (int r = 0; r < 4; ++r) a.rank_w[r] = p.rank_w[r];
+  for (int r = 0; r < 4; ++r) a.slot_w[r] = p.slot_w[r];
   if (env_int("PKVD_LOG", 0))
     fprintf(stderr,
-            "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d tail=%d/%d\n",
-            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel,
-            p.tail_tasks, p.tail_q);
+            "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d\n",
+            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

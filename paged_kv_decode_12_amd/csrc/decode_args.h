@@ -29,15 +29,13 @@ struct DecodeArgs {
   // outputs
   uint16_t* out;                   // contiguous (B * Lq, Hq, D)
   float* lse;                      // nullptr: not requested
-  // workspace: a run that cuts a unit leaves a normalised partial state in
-  // slot 2 * piece + side of the piece it started at (decode_common.h, tail
-  // sharing); the run whose blocks complete the unit merges them
+  // workspace: a wave whose slice cuts a unit leaves a normalised partial
+  // state in slot 2 * wave + side (decode_common.h, unit_pieces); the wave
+  // whose blocks complete the unit merges them (or the merge kernel does)
   float* ws_o;                     // [slots][rows_per_tile * D], engine order
   float* ws_lse;                   // [slots][rows_per_tile], base 2
   // int32 state that every call leaves at zero
   int32_t* counters;               // [B * Hkv * row_tiles] blocks of each unit delivered
-  int32_t* claims;                 // [num_waves] tail tasks claimed: owner << 16 | partner
-  int32_t* pairdone;               // [num_waves] waves of a pair that are done
   int32_t* marks;                  // [slots][rows_per_tile] unit + 1 of a written partial
   int32_t* ws_pref;                // [B + 1] block prefix of the requests (merge kernel mode)
   // shapes
@@ -49,11 +47,7 @@ struct DecodeArgs {
   int32_t groups;                  // workgroups launched (groups * waves per group >= num_waves)
   int32_t min_wave_blocks;         // a wave gets at least this many blocks (fewer waves run)
   int32_t merge_kernel;            // 1: cut units are merged by a second kernel, not in place
-  int32_t tail_tasks;              // K: tail tasks per slice (0: no sharing)
-  int32_t tail_q;                  // the tail's share of a slice, in sixteenths
-  int32_t tail_owner_max;          // tail tasks a wave may claim for itself (tests: 0)
-  int32_t rank_waves;              // waves per age rank (one wave per SIMD of every group)
-  int32_t rank_w[4];               // slice weight of the waves of age rank 0, 1, 2, >= 3
+  int32_t slot_w[4];               // slice weight of the waves at position 0, 1, 2, >= 3 on their SIMD
 #ifdef PKVD_TRACE
   uint64_t* trace;                 // instrumented builds only: [waves][16] timestamps
 #endif

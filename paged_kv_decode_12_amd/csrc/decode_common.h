@@ -231,6 +231,21 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
   return O / Z;
 }
 
+// floor(n / d) for 0 <= n < 2^62, 0 < d < 2^62, and a quotient below 2^31.
+// The fp64 quotient has a relative error of about 2^-52 (the rounding of n
+// and of the division), so it is within one of the true quotient; integer
+// corrections make it exact.  About a tenth of the instructions of a generic
+// 64-bit integer division, which matters in the prologue every wave runs.
+__device__ __forceinline__ int64_t qdiv(int64_t n, int64_t d) {
+  int64_t q = (int)((double)n / (double)d);
+  int64_t r = n - q * d;
+  if (r < 0) { --q; r += d; }
+  if (r < 0) { --q; r += d; }
+  if (r >= d) { ++q; r -= d; }
+  if (r >= d) ++q;
+  return q;
+}
+
 // ---------------------------------------------------------------------------
 // balanced persistent schedule
 // ---------------------------------------------------------------------------
@@ -238,130 +253,114 @@ __device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, flo
 // row tile) in that order: request b owns blocks [pref[b], pref[b + 1]) and
 // each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  The
 // NW waves split it into consecutive slices, wave w's in proportion to its
-// weight: W[r] for the waves of age rank r = min(w / rank_waves, 3) (waves
-// are numbered across workgroups first, so rank r holds the r-th oldest wave
-// of every SIMD).  Equal weights give
-// [w T / NW, (w + 1) T / NW): every wave streams the same number of blocks
-// (to within one) whatever the mix of sequence lengths.  The slice sizes
-// never depend on the lengths, only on T.
+// weight.  Waves are numbered group by group, PER = ceil(NW / groups) per
+// group, and a group's wave i runs on SIMD i % 4 as the (i / 4)-th wave
+// there; W[s] is the weight of the waves at position s = min(i / 4, 3) on
+// their SIMD.  (Of two waves sharing a SIMD the first issues ahead of the
+// second and streams faster, so it may be given more blocks.)  Equal weights
+// give [w T / NW, (w + 1) T / NW): every wave streams the same number of
+// blocks (to within one) whatever the mix of sequence lengths.  The slice
+// sizes never depend on the lengths, only on T.
 struct Slices {
   int T, NW;
-  int uniform;   // all weights equal: closed forms
-  int RW;        // waves per age rank
+  int uniform;   // all weights in use equal: closed forms
+  int PER;       // waves per group
   int W[4];
+  int64_t SP;    // total weight of one group's PER waves
   int64_t S;     // total weight of the NW waves
   int n_min;     // blocks of the shortest slice (a lower bound)
 };
-// Total weight of waves [0, w).
-__device__ __forceinline__ int64_t weight_before(const Slices& s, int w) {
+// Total weight of the first m waves of a group (0 <= m <= PER).
+__device__ __forceinline__ int64_t group_weight(const Slices& s, int m) {
   int64_t acc = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t lo = (int64_t)r * s.RW, hi = r == 3 ? (int64_t)w : (int64_t)(r + 1) * s.RW;
-    const int64_t n = w < lo ? 0 : (w < hi ? w - lo : hi - lo);
-    acc += n * s.W[r];
+    const int lo = r * kSimdsPerCu;
+    int n = m - lo;
+    n = n < 0 ? 0 : (r < 3 && n > kSimdsPerCu ? kSimdsPerCu : n);
+    acc += (int64_t)n * s.W[r];
   }
   return acc;
+}
+// Total weight of waves [0, w).
+__device__ __forceinline__ int64_t weight_before(const Slices& s, int w) {
+  const int full = w / s.PER;
+  return (int64_t)full * s.SP + group_weight(s, w - full * s.PER);
 }
 __device__ __forceinline__ Slices make_slices(const DecodeArgs& a, int T, int NW) {
   Slices s;
   s.T = T;
   s.NW = NW;
-  s.RW = a.rank_waves > 0 ? a.rank_waves : NW;
+  const int groups = a.groups > 0 ? a.groups : 1;
+  s.PER = (NW + groups - 1) / groups;
   int wmin = 1 << 30;
   s.uniform = 1;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s.W[r] = a.rank_w[r];
-    if (s.W[r] != s.W[0]) s.uniform = 0;
-    if ((int64_t)r * s.RW < NW && s.W[r] < wmin) wmin = s.W[r];
+    s.W[r] = a.slot_w[r];
+    if (r * kSimdsPerCu < s.PER) {
+      if (s.W[r] != s.W[0]) s.uniform = 0;
+      if (s.W[r] < wmin) wmin = s.W[r];
+    }
   }
+  s.SP = group_weight(s, s.PER);
   s.S = weight_before(s, NW);
-  s.n_min = s.uniform ? T / NW : (int)((int64_t)T * wmin / s.S);
+  s.n_min = s.uniform ? T / NW : (int)qdiv((int64_t)T * wmin, s.S);
   return s;
 }
 // First block of wave w's slice (w <= NW).
 __device__ __forceinline__ int slice_begin(const Slices& s, int w) {
-  if (s.uniform) return (int)((int64_t)s.T * w / s.NW);
-  return (int)((int64_t)s.T * weight_before(s, w) / s.S);
+  if (s.uniform) return (int)qdiv((int64_t)s.T * w, s.NW);
+  return (int)qdiv((int64_t)s.T * weight_before(s, w), s.S);
 }
-// The wave whose slice holds block x (0 <= x < T).
+// The wave whose slice holds block x (0 <= x < T): the largest w with
+// slice_begin(w) <= x, i.e. with weight_before(w) <= ((x + 1) S - 1) / T.
+// That weight is inverted in closed form: whole groups first, then the
+// group's waves slot by slot (weights are positive).
 __device__ __forceinline__ int slice_of(const Slices& s, int64_t x) {
-  if (s.uniform) return (int)(((x + 1) * s.NW - 1) / s.T);
-  int lo = 0, hi = s.NW - 1;   // largest w with slice_begin(w) <= x
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (slice_begin(s, mid) <= x) lo = mid;
-    else hi = mid - 1;
+  if (s.uniform) return (int)qdiv((x + 1) * s.NW - 1, s.T);
+  const int64_t target = qdiv((x + 1) * s.S - 1, s.T);
+  const int64_t full = qdiv(target, s.SP);
+  int64_t rem = target - full * s.SP;
+  int m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int lo = r * kSimdsPerCu;
+    int cap = s.PER - lo;
+    cap = cap < 0 ? 0 : (r < 3 && cap > kSimdsPerCu ? kSimdsPerCu : cap);
+    int64_t n = rem / s.W[r];
+    n = n > cap ? cap : n;
+    if (m == lo) {   // earlier slots full: this slot's waves follow
+      m += (int)n;
+      rem -= n * s.W[r];
+    }
   }
-  return lo;
+  const int64_t w = full * s.PER + m;
+  return (int)(w < s.NW - 1 ? w : s.NW - 1);
 }
 
-// Tail sharing.  With K > 0 tail tasks, the last nt = (hi - lo) * tail_q / 16
-// blocks of wave w's slice [lo, hi) form K tasks; piece 0 (home) is
-// [lo, hi - nt) and piece 1 + k (task k) is
-// [hi - nt + nt k / K, hi - nt + nt (k + 1) / K).  The wave always streams its
-// home piece and claims its tasks front to back; its partner wave
-// NW - 1 - w, once done with its own slice, claims them back to front.
-// Pieces are numbered w (K + 1) + j over the whole grid.  With K = 0 the
-// only piece of a wave is its slice.
-__device__ __forceinline__ int piece_begin(const Slices& s, int K, int tq, int w, int j) {
-  const int lo = slice_begin(s, w);
-  if (j == 0) return lo;
-  const int hi = slice_begin(s, w + 1);
-  const int nt = (int)(((int64_t)(hi - lo) * tq) >> 4);
-  return hi - nt + (int)((int64_t)nt * (j - 1) / K);
-}
-// Piece j of wave w holding block x (lo <= x < hi).
-__device__ __forceinline__ int piece_of(const Slices& s, int K, int tq, int w, int64_t x) {
-  if (K == 0) return 0;
-  const int lo = slice_begin(s, w), hi = slice_begin(s, w + 1);
-  const int nt = (int)(((int64_t)(hi - lo) * tq) >> 4);
-  const int64_t y = x - (hi - nt);
-  if (y < 0) return 0;
-  return 1 + (int)(((y + 1) * K - 1) / nt);
-}
-
-// Where the partial states of a cut unit [us, ue) can be.  A run (a wave's
-// own home piece and the tasks it claimed, or one task taken by the
-// partner) writes the partial of each unit it cuts into slot
-// 2 P + side of the piece P it started at, side 0 when the run starts at or
-// after the unit's first block, 1 otherwise.  The pieces P0 .. P1 holding the
-// unit's blocks are candidates, plus the home piece of the first wave when P0
-// is a task (the wave's own run may have started there and claimed P0).  A
-// marker (unit + 1) beside each written partial tells which candidates hold
-// one.
+// Where the partial states of a cut unit [us, ue) are.  Wave w writes the
+// partial state of each unit its slice cuts into slot 2 w + side: side 0 for
+// the slice's first segment, 1 for its last (a slice cuts at most those
+// two).  The candidates for a unit are the waves w0 .. w1 whose slices hold
+// its blocks; wave w's piece is its first segment exactly when its slice
+// starts at or after us.  A marker (unit + 1) beside each written partial
+// confirms it.
 struct UnitPieces {
-  int P0;      // first piece holding a block of the unit
-  int n;       // candidates
-  int extra;   // 1: candidate 0 is the home piece of wave w0
-  int w0;
+  int w0;      // first wave holding a block of the unit
+  int n;       // candidates: waves w0 .. w0 + n - 1
 };
-__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int K, int tq, int64_t us,
-                                                  int64_t ue) {
+__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int64_t us, int64_t ue) {
   UnitPieces p;
   p.w0 = slice_of(s, us);
-  const int w1 = slice_of(s, ue - 1);
-  const int j0 = piece_of(s, K, tq, p.w0, us);
-  const int j1 = piece_of(s, K, tq, w1, ue - 1);
-  p.P0 = p.w0 * (K + 1) + j0;
-  p.extra = j0 > 0 ? 1 : 0;
-  p.n = w1 * (K + 1) + j1 - p.P0 + 1 + p.extra;
+  p.n = slice_of(s, ue - 1) - p.w0 + 1;
   return p;
 }
 // Slot of candidate c.
-__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int K, int tq,
-                                              int64_t us, int c) {
-  const int P = (p.extra && c == 0) ? p.w0 * (K + 1) : p.P0 + c - p.extra;
-  const int w = P / (K + 1), j = P - w * (K + 1);
-  return 2 * P + (piece_begin(s, K, tq, w, j) >= us ? 0 : 1);
-}
-
-// Tail tasks per slice for a launch: the requested count, lowered so that
-// every task of the shortest slice holds at least one block.
-__device__ __forceinline__ int tail_task_count(const DecodeArgs& a, const Slices& s) {
-  const int nt_min = (int)(((int64_t)s.n_min * a.tail_q) >> 4);
-  return a.tail_tasks < nt_min ? a.tail_tasks : nt_min;
+__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int64_t us,
+                                              int c) {
+  const int w = p.w0 + c;
+  return 2 * w + (slice_begin(s, w) >= us ? 0 : 1);
 }
 
 // Waves that take part: at most one per min_wave_blocks blocks, and >= 1.
@@ -479,21 +478,29 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
 // page ids of a chunk
 // ---------------------------------------------------------------------------
 // Page ids of a chunk's block-table columns col0 .. col0 + 127, one column per
-// lane in each of two registers.
+// lane in each of two registers, as loaded.  They are clamped into the pool
+// [0, plast] where a page is taken from the window, not when the window is
+// fetched: a clamp at the fetch would make the wave wait for the block-table
+// load there (and so for every load issued before it), a full memory round
+// trip at each chunk set-up.
 struct PageWindow {
-  int p0, p1;   // columns col0 + lane, col0 + 64 + lane
+  int p0, p1;   // columns col0 + lane, col0 + 64 + lane (unclamped)
   int col0;
+  int plast;    // last page of the pool
 };
 
+__device__ __forceinline__ int clamp_page(const PageWindow& w, int p) {
+  return (unsigned)p <= (unsigned)w.plast ? p : w.plast;
+}
 // Page of column col0 + c for a wave-uniform c.
 __device__ __forceinline__ int page_uniform(const PageWindow& w, int c) {
-  return __builtin_amdgcn_readlane(c < 64 ? w.p0 : w.p1, c & 63);
+  return clamp_page(w, __builtin_amdgcn_readlane(c < 64 ? w.p0 : w.p1, c & 63));
 }
 // Page of column col0 + c for a per-lane c.
 __device__ __forceinline__ int page_lane(const PageWindow& w, int c) {
   const int a0 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p0);
   const int a1 = __builtin_amdgcn_ds_bpermute((c & 63) << 2, w.p1);
-  return c < 64 ? a0 : a1;
+  return clamp_page(w, c < 64 ? a0 : a1);
 }
 
 }  // namespace dev

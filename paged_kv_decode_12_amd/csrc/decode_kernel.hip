@@ -10,21 +10,20 @@
 // of waves.  Every workgroup rebuilds, from seq_lens_kv, the prefix of the
 // linear block space of all units, so planning never reads lengths on the
 // host; wave w then streams its own slice of that space (decode_common.h:
-// equal slices by default, optionally weighted by age rank), crossing
-// unit boundaries as needed, so every wave does the same amount of work
-// whatever the mix of lengths.  The slice is one continuous stream of
-// chunks: the last round of a chunk already issues the first loads of the
+// equal slices, or weighted by the wave's position on its SIMD), crossing
+// unit boundaries as needed, so a wave's share of the work is set by its
+// weight alone, whatever the mix of lengths.  The slice is one continuous
+// stream of chunks: the last round of a chunk already issues the first loads of the
 // next one (next segment included), and the next segment's Q rows are loaded
-// before the current segment's epilogue.  A unit inside one run is written
-// directly; a unit cut between runs leaves a normalised partial state (o,
-// base-2 LSE) per piece in the slot of the piece its run started at, with a
-// marker naming the unit.  Either the run whose blocks complete the unit (an
-// atomic count of delivered blocks, taken once the run is streamed) merges
+// before the current segment's epilogue.  A unit inside one slice is written
+// directly; a unit cut between slices leaves a normalised partial state (o,
+// base-2 LSE) per piece in the slot of the wave that streamed it, with a
+// marker naming the unit.  Either the wave whose blocks complete the unit (an
+// atomic count of delivered blocks, taken once its slice is streamed) merges
 // the pieces in block order with the base-2 LSE rule (Note / LSE
 // convention: base-2 LSE states are what the cascade merge consumes), or a
-// second kernel merges all cut units.  Optional tail sharing lets a wave that
-// is done take tail tasks of its partner's slice (decode_common.h); without
-// it the split of the work, and so the result, is the same in every run.
+// second kernel merges all cut units.  The split of the work depends on the
+// shapes and lengths only, so the result is the same in every call.
 //
 // The per-wave arithmetic comes from an engine: VALU dot products for tiles
 // of up to 8 rows (engine_valu.h), MFMA for 16-row tiles (engine_mfma.h).
@@ -75,7 +74,7 @@ __device__ __forceinline__ void store_item(const DecodeArgs& a, int64_t rowhead,
   if (a.lse && lead) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
 }
 
-// Writes one item of a run's partial state for a cut unit: the normalised
+// Writes one item of a slice's partial state for a cut unit: the normalised
 // output o = O / L (in the engine's lane-contiguous order, with
 // device-coherent stores so that a merging wave on another CU reads them
 // after its ticket) and, from the row's lead lane, its base-2 LSE and the
@@ -103,16 +102,15 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot, int
 // loads in flight), raising the running maximum once per group.  The markers
 // read are cleared for the next call.
 template <class Eng, int D, bool BF16>
-__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int K, int unit,
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int unit,
                                            int us, int ue, const typename Eng::Lane& ln, int lane,
                                            int R) {
   constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
-  const int tq = a.tail_q;
   const int per_req = a.Hkv * a.row_tiles;
   const int b = unit / per_req, uidx = unit - b * per_req;
   const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
-  const UnitPieces up = unit_pieces(sl_, K, tq, us, ue);
+  const UnitPieces up = unit_pieces(sl_, us, ue);
   int rr[NI], dd[NI];
 #pragma unroll
   for (int it = 0; it < NI; ++it) Eng::item_pos(ln, it, rr[it], dd[it]);
@@ -129,7 +127,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
     int slot = 0;
     bool valid = false;
     if (c < up.n) {
-      slot = candidate_slot(up, sl_, K, tq, us, c);
+      slot = candidate_slot(up, sl_, us, c);
       valid = load_coherent(a.marks + (int64_t)slot * RT) == unit + 1;
     }
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
@@ -205,7 +203,6 @@ void decode_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const typename Eng::Lane ln = Eng::lane_of(lane);
-  const int tq = a.tail_q;
 
 #ifdef PKVD_TRACE
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
@@ -220,44 +217,21 @@ void decode_kernel(const DecodeArgs a) {
   // Each workgroup takes a run of consecutive slices (its CU then streams
   // neighbouring kv heads of the same requests): ceil(NW / groups) waves of
   // each group are active, so a short grid still spreads over all groups.
-  const int active = (NW + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int active = (NW + a.groups - 1) / a.groups;
   const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
   const Slices sl_ = make_slices(a, T, NW);
   const int lo = T ? slice_begin(sl_, gw) : 0, hi = T ? slice_begin(sl_, gw + 1) : 0;
   if (T == 0 || gw >= NW || lo >= hi) return;   // no slice
   PKVD_COUNT(a, gw, 0, t_start);
   PKVD_COUNT(a, gw, 1, t_prefix);
-  const int K = tail_task_count(a, sl_);   // no task is empty
-  const int partner = NW - 1 - gw;
   const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
   const int chunk_blocks = max(1, ((kWindow - 2) * a.ps + 1) / kBlockKeys);
 
-  // The run being streamed covers blocks [rlo, rhi) and holds [rlo, bound).
-  // The wave's own run starts with its home piece and moves bound to the end
-  // of each tail task it claims; a claim is issued when the chunk before the
-  // one that ends at bound is set up, and looked at when that chunk is (so a
-  // full chunk hides the atomic's latency).  If the partner got the task,
-  // the run ends at bound.  A task taken from the partner is a run of its own.
-  // A wave with no partner (K = 0, or the middle wave of an odd grid) holds
-  // its whole slice without claims.
-  const int solo = K == 0 || partner == gw;
-  const int omax = solo ? 0 : min(K, a.tail_owner_max);   // tasks the wave may claim
-  int rlo = lo, rhi = hi;
-  int bound = solo ? hi : piece_begin(sl_, K, tq, gw, 1);
-  if (!solo && omax == 0) rhi = bound;
-  int piece = gw * (K + 1);     // piece the run started at: its partial slots
-  int kown = 0;                 // tail tasks the wave holds
-  // the claim on the first tail task goes out now; claim_ret (lane 0) holds
-  // a claim's old word until it is looked at
-  int claim_ret = 0;
-  int claim_pending = omax > 0;
-  if (claim_pending && lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
-
-  // The run is one stream of chunks: blocks [cb, ce) of a segment (a unit's
-  // part of the run), at most chunk_blocks long so its page ids fit the
-  // 128-column window, and ending at bound.  Each chunk is padded to a whole
+  // The slice is one stream of chunks: blocks [cb, ce) of a segment (a
+  // unit's part of the slice), at most chunk_blocks long so its page ids fit
+  // the 128-column window.  Each chunk is padded to a whole
   // number of rounds of NBUF groups (the padding groups are loaded again from
   // the chunk and not scored), so group g of every chunk lives in
   // buf[g % NBUF] and the last round of a chunk issues the first loads of the
@@ -272,8 +246,7 @@ void decode_kernel(const DecodeArgs a) {
     Chunk c;
     c.sg = sg;
     c.cb = cb;
-    const int lim = bound - sg.ustart + sg.u.first_blk;   // block at bound
-    c.ce = min(min(sg.blk_end, cb + chunk_blocks), lim);
+    c.ce = min(sg.blk_end, cb + chunk_blocks);
     c.kb = max(sg.u.key_lo, cb * kBlockKeys);
     c.ke = min(sg.u.n, c.ce * kBlockKeys);
     c.ng = (c.ce - c.cb) * GPB;
@@ -287,42 +260,20 @@ void decode_kernel(const DecodeArgs a) {
     return c.sg.ustart + (c.ce - c.sg.u.first_blk);
   };
   // The chunk after c: the same segment's next one, or the next segment's
-  // first.  At bound the pending claim decides whether the run goes on; if
-  // not, c becomes the run's last chunk (its segment is cut there).
-  auto next_chunk = [&](Chunk& c) {
+  // first (invalid at the end of the slice).
+  auto next_chunk = [&](const Chunk& c) {
     const int pos = chunk_end(c);
-    if (pos == bound && bound < rhi) {
-      // the claim on the task at bound: pending exactly when kown < omax
-      const int old = uniform(claim_ret);
-      const int took = kown < omax && (old >> 16) + (old & 0xffff) < K;
-      claim_pending = 0;
-      if (took) {            // the task is the wave's
-        ++kown;
-        bound = piece_begin(sl_, K, tq, gw, kown + 1);
-      } else {               // the partner's (or beyond omax): stop here
-        rhi = bound;
-        if (!c.last) {
-          c.last = 1;
-          c.sg.blk_end = c.ce;
-          c.sg.whole = 0;
-        }
-      }
-    }
     Chunk n = c;
     n.valid = 0;
     if (!c.last) {
       n = make_chunk(c.sg, c.ce);
-    } else if (pos < rhi) {
-      const Segment sg = locate(a, s_pref, s_nlen, pos, rlo, rhi);
+    } else if (pos < hi) {
+      const Segment sg = locate(a, s_pref, s_nlen, pos, lo, hi);
       n = make_chunk(sg, sg.blk_begin);
-    }
-    if (n.valid && !claim_pending && kown < omax && bound < rhi && chunk_end(n) == bound) {
-      if (lane == 0) claim_ret = atomicAdd(&a.claims[gw], 1 << 16);
-      claim_pending = 1;
     }
     return n;
   };
-  // page ids of a chunk's columns, clamped into the pool (issued early)
+  // page ids of a chunk's columns (issued early; clamped into the pool where used)
   auto fetch_pages = [&](const Chunk& c) {
     PageWindow w;
     w.col0 = c.kb / a.ps;
@@ -330,167 +281,140 @@ void decode_kernel(const DecodeArgs a) {
     const int32_t* row = a.bt + (int64_t)c.sg.b * a.bt_sr + w.col0;
     const int p0 = row[min(lane, ncol - 1)];
     const int p1 = row[min(64 + lane, ncol - 1)];
-    w.p0 = (unsigned)p0 < (unsigned)a.P ? p0 : a.P - 1;
-    w.p1 = (unsigned)p1 < (unsigned)a.P ? p1 : a.P - 1;
+    w.p0 = p0;
+    w.p1 = p1;
+    w.plast = a.P - 1;
     return w;
   };
 
 #ifdef PKVD_TRACE
-  int n_seg = 0, n_chunk = 0, n_blk = 0, n_steal = 0, n_stolen_blk = 0;
+  int n_seg = 0, n_chunk = 0, n_blk = 0;
 #endif
-  for (int run = 0;; ++run) {
-    if (rlo < rhi) {
-      // pieces of units this run cuts: at most its first and last segments;
-      // their tickets are taken once the run is streamed
-      int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_us[2] = {0, 0}, pend_ue[2] = {0, 0};
-      Chunk cur;
-      {
-        const Segment sg = locate(a, s_pref, s_nlen, rlo, rlo, rhi);
-        cur = make_chunk(sg, sg.blk_begin);
-      }
-      PageWindow pw = fetch_pages(cur);
-      Chunk nxt = next_chunk(cur);
-      PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
-      typename Eng::Q qr;
-      typename Eng::State st;
-      int max_lo = 0, min_hi = 0;
-      typename Eng::Buf buf[NBUF];
-      // loads of group g of chunk c (clamped to its last group)
-      auto load_group = [&](typename Eng::Buf& x, const Chunk& c, const PageWindow& w, int g) {
-        Eng::template load<PAGE_POW2>(x, a, c.sg.kvh, c.cb * GPB + min(g, c.ng - 1), c.kb, c.ke, w,
-                                      ps_shift, ln);
-      };
+  {
+    // pieces of units the slice cuts: at most its first and last segments;
+    // their tickets are taken once the slice is streamed
+    int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_us[2] = {0, 0}, pend_ue[2] = {0, 0};
+    Chunk cur;
+    {
+      const Segment sg = locate(a, s_pref, s_nlen, lo, lo, hi);
+      cur = make_chunk(sg, sg.blk_begin);
+    }
+    PageWindow pw = fetch_pages(cur);
+    Chunk nxt = next_chunk(cur);
+    PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
+    PKVD_STAMP(a, gw, 3);
+    typename Eng::Q qr;
+    typename Eng::State st;
+    int max_lo = 0, min_hi = 0;
+    typename Eng::Buf buf[NBUF];
+    // loads of group g of chunk c (clamped to its last group)
+    auto load_group = [&](typename Eng::Buf& x, const Chunk& c, const PageWindow& w, int g) {
+      Eng::template load<PAGE_POW2>(x, a, c.sg.kvh, c.cb * GPB + min(g, c.ng - 1), c.kb, c.ke, w,
+                                    ps_shift, ln);
+    };
 #pragma unroll
-      for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
-      Eng::fetch_q(a, cur.sg, R, ln, qr);
-      Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
-      if (run == 0) PKVD_STAMP(a, gw, 2);
+    for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
+    PKVD_STAMP(a, gw, 4);
+    Eng::fetch_q(a, cur.sg, R, ln, qr);
+    Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+    PKVD_STAMP(a, gw, 2);
 
-      for (;;) {
+    for (;;) {
 #ifdef PKVD_TRACE
-        n_chunk++;
-        if (run == 0) n_blk += cur.ce - cur.cb;
-        else n_stolen_blk += cur.ce - cur.cb;
+      n_chunk++;
+      n_blk += cur.ce - cur.cb;
 #endif
-        {
-          const int g0 = cur.cb * GPB;
-          const int rounds = cur.ngp / NBUF;
-          auto score = [&](int s, int i) {
-            if (i < cur.ng) {   // padding groups are not scored
-              const int j0 = (g0 + i) * KPG;
-              const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
-              Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
-            }
-          };
-          // each sub-step issues the loads of the group PF ahead, then scores its own
-          for (int rd = 0; rd + 1 < rounds; ++rd) {
-#pragma unroll
-            for (int s = 0; s < NBUF; ++s) {
-              load_group(buf[(s + PF) % NBUF], cur, pw, rd * NBUF + s + PF);
-              score(s, rd * NBUF + s);
-            }
+      {
+        const int g0 = cur.cb * GPB;
+        const int rounds = cur.ngp / NBUF;
+        auto score = [&](int s, int i) {
+          if (i < cur.ng) {   // padding groups are not scored
+            const int j0 = (g0 + i) * KPG;
+            const bool full = j0 >= max_lo && j0 + KPG - 1 <= min_hi;
+            Eng::score(st, buf[s], qr, a.scale_log2, full, j0, ln);
           }
-          // last round: sub-steps s >= NBUF - PF load groups s + PF - NBUF of the
-          // next chunk (at the end of the run: this chunk's last group again)
-          const Chunk& lc = nxt.valid ? nxt : cur;
-          const PageWindow lw = nxt.valid ? pwn : pw;
-          const int i0 = (rounds - 1) * NBUF;
+        };
+        // each sub-step issues the loads of the group PF ahead, then scores its own
+        for (int rd = 0; rd + 1 < rounds; ++rd) {
 #pragma unroll
           for (int s = 0; s < NBUF; ++s) {
-            if (s + PF < NBUF) load_group(buf[(s + PF) % NBUF], cur, pw, i0 + s + PF);
-            else load_group(buf[(s + PF) % NBUF], lc, lw, nxt.valid ? s + PF - NBUF : cur.ng - 1);
-            score(s, i0 + s);
+            load_group(buf[(s + PF) % NBUF], cur, pw, rd * NBUF + s + PF);
+            score(s, rd * NBUF + s);
           }
         }
-        if (cur.last) {
-          // the segment is done.  The next segment's Q rows are loaded first, so
-          // their latency overlaps this epilogue (its first groups are in flight)
-          if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
-          // the whole unit's output, or this piece's partial
-          const Segment& sg = cur.sg;
-          const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
-          Eng::finish(st, ln);
-          const int slot = 2 * piece + sg.side;
+        // last round: sub-steps s >= NBUF - PF load groups s + PF - NBUF of the
+        // next chunk (at the end of the slice: this chunk's last group again)
+        const Chunk& lc = nxt.valid ? nxt : cur;
+        const PageWindow lw = nxt.valid ? pwn : pw;
+        const int i0 = (rounds - 1) * NBUF;
 #pragma unroll
-          for (int it = 0; it < Eng::kItems; ++it) {
-            int r, d0;
-            float M, Lsum, O[8];
-            const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
-            const int row = sg.tile * RT + r;
-            if (sg.whole) {
-              if (ok && row < R) {
-                const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
-                store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
-                                                    qhead, d0, d0 == 0, M, Lsum, O);
-              }
-            } else if (ok) {
-              store_partial<Eng, D>(a, slot, row < R ? unit + 1 : 0, ln, r, d0, M, Lsum, O);
+        for (int s = 0; s < NBUF; ++s) {
+          if (s + PF < NBUF) load_group(buf[(s + PF) % NBUF], cur, pw, i0 + s + PF);
+          else load_group(buf[(s + PF) % NBUF], lc, lw, nxt.valid ? s + PF - NBUF : cur.ng - 1);
+          score(s, i0 + s);
+        }
+      }
+      if (cur.last) {
+        // the segment is done.  The next segment's Q rows are loaded first, so
+        // their latency overlaps this epilogue (its first groups are in flight)
+        if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
+        // the whole unit's output, or this piece's partial
+        const Segment& sg = cur.sg;
+        const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
+        Eng::finish(st, ln);
+        const int slot = 2 * gw + sg.side;
+#pragma unroll
+        for (int it = 0; it < Eng::kItems; ++it) {
+          int r, d0;
+          float M, Lsum, O[8];
+          const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
+          const int row = sg.tile * RT + r;
+          if (sg.whole) {
+            if (ok && row < R) {
+              const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
+              store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
+                                                  qhead, d0, d0 == 0, M, Lsum, O);
             }
+          } else if (ok) {
+            store_partial<Eng, D>(a, slot, row < R ? unit + 1 : 0, ln, r, d0, M, Lsum, O);
           }
-          if (!sg.whole) {
-            const int k = sg.side;
-            pend_unit[k] = unit;
-            pend_n[k] = sg.blk_end - sg.blk_begin;
-            pend_us[k] = sg.ustart;
-            pend_ue[k] = sg.uend;
-          }
+        }
+        if (!sg.whole) {
+          const int k = sg.side;
+          pend_unit[k] = unit;
+          pend_n[k] = sg.blk_end - sg.blk_begin;
+          pend_us[k] = sg.ustart;
+          pend_ue[k] = sg.uend;
+        }
 #ifdef PKVD_TRACE
-          if (run == 0 && n_seg++ == 0) PKVD_STAMP(a, gw, 5);
+        if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
 #endif
-        }
-        if (!nxt.valid) break;
-        cur = nxt;
-        pw = pwn;
-        if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
-        nxt = next_chunk(cur);
-        if (nxt.valid) pwn = fetch_pages(nxt);
       }
-      if (run == 0) PKVD_STAMP(a, gw, 6);
-
-      if (!a.merge_kernel) {
-        // tickets of the cut units: blocks delivered, after this run's partial
-        // stores have completed.  The run that completes a unit merges it.
-        __builtin_amdgcn_s_waitcnt(0);
-        int prev[2] = {0, 0};
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (pend_unit[k] >= 0 && lane == 0)
-            prev[k] = atomicAdd(&a.counters[pend_unit[k]], pend_n[k]);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          if (pend_unit[k] < 0) continue;
-          if (uniform(prev[k]) + pend_n[k] != pend_ue[k] - pend_us[k]) continue;
-          if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-          merge_unit<Eng, D, BF16>(a, sl_, K, pend_unit[k], pend_us[k], pend_ue[k], ln, lane, R);
-        }
-      }
+      if (!nxt.valid) break;
+      cur = nxt;
+      pw = pwn;
+      if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+      nxt = next_chunk(cur);
+      if (nxt.valid) pwn = fetch_pages(nxt);
     }
-    // the next run: a tail task of the partner's slice, taken from its back
-    if (solo) break;
-    int old = 0;
-    if (lane == 0) old = atomicAdd(&a.claims[partner], 1);
-    old = uniform(old);
-    if ((old >> 16) + (old & 0xffff) >= K) break;
-    const int k = K - 1 - (old & 0xffff);
-    rlo = piece_begin(sl_, K, tq, partner, k + 1);
-    rhi = piece_begin(sl_, K, tq, partner, k + 2);
-    bound = rhi;
-    piece = partner * (K + 1) + k + 1;
-#ifdef PKVD_TRACE
-    n_steal++;
-#endif
-  }
+    PKVD_STAMP(a, gw, 6);
 
-  // The second wave of a pair to finish clears both claim words (no claim
-  // on them is outstanding then) and the pair's counter.  A wave with no
-  // partner touched no claim word.
-  if (!solo && lane == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    const int pi = min(gw, partner);
-    if (atomicAdd(&a.pairdone[pi], 1) == 1) {
-      store_coherent(&a.claims[gw], 0);
-      store_coherent(&a.claims[partner], 0);
-      store_coherent(&a.pairdone[pi], 0);
+    if (!a.merge_kernel) {
+      // tickets of the cut units: blocks delivered, after this slice's partial
+      // stores have completed.  The wave that completes a unit merges it.
+      __builtin_amdgcn_s_waitcnt(0);
+      int prev[2] = {0, 0};
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (pend_unit[k] >= 0 && lane == 0)
+          prev[k] = atomicAdd(&a.counters[pend_unit[k]], pend_n[k]);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (pend_unit[k] < 0) continue;
+        if (uniform(prev[k]) + pend_n[k] != pend_ue[k] - pend_us[k]) continue;
+        if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
+        merge_unit<Eng, D, BF16>(a, sl_, pend_unit[k], pend_us[k], pend_ue[k], ln, lane, R);
+      }
     }
   }
   PKVD_STAMP(a, gw, 7);
@@ -503,9 +427,6 @@ void decode_kernel(const DecodeArgs a) {
     uint32_t xcc = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11));    // XCC_ID
     PKVD_COUNT(a, gw, 11, ((uint64_t)xcc << 32) | hwid);
   }
-  PKVD_COUNT(a, gw, 12, n_steal);
-  PKVD_COUNT(a, gw, 13, kown);
-  PKVD_COUNT(a, gw, 14, n_stolen_blk);
 #endif
 }
 
@@ -517,7 +438,7 @@ void decode_kernel(const DecodeArgs a) {
 // pieces in block order, eight pieces' loads in flight.  Each lane owns its
 // dims, so every sum has a fixed order for a given set of pieces.  Writes out
 // (sink in the denominator) and the base-2 LSE, and clears the markers it
-// read.  A unit with no written partial was whole in one run and is left as
+// read.  A unit with no written partial was whole in one slice and is left as
 // the decode kernel wrote it.
 constexpr int kMergeWaves = 4;
 
@@ -549,11 +470,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   const int T = a.ws_pref[a.B];
   const int NW = wave_count(a, T);
   const Slices sl_ = make_slices(a, T, NW);
-  const int K = tail_task_count(a, sl_), tq = a.tail_q;
   const int64_t us = a.ws_pref[b] + (int64_t)uidx * u.nblk, ue = us + u.nblk;
   if (ue > T) return;
-  const UnitPieces up = unit_pieces(sl_, K, tq, us, ue);
-  if (up.n - up.extra == 1) return;   // inside one piece: one run wrote it whole
+  const UnitPieces up = unit_pieces(sl_, us, ue);
+  if (up.n == 1) return;   // inside one slice: written whole by the decode kernel
   float M = -INFINITY, W = 0.f, acc[NDL];
 #pragma unroll
   for (int e = 0; e < NDL; ++e) acc[e] = 0.f;
@@ -567,7 +487,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     float l = -INFINITY;
     bool valid = false;
     if (c < up.n) {
-      slot = candidate_slot(up, sl_, K, tq, us, c);
+      slot = candidate_slot(up, sl_, us, c);
       valid = a.marks[(int64_t)slot * RT + r] == unit + 1;
       if (valid) l = a.ws_lse[(int64_t)slot * RT + r];
     }
@@ -607,7 +527,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     }
     if (valid) a.marks[(int64_t)slot * RT + r] = 0;
   }
-  if (!any) return;   // whole in one run: written by the decode kernel
+  if (!any) return;   // whole in one slice: written by the decode kernel
   const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
   const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
   // acc / W is the merged normalised output; final_value divides by W + sink
@@ -624,10 +544,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 // blocks in flight ahead of the scoring, and waves per SIMD the register
 // budget is fitted to, per engine
 #ifndef PKVD_PF4
-#define PKVD_PF4 3
+#define PKVD_PF4 6
 #endif
 #ifndef PKVD_WPE4
-#define PKVD_WPE4 2
+#define PKVD_WPE4 1
 #endif
 #ifndef PKVD_PF8
 #define PKVD_PF8 1
@@ -636,16 +556,16 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #define PKVD_WPE8 2
 #endif
 #ifndef PKVD_PF16
-#define PKVD_PF16 2
+#define PKVD_PF16 3
 #endif
 #ifndef PKVD_WPE16
-#define PKVD_WPE16 2
+#define PKVD_WPE16 1
 #endif
 #ifndef PKVD_PF16_D64
 #define PKVD_PF16_D64 2
 #endif
 #ifndef PKVD_WPE16_D64
-#define PKVD_WPE16_D64 3
+#define PKVD_WPE16_D64 2
 #endif
 
 using KernelFn = void (*)(DecodeArgs);

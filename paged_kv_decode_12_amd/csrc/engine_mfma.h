@@ -132,7 +132,10 @@ struct MfmaEngine {
     const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
                          (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.q * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) q.c[c] = live ? load16(qp + c * 32) : u32x4{0, 0, 0, 0};
+    // padding lanes (rows past R) load row 0 of the unit, which is live,
+    // rather than selecting zeros: a select on the loaded value would make
+    // the wave wait for the load here.  Padding rows are never stored.
+    for (int c = 0; c < NC; ++c) q.c[c] = load16(qp + c * 32);
   }
 
   static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg, int R,

@@ -239,7 +239,10 @@ struct ValuEngine {
       const int hl = live ? rr - i * a.g : 0;
       const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
                            (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.part * 8;
-      q.r[r] = live ? load16(qp) : u32x4{0, 0, 0, 0};
+      // a padding row (past R) loads row 0 of the unit, which is live,
+      // rather than selecting zeros: a select on the loaded value would make
+      // the wave wait for the load here.  Padding rows are never stored.
+      q.r[r] = load16(qp);
     }
   }
 

@@ -130,8 +130,8 @@ def test_plans_of_the_workloads():
         p = pk.plan(q, k, bt, w.q_len_per_req, w.window_left)
         rows = (w.Hq // w.Hkv) * w.q_len_per_req
         assert p["rows_per_tile"] * p["row_tiles"] >= rows
-        # MFMA exactly when the rows fill 16-row tiles; VALU tiles of 4 or 8 otherwise
-        if rows >= 16:
+        # MFMA (16-row tiles) for more than 4 rows; VALU tiles of 4 otherwise
+        if rows > 4:
             assert (p["path"], p["rows_per_tile"]) == ("mfma", 16)
         else:
             assert p["path"] == "valu" and p["rows_per_tile"] == (4 if rows <= 4 else 8)

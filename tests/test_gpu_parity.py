@@ -119,29 +119,21 @@ SCHEDULES = {
     "auto": {},
     "cut7": {"PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "cut64": {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
-    # the other engine than the planner picks (MFMA for < 16 rows, VALU for >= 16)
+    # the other engine than the planner picks (MFMA for <= 4 rows, VALU for > 4)
     "mfma_cut7": {"PKVD_FORCE_PATH": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "valu": {"PKVD_FORCE_PATH": "0"},
     # cut units merged by the second kernel instead of by their last piece
     "mk_cut7": {"PKVD_MERGE_KERNEL": "1", "PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
     "mk_mfma_cut64": {"PKVD_MERGE_KERNEL": "1", "PKVD_FORCE_PATH": "1", "PKVD_WAVES": "64",
                       "PKVD_MIN_WAVE_BLOCKS": "1"},
-    # tail sharing: every tail task handed to the partner wave (a fixed split),
-    # merged in place and by the merge kernel; and no tail tasks at all
-    "tail_all": {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_TAIL_OWNER_MAX": "0",
-                 "PKVD_TAIL_TASKS": "3", "PKVD_TAIL_Q": "12"},
-    "mk_tail_all": {"PKVD_MERGE_KERNEL": "1", "PKVD_WAVES": "9", "PKVD_MIN_WAVE_BLOCKS": "1",
-                    "PKVD_TAIL_OWNER_MAX": "0", "PKVD_TAIL_TASKS": "5", "PKVD_TAIL_Q": "15"},
-    "tail": {"PKVD_TAIL_TASKS": "4"},
-    "mk_tail": {"PKVD_TAIL_TASKS": "3", "PKVD_TAIL_Q": "12", "PKVD_MERGE_KERNEL": "1",
-                "PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
-    # slices weighted by dispatch rank (ranks of 7 waves here), with and
-    # without tail tasks handed to the partner
-    "weighted": {"PKVD_WAVES": "40", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_RANK_WAVES": "7",
-                 "PKVD_RANK_W": "1400,1000,700,400"},
-    "weighted_tail": {"PKVD_WAVES": "24", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_RANK_WAVES": "5",
-                      "PKVD_RANK_W": "900,1200,1000,700", "PKVD_TAIL_OWNER_MAX": "0",
-                      "PKVD_TAIL_TASKS": "2", "PKVD_TAIL_Q": "8"},
+    # slices weighted by the wave's position on its SIMD (5 or 3 fuller
+    # workgroups, so that groups hold second waves: the engines that run two
+    # waves per SIMD, VALU 8-row tiles and MFMA at D = 64), merged in place
+    # and by the merge kernel
+    "weighted": {"PKVD_WAVES": "40", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_GROUPS": "5",
+                 "PKVD_SLOT_W": "140,100", "PKVD_FORCE_PATH": "0"},
+    "mk_weighted": {"PKVD_WAVES": "24", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_GROUPS": "3",
+                    "PKVD_SLOT_W": "90,120", "PKVD_MERGE_KERNEL": "1", "PKVD_FORCE_PATH": "1"},
 }
 
 
@@ -182,7 +174,7 @@ class env:
 
 
 @pytest.mark.parametrize("name,path", [("llama3_8b", "1"), ("spec_verify", "0"),
-                                       ("sink_window", "1")])
+                                       ("sink_window", "0"), ("long_ctx", "0")])
 def test_config_other_engine(name, path):
     """Full-size configs on the engine the planner does not pick for them."""
     log(f"[engine] config={name} PKVD_FORCE_PATH={path}")
@@ -214,14 +206,11 @@ def test_config_other_merge(name, mode):
     compare(f"{name}/merge{mode}/again", out2, lse2, ref_out, ref_lse)
 
 
-@pytest.mark.parametrize("knobs", [{},
-                                   {"PKVD_TAIL_TASKS": "4", "PKVD_TAIL_OWNER_MAX": "0"},
-                                   {"PKVD_TAIL_TASKS": "4", "PKVD_TAIL_OWNER_MAX": "0",
-                                    "PKVD_MERGE_KERNEL": "1"}],
-                         ids=["notail", "tail_all", "tail_all_mk"])
+@pytest.mark.parametrize("knobs", [{}, {"PKVD_MERGE_KERNEL": "1"}, {"PKVD_FORCE_PATH": "1"}],
+                         ids=["in_place", "merge_kernel", "mfma"])
 def test_determinism(knobs):
-    """With a fixed split of the work (no tail tasks, or every tail task given
-    to the partner wave) repeat calls are bitwise identical."""
+    """The split of the work depends on shapes and lengths only, so repeat
+    calls are bitwise identical."""
     name = "llama3_8b"
     log(f"[determinism] {knobs}")
     inp, (ref_out, ref_lse, _) = config_inputs(name)
@@ -236,18 +225,16 @@ def test_determinism(knobs):
 
 @pytest.mark.parametrize("name", ["llama3_8b", "long_ctx"])
 def test_schedule_invariance(name):
-    """Other wave counts and tail splits (units cut at other places, merged
+    """Other wave counts and slice weights (units cut at other places, merged
     from more pieces) agree with the oracle; the default split twice."""
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
     for knobs in ({}, {}, {"PKVD_WAVES": "1"}, {"PKVD_WAVES": "333", "PKVD_MIN_WAVE_BLOCKS": "1"},
                   {"PKVD_WAVES": "5000", "PKVD_MIN_WAVE_BLOCKS": "1"},
-                  {"PKVD_TAIL_TASKS": "4"}, {"PKVD_TAIL_TASKS": "4"},
-                  {"PKVD_TAIL_TASKS": "8", "PKVD_TAIL_Q": "15"},
-                  {"PKVD_TAIL_TASKS": "1", "PKVD_TAIL_Q": "2"},
-                  {"PKVD_TAIL_OWNER_MAX": "1", "PKVD_TAIL_TASKS": "6"},
-                  {"PKVD_RANK_W": "1170,980,850"},
-                  {"PKVD_RANK_W": "1170,980,850", "PKVD_TAIL_TASKS": "3"}):
+                  {"PKVD_SLOT_W": "124,100"}, {"PKVD_SLOT_W": "100,130"},
+                  {"PKVD_SLOT_W": "100"},
+                  {"PKVD_FORCE_PATH": "0", "PKVD_SLOT_W": "300,100"},
+                  {"PKVD_FORCE_PATH": "0", "PKVD_SLOT_W": "100,250", "PKVD_MERGE_KERNEL": "1"}):
         log(f"[invariance] config={name} {knobs}")
         with env(**knobs):
             o, l = run_gpu(d)
@@ -313,12 +300,11 @@ def test_short_rows_out_of_contract():
     compare("short_rows", out, lse, ref_out, ref_lse)
 
 
-@pytest.mark.parametrize("sched,bitwise", [("cut7", True), ("auto", True), ("tail", False),
-                                           ("tail_all", True), ("mk_tail_all", True)])
-def test_graph_replay(sched, bitwise):
+@pytest.mark.parametrize("sched", ["cut7", "auto", "mk_cut7", "weighted", "mk_weighted"])
+def test_graph_replay(sched):
     """Capture one call in a HIP graph (workspace reserved first) and replay it
     several times with eager work in between; every replay matches the oracle,
-    and equals the eager call where the split of the work is fixed."""
+    and equals the eager call bit for bit (the split of the work is fixed)."""
     pk = _pk()
     inp = workloads.make_case(B=4, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(100, 900, 33, 2000),
                               seed=9)
@@ -349,6 +335,5 @@ def test_graph_replay(sched, bitwise):
             torch.cuda.synchronize()
             o = out.float().cpu().numpy().reshape(-1, out.shape[-1])
             compare(f"graph/{sched}/{it}", o, lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
-            if bitwise:
-                assert torch.equal(out, eager_o), it
-                assert torch.equal(lse, eager_l), it
+            assert torch.equal(out, eager_o), it
+            assert torch.equal(lse, eager_l), it
