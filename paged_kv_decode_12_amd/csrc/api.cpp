@@ -61,12 +61,12 @@ struct Plan {
   int64_t slots;         // partial-state slots: two per wave
   // Workspace: one allocation whose first eighth (int_area) holds int32
   // state that is zero when allocated and that every call leaves at zero:
-  // arrival counters (at 0) and markers.  The
+  // the arrival counters (at 0).  The
   // partial LSEs, outputs and the request prefix follow the int area.  The
   // int area's size belongs to the allocation, not the plan, so floats of
   // one plan never lie where another plan keeps int state.  Offsets are
   // relative to each area's start; ws_bytes is the allocation size needed.
-  size_t ws_marks, int_bytes;
+  size_t int_bytes;
   size_t ws_lse, ws_o, ws_pref, float_bytes;
   size_t ws_bytes;
 };
@@ -251,8 +251,7 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   p.slots = (int64_t)2 * nw;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t rows = (size_t)p.slots * p.rows_per_tile;
-  p.ws_marks = up((size_t)p.units * 4);   // the arrival counters come first
-  p.int_bytes = p.ws_marks + up(rows * 4);
+  p.int_bytes = up((size_t)p.units * 4);   // the arrival counters
   p.ws_lse = 0;
   p.ws_o = up(rows * 4);
   p.ws_pref = p.ws_o + up(rows * (size_t)s.D * 4);
@@ -471,7 +470,6 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   char* wi = static_cast<char*>(ws);            // int area
   char* wf = wi + int_area(ws_size);            // floats follow it
   a.counters = reinterpret_cast<int32_t*>(wi);
-  a.marks = reinterpret_cast<int32_t*>(wi + p.ws_marks);
   a.ws_lse = reinterpret_cast<float*>(wf + p.ws_lse);
   a.ws_o = reinterpret_cast<float*>(wf + p.ws_o);
   a.ws_pref = reinterpret_cast<int32_t*>(wf + p.ws_pref);

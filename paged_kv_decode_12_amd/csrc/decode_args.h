@@ -36,7 +36,6 @@ struct DecodeArgs {
   float* ws_lse;                   // [slots][rows_per_tile], base 2
   // int32 state that every call leaves at zero
   int32_t* counters;               // [B * Hkv * row_tiles] blocks of each unit delivered
-  int32_t* marks;                  // [slots][rows_per_tile] unit + 1 of a written partial
   int32_t* ws_pref;                // [B + 1] block prefix of the requests (merge kernel mode)
   // shapes
   int32_t B, Hq, Hkv, g, Lq, ps, P, C, D;

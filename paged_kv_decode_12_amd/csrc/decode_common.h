@@ -344,8 +344,9 @@ __device__ __forceinline__ int slice_of(const Slices& s, int64_t x) {
 // the slice's first segment, 1 for its last (a slice cuts at most those
 // two).  The candidates for a unit are the waves w0 .. w1 whose slices hold
 // its blocks; wave w's piece is its first segment exactly when its slice
-// starts at or after us.  A marker (unit + 1) beside each written partial
-// confirms it.
+// starts at or after us.  A candidate wrote a partial state exactly when its
+// slice is not empty (weighted slices can be), and a unit with a single
+// non-empty candidate was whole in that slice and written directly.
 struct UnitPieces {
   int w0;      // first wave holding a block of the unit
   int n;       // candidates: waves w0 .. w0 + n - 1
@@ -356,11 +357,13 @@ __device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int64_t us, i
   p.n = slice_of(s, ue - 1) - p.w0 + 1;
   return p;
 }
-// Slot of candidate c.
+// Slot of candidate c, and whether it holds a partial state of this call.
 __device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int64_t us,
-                                              int c) {
+                                              int c, bool& written) {
   const int w = p.w0 + c;
-  return 2 * w + (slice_begin(s, w) >= us ? 0 : 1);
+  const int b0 = slice_begin(s, w);
+  written = b0 < slice_begin(s, w + 1);
+  return 2 * w + (b0 >= us ? 0 : 1);
 }
 
 // Waves that take part: at most one per min_wave_blocks blocks, and >= 1.

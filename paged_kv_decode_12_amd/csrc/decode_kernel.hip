@@ -13,12 +13,12 @@
 // equal slices, or weighted by the wave's position on its SIMD), crossing
 // unit boundaries as needed, so a wave's share of the work is set by its
 // weight alone, whatever the mix of lengths.  The slice is one continuous
-// stream of chunks: the last round of a chunk already issues the first loads of the
-// next one (next segment included), and the next segment's Q rows are loaded
-// before the current segment's epilogue.  A unit inside one slice is written
+// stream of chunks: the last round of a chunk already issues the first loads
+// of the next one (next segment included), and the next segment's Q rows are
+// loaded before the current segment's epilogue.  A unit inside one slice is written
 // directly; a unit cut between slices leaves a normalised partial state (o,
-// base-2 LSE) per piece in the slot of the wave that streamed it, with a
-// marker naming the unit.  Either the wave whose blocks complete the unit (an
+// base-2 LSE) per piece in the slot of the wave that streamed it.  Either
+// the wave whose blocks complete the unit (an
 // atomic count of delivered blocks, taken once its slice is streamed) merges
 // the pieces in block order with the base-2 LSE rule (Note / LSE
 // convention: base-2 LSE states are what the cascade merge consumes), or a
@@ -77,11 +77,9 @@ __device__ __forceinline__ void store_item(const DecodeArgs& a, int64_t rowhead,
 // Writes one item of a slice's partial state for a cut unit: the normalised
 // output o = O / L (in the engine's lane-contiguous order, with
 // device-coherent stores so that a merging wave on another CU reads them
-// after its ticket) and, from the row's lead lane, its base-2 LSE and the
-// marker (unit + 1; 0: no marker, for padding rows) that tells the merge this
-// slot holds the unit's partial.
+// after its ticket) and, from the row's lead lane, its base-2 LSE.
 template <class Eng, int D>
-__device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot, int mark,
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
                                               const typename Eng::Lane& ln, int r, int d0,
                                               float M, float L, const float (&O)[8]) {
   constexpr int RT = Eng::kRows;
@@ -89,18 +87,15 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot, int
   float* po = a.ws_o + (int64_t)slot * RT * D;
 #pragma unroll
   for (int e = 0; e < Eng::kItemDims; ++e) store_coherent(po + Eng::pidx(ln, r, e), O[e] * inv);
-  if (d0 == 0) {
-    store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
-    if (mark) store_coherent(a.marks + (int64_t)slot * RT + r, mark);
-  }
+  if (d0 == 0) store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
 }
 
 // Merges the partial states of the cut unit `unit` (linear blocks [us, ue))
-// for all output items of the lane and writes the final values.  Candidate
-// slots are checked 64 at a time (lane c reads candidate c's row-0 marker);
-// the written ones are read kDepth at a time in block order (every item's
-// loads in flight), raising the running maximum once per group.  The markers
-// read are cleared for the next call.
+// for all output items of the lane and writes the final values.  Candidates
+// are taken 64 at a time (lane c works out whether candidate c wrote a
+// partial state); the written ones are read kDepth at a time in block order
+// (every item's loads in flight), raising the running maximum once per
+// group.
 template <class Eng, int D, bool BF16>
 __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int unit,
                                            int us, int ue, const typename Eng::Lane& ln, int lane,
@@ -126,10 +121,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
     const int c = c0 + lane;
     int slot = 0;
     bool valid = false;
-    if (c < up.n) {
-      slot = candidate_slot(up, sl_, us, c);
-      valid = load_coherent(a.marks + (int64_t)slot * RT) == unit + 1;
-    }
+    if (c < up.n) slot = candidate_slot(up, sl_, us, c, valid);
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
     // slot of the batch's first written candidate: off entries of a group
     // read it (finite values) and get weight 0
@@ -171,8 +163,6 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
         Mx[it] = Mn;
       }
     }
-    if (valid)
-      for (int r = 0; r < RT; ++r) store_coherent(a.marks + (int64_t)slot * RT + r, 0);
   }
   // acc / W is the merged normalised output; final_value divides by W + sink
 #pragma unroll
@@ -376,7 +366,7 @@ void decode_kernel(const DecodeArgs a) {
                                                   qhead, d0, d0 == 0, M, Lsum, O);
             }
           } else if (ok) {
-            store_partial<Eng, D>(a, slot, row < R ? unit + 1 : 0, ln, r, d0, M, Lsum, O);
+            store_partial<Eng, D>(a, slot, ln, r, d0, M, Lsum, O);
           }
         }
         if (!sg.whole) {
@@ -432,14 +422,14 @@ void decode_kernel(const DecodeArgs a) {
 
 // Merge kernel (for plans whose cut units leave large partial states): one
 // wave per (unit, row of its tile), launched after the decode kernel.  Lane c
-// checks candidate slot c's marker (64 at a time); the batch maximum of the
+// takes candidate c (64 at a time, written or not); the batch maximum of the
 // written pieces' LSEs and their weights 2^(lse - max) come from wave
 // reductions, and every lane accumulates its D / 64 output dims over those
 // pieces in block order, eight pieces' loads in flight.  Each lane owns its
 // dims, so every sum has a fixed order for a given set of pieces.  Writes out
-// (sink in the denominator) and the base-2 LSE, and clears the markers it
-// read.  A unit with no written partial was whole in one slice and is left as
-// the decode kernel wrote it.
+// (sink in the denominator) and the base-2 LSE.  A unit with fewer than two
+// written partials was whole in one slice and is left as the decode kernel
+// wrote it.
 constexpr int kMergeWaves = 4;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -480,20 +470,19 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   int pos[NDL];
 #pragma unroll
   for (int e = 0; e < NDL; ++e) pos[e] = Eng::ppos(r, lane * NDL + e);
-  bool any = false;
+  int written = 0;   // candidates that wrote a partial state
   for (int c0 = 0; c0 < up.n; c0 += 64) {
     const int c = c0 + lane;
     int slot = 0;
     float l = -INFINITY;
     bool valid = false;
     if (c < up.n) {
-      slot = candidate_slot(up, sl_, us, c);
-      valid = a.marks[(int64_t)slot * RT + r] == unit + 1;
+      slot = candidate_slot(up, sl_, us, c, valid);
       if (valid) l = a.ws_lse[(int64_t)slot * RT + r];
     }
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
     if (m == 0) continue;
-    any = true;
+    written += __builtin_popcountll(m);
     const float Mn = fmaxf(M, wave_max(l));
     const float wt = valid ? rescale(l, Mn) : 0.f;
     const float sc = rescale(M, Mn);
@@ -525,9 +514,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #pragma unroll
         for (int x = 0; x < NDL; ++x) acc[x] = fmaf(wq[e], oq[e][x], acc[x]);
     }
-    if (valid) a.marks[(int64_t)slot * RT + r] = 0;
   }
-  if (!any) return;   // whole in one slice: written by the decode kernel
+  if (written < 2) return;   // whole in one slice: written by the decode kernel
   const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
   const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
   // acc / W is the merged normalised output; final_value divides by W + sink

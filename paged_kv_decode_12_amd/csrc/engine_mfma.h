@@ -42,7 +42,7 @@ __device__ __forceinline__ u32x2 load8_stream(const uint16_t* p) {
 // K rows are read 64 bytes per key per instruction (16 keys per MFMA operand),
 // so each 128-byte line is touched by two instructions in a row
 #ifndef PKVD_MFMA_K_NT
-#define PKVD_MFMA_K_NT 0
+#define PKVD_MFMA_K_NT 1
 #endif
 __device__ __forceinline__ u32x4 load16_k(const uint16_t* p) {
 #if PKVD_MFMA_K_NT
