@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["decode", "plan", "workspace_bytes", "reserve_workspace", "library_path",
-           "PkvdError"]
+__all__ = ["decode", "bind_decode", "plan", "workspace_bytes", "reserve_workspace",
+           "library_path", "PkvdError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PKVD_LIBRARY selects another build of the same library (A/B comparisons)
@@ -143,6 +143,64 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               _ref(_desc(lse) if want_lse else None), ctypes.c_void_p(stream))
     _check(st)
     return (out, lse) if want_lse else out
+
+
+class BoundDecode:
+    """One decode call with its arguments marshalled once (see bind_decode).
+
+    Calling it enqueues pkvd_decode on torch's current stream of q's device
+    (or the given stream) and returns out, or (out, lse).  The tensors are
+    held, not copied: write new inputs into them in place between calls.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_tables, seq_lens_kv, scale, q_len_per_req,
+                 window_left, sinks, out, lse):
+        self._tensors = (q, k_cache, v_cache, block_tables, seq_lens_kv, sinks, out, lse)
+        self._descs = [_desc(t) for t in self._tensors]
+        self._refs = [_ref(d) for d in self._descs]
+        self._scale = ctypes.c_float(scale)
+        self._lq = ctypes.c_int32(q_len_per_req)
+        self._wl = ctypes.c_int32(window_left)
+        self._device = q.device
+        self._result = (out, lse) if lse is not None else out
+
+    def __call__(self, stream=None):
+        r = self._refs
+        if stream is None:
+            stream = torch.cuda.current_stream(self._device).cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        st = _lib.pkvd_decode(r[0], r[1], r[2], r[3], r[4], self._scale, self._lq, self._wl,
+                              r[5], r[6], r[7], ctypes.c_void_p(stream))
+        _check(st)
+        return self._result
+
+
+def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_tables: torch.Tensor, seq_lens_kv: torch.Tensor,
+                scale: Optional[float] = None, q_len_per_req: int = 1, window_left: int = -1,
+                sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, return_lse: bool = False) -> BoundDecode:
+    """The arguments of ``decode`` marshalled once, for calls repeated on the
+    same buffers (a decode step of a serving loop, a benchmark): the returned
+    object enqueues the same pkvd_decode call each time it is called, without
+    rebuilding the descriptors.  Outputs are allocated here when None.  The
+    library checks every argument on every call, as for ``decode``.  The
+    current device must be q's device when it is called."""
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("seq_lens_kv", seq_lens_kv),
+                    ("sinks", sinks), ("out", out), ("lse", lse)):
+        if t is not None and (t.device.type != "cuda" or t.device != dev):
+            raise ValueError(f"{name} must be a GPU tensor on q's device ({dev})")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    if (return_lse or lse is not None) and lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    return BoundDecode(q, k_cache, v_cache, block_tables, seq_lens_kv, float(scale),
+                       int(q_len_per_req), int(window_left), sinks, out, lse)
 
 
 def plan(q, k_cache, block_tables, q_len_per_req: int = 1, window_left: int = -1) -> dict:

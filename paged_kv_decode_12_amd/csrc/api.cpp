@@ -57,6 +57,7 @@ struct Plan {
   int64_t workgroups;
   int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
   int merge_kernel;      // 1: cut units are merged by a second kernel
+  int seg_cost;          // virtual blocks ahead of each unit in the sliced block space
   int slot_w[4];         // slice weights of the waves at position 0..3 on their SIMD
   int64_t slots;         // partial-state slots: two per wave
   // Workspace: one allocation whose first eighth (int_area) holds int32
@@ -67,7 +68,7 @@ struct Plan {
   // one plan never lie where another plan keeps int state.  Offsets are
   // relative to each area's start; ws_bytes is the allocation size needed.
   size_t int_bytes;
-  size_t ws_lse, ws_o, ws_pref, float_bytes;
+  size_t ws_lse, ws_o, ws_pref, ws_vpref, float_bytes;
   size_t ws_bytes;
 };
 
@@ -163,6 +164,12 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
   return f;
 }
 
+// Virtual blocks ahead of each unit in the sliced block space (see make_plan),
+// per engine, measured on MI355X (llama3_8b-shaped batch, VALU engine:
+// 0 -> 114.3 us, 2 -> 109.9, 3 -> 108.3, 4 -> 106.7, 6 -> 107.1; MFMA engine,
+// spec_verify: 0 -> 118.5 us, 6 -> 116.6).
+int default_seg_cost(int path) { return path == pkvd::kPathMfma ? 6 : 4; }
+
 // Default slice weight of the waves at position `slot` on their SIMD.  Equal
 // weights measured fastest for the default engines on MI355X (the MFMA
 // engine at D = 128 runs one wave per SIMD; for the others the second wave
@@ -200,7 +207,12 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   int64_t kcap = s.C * s.ps;
   if (wl >= 0) kcap = std::min<int64_t>(kcap, (int64_t)wl + Lq);
   const int64_t max_blocks = (kcap + pkvd::kBlockKeys - 1) / pkvd::kBlockKeys + 1;
-  if (p.units * max_blocks >= INT32_MAX) return Plan{-1};
+  // Each unit is preceded by seg_cost virtual blocks in the space the waves'
+  // slices divide, so a slice that starts a unit (a segment switch costs the
+  // wave about as long as streaming a few blocks) holds that many fewer real
+  // blocks.  PKVD_SEG_COST overrides the default (0 turns it off).
+  p.seg_cost = std::min(64, std::max(0, env_int("PKVD_SEG_COST", default_seg_cost(p.path))));
+  if (p.units * (max_blocks + p.seg_cost) >= INT32_MAX) return Plan{-1};
 
   const DeviceFit f = device_fit(p.path, p.rows_per_tile, s);
   int64_t nw = (int64_t)f.cus * f.blocks_per_cu * f.group_waves;
@@ -255,7 +267,8 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   p.ws_lse = 0;
   p.ws_o = up(rows * 4);
   p.ws_pref = p.ws_o + up(rows * (size_t)s.D * 4);
-  p.float_bytes = p.ws_pref + up((size_t)(s.B + 1) * 4);
+  p.ws_vpref = p.ws_pref + up((size_t)(s.B + 1) * 4);
+  p.float_bytes = p.ws_vpref + up((size_t)(s.B + 1) * 4);
   // smallest allocation whose int area and remainder hold both parts
   size_t S = std::max(8 * p.int_bytes + 2048, p.float_bytes + p.float_bytes / 7 + 2048);
   S = up(S);
@@ -473,6 +486,8 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   a.ws_lse = reinterpret_cast<float*>(wf + p.ws_lse);
   a.ws_o = reinterpret_cast<float*>(wf + p.ws_o);
   a.ws_pref = reinterpret_cast<int32_t*>(wf + p.ws_pref);
+  a.ws_vpref = reinterpret_cast<int32_t*>(wf + p.ws_vpref);
+  a.seg_cost = p.seg_cost;
   a.merge_kernel = p.merge_kernel;
   for (int r = 0; r < 4; ++r) a.slot_w[r] = p.slot_w[r];
   if (env_int("PKVD_LOG", 0))

@@ -37,6 +37,7 @@ struct DecodeArgs {
   // int32 state that every call leaves at zero
   int32_t* counters;               // [B * Hkv * row_tiles] blocks of each unit delivered
   int32_t* ws_pref;                // [B + 1] block prefix of the requests (merge kernel mode)
+  int32_t* ws_vpref;               // [B + 1] the same in the virtual block space
   // shapes
   int32_t B, Hq, Hkv, g, Lq, ps, P, C, D;
   int32_t window_left;
@@ -46,6 +47,7 @@ struct DecodeArgs {
   int32_t groups;                  // workgroups launched (groups * waves per group >= num_waves)
   int32_t min_wave_blocks;         // a wave gets at least this many blocks (fewer waves run)
   int32_t merge_kernel;            // 1: cut units are merged by a second kernel, not in place
+  int32_t seg_cost;                // virtual blocks ahead of each unit in the sliced space
   int32_t slot_w[4];               // slice weight of the waves at position 0, 1, 2, >= 3 on their SIMD
 #ifdef PKVD_TRACE
   uint64_t* trace;                 // instrumented builds only: [waves][16] timestamps

@@ -339,31 +339,35 @@ __device__ __forceinline__ int slice_of(const Slices& s, int64_t x) {
   return (int)(w < s.NW - 1 ? w : s.NW - 1);
 }
 
-// Where the partial states of a cut unit [us, ue) are.  Wave w writes the
-// partial state of each unit its slice cuts into slot 2 w + side: side 0 for
-// the slice's first segment, 1 for its last (a slice cuts at most those
-// two).  The candidates for a unit are the waves w0 .. w1 whose slices hold
-// its blocks; wave w's piece is its first segment exactly when its slice
-// starts at or after us.  A candidate wrote a partial state exactly when its
-// slice is not empty (weighted slices can be), and a unit with a single
+// Where the partial states of a cut unit are.  Wave w writes the partial
+// state of each unit its slice cuts into slot 2 w + side: side 0 for the
+// slice's first segment, 1 for its last (a slice cuts at most those two).
+// Slices are taken in the virtual block space: the unit starts at virtual
+// block vs and its real blocks sit at [vs + seg_cost, vs + seg_cost + nblk).
+// The candidates are the waves w0 .. w1 whose slices hold those blocks; wave
+// w's piece is its first segment exactly when its slice starts at or after
+// vs (a slice that starts among the unit's virtual blocks starts at the
+// unit's first real block).  Every candidate with a non-empty slice holds
+// real blocks of the unit and wrote a partial state; a unit with a single
 // non-empty candidate was whole in that slice and written directly.
 struct UnitPieces {
   int w0;      // first wave holding a block of the unit
   int n;       // candidates: waves w0 .. w0 + n - 1
 };
-__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int64_t us, int64_t ue) {
+__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int64_t vs, int seg_cost,
+                                                  int nblk) {
   UnitPieces p;
-  p.w0 = slice_of(s, us);
-  p.n = slice_of(s, ue - 1) - p.w0 + 1;
+  p.w0 = slice_of(s, vs + seg_cost);
+  p.n = slice_of(s, vs + seg_cost + nblk - 1) - p.w0 + 1;
   return p;
 }
 // Slot of candidate c, and whether it holds a partial state of this call.
-__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int64_t us,
+__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int64_t vs,
                                               int c, bool& written) {
   const int w = p.w0 + c;
   const int b0 = slice_begin(s, w);
   written = b0 < slice_begin(s, w + 1);
-  return 2 * w + (b0 >= us ? 0 : 1);
+  return 2 * w + (b0 >= vs ? 0 : 1);
 }
 
 // Waves that take part: at most one per min_wave_blocks blocks, and >= 1.
@@ -376,34 +380,50 @@ __device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
 // the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
 // (carve-up) both take the offsets from here.
 struct LdsLayout {
-  int scan, pref, nlen, total;
+  int scan, vscan, pref, vpref, nlen, total;
 };
 __host__ __device__ inline LdsLayout lds_layout(int B, int NT) {
   LdsLayout l;
   l.scan = 0;
-  l.pref = l.scan + NT;
-  l.nlen = l.pref + B + 1;
+  l.vscan = l.scan + NT;
+  l.pref = l.vscan + NT;
+  l.vpref = l.pref + B + 1;
+  l.nlen = l.vpref + B + 1;
   l.total = l.nlen + B;
   return l;
 }
 
-// Builds pref[0..B] and the raw lengths nlen[0..B-1] in LDS (one workgroup,
-// ends with a barrier) and returns T = pref[B].  Requests with no visible key
-// get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
+// The slices divide a virtual block space in which every unit with blocks
+// is preceded by seg_cost virtual blocks that are never streamed: a wave
+// whose slice starts a unit (a segment switch: epilogue, new Q rows, a
+// refilled load ring) gets that many fewer real blocks.  Unit u of request b
+// starts at real block pref[b] + u nblk(b) and virtual block
+// vpref[b] + u (nblk(b) + seg_cost); its real blocks sit at virtual offsets
+// seg_cost .. seg_cost + nblk(b) - 1.  With seg_cost = 0 both spaces agree.
+struct Prefix {
+  int T;    // real blocks
+  int TV;   // virtual blocks
+};
+
+// Builds pref[0..B], vpref[0..B] and the raw lengths nlen[0..B-1] in LDS
+// (one workgroup, ends with a barrier).  Requests with no visible key get
+// out = 0, lse = -inf here, written by workgroup b % gridDim.x.
 template <bool BF16, int NT>
-__device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, int* s_nlen,
-                                            int* s_scan) {
+__device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref, int* s_vpref,
+                                               int* s_nlen, int* s_scan, int* s_vscan) {
   const int B = a.B;
   const int per_req = a.Hkv * a.row_tiles;
+  const int c = a.seg_cost;
   const int CH = (B + NT - 1) / NT;
   const int t = threadIdx.x;
   const int lo = min(B, t * CH), hi = min(B, lo + CH);
-  int sum = 0;
+  int sum = 0, vsum = 0;
   for (int b = lo; b < hi; ++b) {
     const int nraw = a.seq_lens[b];
     s_nlen[b] = nraw;
     const int nb = unit_range_n(a, nraw).nblk;
     sum += nb * per_req;
+    vsum += (nb > 0 ? nb + c : 0) * per_req;
     if (nb == 0 && b % (int)gridDim.x == (int)blockIdx.x) {
       for (int r = b * a.Lq; r < (b + 1) * a.Lq; ++r)
         for (int h = 0; h < a.Hq; ++h) {
@@ -414,21 +434,33 @@ __device__ __forceinline__ int build_prefix(const DecodeArgs& a, int* s_pref, in
     }
   }
   s_scan[t] = sum;
+  s_vscan[t] = vsum;
   __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {      // inclusive Hillis-Steele scan
+  for (int off = 1; off < NT; off <<= 1) {      // inclusive Hillis-Steele scans
     const int v = t >= off ? s_scan[t - off] : 0;
+    const int vv = t >= off ? s_vscan[t - off] : 0;
     __syncthreads();
     s_scan[t] += v;
+    s_vscan[t] += vv;
     __syncthreads();
   }
-  int excl = s_scan[t] - sum;
+  int excl = s_scan[t] - sum, vexcl = s_vscan[t] - vsum;
   for (int b = lo; b < hi; ++b) {
     s_pref[b] = excl;
-    excl += unit_range_n(a, s_nlen[b]).nblk * per_req;
+    s_vpref[b] = vexcl;
+    const int nb = unit_range_n(a, s_nlen[b]).nblk;
+    excl += nb * per_req;
+    vexcl += (nb > 0 ? nb + c : 0) * per_req;
   }
-  if (t == NT - 1) s_pref[B] = s_scan[t];
+  if (t == NT - 1) {
+    s_pref[B] = s_scan[t];
+    s_vpref[B] = s_vscan[t];
+  }
   __syncthreads();
-  return s_pref[B];
+  Prefix p;
+  p.T = s_pref[B];
+  p.TV = s_vpref[B];
+  return p;
 }
 
 // Largest b with pref[b] <= pos (the request holding linear block pos).
@@ -449,17 +481,19 @@ struct Segment {
   UnitRange u;
   int blk_begin, blk_end;    // absolute 16-key blocks [blk_begin, blk_end)
   int ustart, uend;          // the unit's linear block range (the block space fits int32)
+  int vstart;                // the unit's first virtual block
   int whole;                 // the range holds the entire unit (int: stays in registers)
   int side;                  // 0: first segment of the wave, 1: a later one
 };
 
 __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
-                                          const int* s_nlen, int pos, int wave_lo,
-                                          int wave_hi) {
+                                          const int* s_vpref, const int* s_nlen, int pos,
+                                          int wave_lo, int wave_hi) {
   Segment g;
   g.b = find_request(s_pref, a.B, pos);
   g.u = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[g.b]));
   const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[g.b]);
+  const int vpref_b = __builtin_amdgcn_readfirstlane(s_vpref[g.b]);
   const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
   const int off = pos - pref_b;
   const int per_req = a.Hkv * a.row_tiles;
@@ -469,12 +503,27 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
   g.tile = uidx - g.kvh * a.row_tiles;
   g.ustart = pref_b + uidx * nb;
   g.uend = g.ustart + nb;
+  g.vstart = vpref_b + uidx * (nb + a.seg_cost);
   const int seg_end = wave_hi < g.uend ? wave_hi : g.uend;
   g.blk_begin = g.u.first_blk + (pos - g.ustart);
   g.blk_end = g.blk_begin + (seg_end - pos);
   g.whole = pos == g.ustart && seg_end == g.uend;
   g.side = pos == wave_lo ? 0 : 1;
   return g;
+}
+
+// The real block at virtual block v (0 <= v <= TV): the unit's first real
+// block for its virtual blocks, T at the end.
+__device__ __forceinline__ int real_of(const DecodeArgs& a, const int* s_pref, const int* s_vpref,
+                                       const int* s_nlen, const Prefix& p, int v) {
+  if (v >= p.TV) return p.T;
+  const int b = find_request(s_vpref, a.B, v);   // a request with blocks
+  const int nb = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[b])).nblk;
+  const int vu = nb + a.seg_cost;
+  const int off = v - __builtin_amdgcn_readfirstlane(s_vpref[b]);
+  const int ul = off / vu;
+  const int o = off - ul * vu - a.seg_cost;
+  return __builtin_amdgcn_readfirstlane(s_pref[b]) + ul * nb + (o > 0 ? o : 0);
 }
 
 // ---------------------------------------------------------------------------

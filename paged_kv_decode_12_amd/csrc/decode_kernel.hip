@@ -98,14 +98,14 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
 // group.
 template <class Eng, int D, bool BF16>
 __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int unit,
-                                           int us, int ue, const typename Eng::Lane& ln, int lane,
-                                           int R) {
+                                           int vs, int nblk, const typename Eng::Lane& ln,
+                                           int lane, int R) {
   constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
   const int per_req = a.Hkv * a.row_tiles;
   const int b = unit / per_req, uidx = unit - b * per_req;
   const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
-  const UnitPieces up = unit_pieces(sl_, us, ue);
+  const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, nblk);
   int rr[NI], dd[NI];
 #pragma unroll
   for (int it = 0; it < NI; ++it) Eng::item_pos(ln, it, rr[it], dd[it]);
@@ -121,7 +121,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
     const int c = c0 + lane;
     int slot = 0;
     bool valid = false;
-    if (c < up.n) slot = candidate_slot(up, sl_, us, c, valid);
+    if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
     // slot of the batch's first written candidate: off entries of a group
     // read it (finite values) and get weight 0
@@ -187,7 +187,9 @@ void decode_kernel(const DecodeArgs a) {
   extern __shared__ int lds[];
   const LdsLayout L = lds_layout(a.B, kThreads);
   int* s_scan = lds + L.scan;
+  int* s_vscan = lds + L.vscan;
   int* s_pref = lds + L.pref;
+  int* s_vpref = lds + L.vpref;
   int* s_nlen = lds + L.nlen;
 
   const int lane = threadIdx.x & 63;
@@ -197,20 +199,28 @@ void decode_kernel(const DecodeArgs a) {
 #ifdef PKVD_TRACE
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 #endif
-  const int T = uniform(build_prefix<BF16, kThreads>(a, s_pref, s_nlen, s_scan));
+  Prefix pf = build_prefix<BF16, kThreads>(a, s_pref, s_vpref, s_nlen, s_scan, s_vscan);
+  pf.T = uniform(pf.T);
+  pf.TV = uniform(pf.TV);
+  const int T = pf.T;
 #ifdef PKVD_TRACE
   const uint64_t t_prefix = __builtin_amdgcn_s_memrealtime();
 #endif
-  if (a.merge_kernel && blockIdx.x == 0)   // the prefix, for the merge kernel
-    for (int i = threadIdx.x; i <= a.B; i += kThreads) a.ws_pref[i] = s_pref[i];
+  if (a.merge_kernel && blockIdx.x == 0)   // the prefixes, for the merge kernel
+    for (int i = threadIdx.x; i <= a.B; i += kThreads) {
+      a.ws_pref[i] = s_pref[i];
+      a.ws_vpref[i] = s_vpref[i];
+    }
   const int NW = wave_count(a, T);
   // Each workgroup takes a run of consecutive slices (its CU then streams
   // neighbouring kv heads of the same requests): ceil(NW / groups) waves of
   // each group are active, so a short grid still spreads over all groups.
   const int active = (NW + a.groups - 1) / a.groups;
   const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
-  const Slices sl_ = make_slices(a, T, NW);
-  const int lo = T ? slice_begin(sl_, gw) : 0, hi = T ? slice_begin(sl_, gw + 1) : 0;
+  // slices of the virtual block space, mapped back to real blocks
+  const Slices sl_ = make_slices(a, pf.TV, NW);
+  const int lo = T ? real_of(a, s_pref, s_vpref, s_nlen, pf, slice_begin(sl_, gw)) : 0;
+  const int hi = T ? real_of(a, s_pref, s_vpref, s_nlen, pf, slice_begin(sl_, gw + 1)) : 0;
   if (T == 0 || gw >= NW || lo >= hi) return;   // no slice
   PKVD_COUNT(a, gw, 0, t_start);
   PKVD_COUNT(a, gw, 1, t_prefix);
@@ -258,7 +268,7 @@ void decode_kernel(const DecodeArgs a) {
     if (!c.last) {
       n = make_chunk(c.sg, c.ce);
     } else if (pos < hi) {
-      const Segment sg = locate(a, s_pref, s_nlen, pos, lo, hi);
+      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, pos, lo, hi);
       n = make_chunk(sg, sg.blk_begin);
     }
     return n;
@@ -283,17 +293,23 @@ void decode_kernel(const DecodeArgs a) {
   {
     // pieces of units the slice cuts: at most its first and last segments;
     // their tickets are taken once the slice is streamed
-    int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_us[2] = {0, 0}, pend_ue[2] = {0, 0};
+    int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_vs[2] = {0, 0}, pend_nb[2] = {0, 0};
     Chunk cur;
     {
-      const Segment sg = locate(a, s_pref, s_nlen, lo, lo, hi);
+      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, lo, lo, hi);
       cur = make_chunk(sg, sg.blk_begin);
     }
     PageWindow pw = fetch_pages(cur);
     Chunk nxt = next_chunk(cur);
     PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
     PKVD_STAMP(a, gw, 3);
-    typename Eng::Q qr;
+    // Q rows of the segment being scored (qr) and of the next one (qn).  The
+    // next segment's rows are loaded as soon as it is known, at the start of
+    // the current segment's last chunk, so they have long arrived when the
+    // segment switches; loading them at the switch made the first score of
+    // the new segment wait for that load, and so for every K/V load issued
+    // before it (one memory latency per switch).
+    typename Eng::Q qr, qn;
     typename Eng::State st;
     int max_lo = 0, min_hi = 0;
     typename Eng::Buf buf[NBUF];
@@ -306,6 +322,7 @@ void decode_kernel(const DecodeArgs a) {
     for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
     PKVD_STAMP(a, gw, 4);
     Eng::fetch_q(a, cur.sg, R, ln, qr);
+    if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qn);
     Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
     PKVD_STAMP(a, gw, 2);
 
@@ -345,9 +362,8 @@ void decode_kernel(const DecodeArgs a) {
         }
       }
       if (cur.last) {
-        // the segment is done.  The next segment's Q rows are loaded first, so
-        // their latency overlaps this epilogue (its first groups are in flight)
-        if (nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qr);
+        // the segment is done: the next one's Q rows (loaded a chunk ago)
+        if (nxt.valid) qr = qn;
         // the whole unit's output, or this piece's partial
         const Segment& sg = cur.sg;
         const int unit = (sg.b * a.Hkv + sg.kvh) * a.row_tiles + sg.tile;
@@ -373,8 +389,8 @@ void decode_kernel(const DecodeArgs a) {
           const int k = sg.side;
           pend_unit[k] = unit;
           pend_n[k] = sg.blk_end - sg.blk_begin;
-          pend_us[k] = sg.ustart;
-          pend_ue[k] = sg.uend;
+          pend_vs[k] = sg.vstart;
+          pend_nb[k] = sg.uend - sg.ustart;
         }
 #ifdef PKVD_TRACE
         if (n_seg++ == 0) PKVD_STAMP(a, gw, 5);
@@ -386,6 +402,7 @@ void decode_kernel(const DecodeArgs a) {
       if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
       nxt = next_chunk(cur);
       if (nxt.valid) pwn = fetch_pages(nxt);
+      if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qn);
     }
     PKVD_STAMP(a, gw, 6);
 
@@ -401,9 +418,9 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         if (pend_unit[k] < 0) continue;
-        if (uniform(prev[k]) + pend_n[k] != pend_ue[k] - pend_us[k]) continue;
+        if (uniform(prev[k]) + pend_n[k] != pend_nb[k]) continue;
         if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-        merge_unit<Eng, D, BF16>(a, sl_, pend_unit[k], pend_us[k], pend_ue[k], ln, lane, R);
+        merge_unit<Eng, D, BF16>(a, sl_, pend_unit[k], pend_vs[k], pend_nb[k], ln, lane, R);
       }
     }
   }
@@ -459,10 +476,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (u.nblk == 0) return;
   const int T = a.ws_pref[a.B];
   const int NW = wave_count(a, T);
-  const Slices sl_ = make_slices(a, T, NW);
+  const Slices sl_ = make_slices(a, a.ws_vpref[a.B], NW);
   const int64_t us = a.ws_pref[b] + (int64_t)uidx * u.nblk, ue = us + u.nblk;
+  const int64_t vs = a.ws_vpref[b] + (int64_t)uidx * (u.nblk + a.seg_cost);
   if (ue > T) return;
-  const UnitPieces up = unit_pieces(sl_, us, ue);
+  const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, u.nblk);
   if (up.n == 1) return;   // inside one slice: written whole by the decode kernel
   float M = -INFINITY, W = 0.f, acc[NDL];
 #pragma unroll
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     float l = -INFINITY;
     bool valid = false;
     if (c < up.n) {
-      slot = candidate_slot(up, sl_, us, c, valid);
+      slot = candidate_slot(up, sl_, vs, c, valid);
       if (valid) l = a.ws_lse[(int64_t)slot * RT + r];
     }
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);

@@ -134,6 +134,12 @@ SCHEDULES = {
                  "PKVD_SLOT_W": "140,100", "PKVD_FORCE_PATH": "0"},
     "mk_weighted": {"PKVD_WAVES": "24", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_GROUPS": "3",
                     "PKVD_SLOT_W": "90,120", "PKVD_MERGE_KERNEL": "1", "PKVD_FORCE_PATH": "1"},
+    # virtual blocks ahead of every unit in the sliced space (slices that
+    # start units hold fewer real blocks; some slices hold none)
+    "segcost": {"PKVD_SEG_COST": "5", "PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1"},
+    "mk_segcost": {"PKVD_SEG_COST": "3", "PKVD_WAVES": "40", "PKVD_MIN_WAVE_BLOCKS": "1",
+                   "PKVD_GROUPS": "5", "PKVD_SLOT_W": "130,100", "PKVD_MERGE_KERNEL": "1",
+                   "PKVD_FORCE_PATH": "0"},
 }
 
 
@@ -234,7 +240,10 @@ def test_schedule_invariance(name):
                   {"PKVD_SLOT_W": "124,100"}, {"PKVD_SLOT_W": "100,130"},
                   {"PKVD_SLOT_W": "100"},
                   {"PKVD_FORCE_PATH": "0", "PKVD_SLOT_W": "300,100"},
-                  {"PKVD_FORCE_PATH": "0", "PKVD_SLOT_W": "100,250", "PKVD_MERGE_KERNEL": "1"}):
+                  {"PKVD_FORCE_PATH": "0", "PKVD_SLOT_W": "100,250", "PKVD_MERGE_KERNEL": "1"},
+                  {"PKVD_SEG_COST": "3"}, {"PKVD_SEG_COST": "0"},
+                  {"PKVD_SEG_COST": "17", "PKVD_MERGE_KERNEL": "1"},
+                  {"PKVD_SEG_COST": "40", "PKVD_MERGE_KERNEL": "0"}):
         log(f"[invariance] config={name} {knobs}")
         with env(**knobs):
             o, l = run_gpu(d)
@@ -300,7 +309,8 @@ def test_short_rows_out_of_contract():
     compare("short_rows", out, lse, ref_out, ref_lse)
 
 
-@pytest.mark.parametrize("sched", ["cut7", "auto", "mk_cut7", "weighted", "mk_weighted"])
+@pytest.mark.parametrize("sched", ["cut7", "auto", "mk_cut7", "weighted", "mk_weighted", "segcost",
+                                   "mk_segcost"])
 def test_graph_replay(sched):
     """Capture one call in a HIP graph (workspace reserved first) and replay it
     several times with eager work in between; every replay matches the oracle,
@@ -337,3 +347,30 @@ def test_graph_replay(sched):
             compare(f"graph/{sched}/{it}", o, lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
             assert torch.equal(out, eager_o), it
             assert torch.equal(lse, eager_l), it
+
+
+def test_bound_decode():
+    """bind_decode marshals once; repeated calls equal decode() bit for bit
+    and follow in-place updates of the inputs."""
+    pk = _pk()
+    inp = workloads.make_case(B=3, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(5, 300, 131),
+                              sinks=True, seed=11)
+    ref_out, ref_lse, _ = oracle.decode(inp)
+    d = to_dev(inp)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens_kv"])
+    kw = dict(scale=d["scale"], q_len_per_req=d["q_len_per_req"], window_left=d["window_left"],
+              sinks=d.get("sinks"))
+    e_out, e_lse = pk.decode(*args, return_lse=True, **kw)
+    call = pk.bind_decode(*args, return_lse=True, **kw)
+    for it in range(3):
+        out, lse = call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out) and torch.equal(lse, e_lse), it
+    compare("bound", out.float().cpu().numpy().reshape(-1, out.shape[-1]),
+            lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
+    # new query values written in place are picked up by the next call
+    d["q"].mul_(-1)
+    out2, _ = call()
+    e2 = pk.decode(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, e2)
