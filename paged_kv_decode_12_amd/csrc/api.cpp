@@ -158,7 +158,7 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
   // (per-wave start stamps: half the waves began only when the first half
   // was done), so the grid is never sized for more than one.
   const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
-                                           pkvd::decode_lds_bytes((int)s.B, 64 * f.group_waves));
+                                           pkvd::decode_lds_bytes((int)s.B, 64 * f.group_waves, 0));
   if (n <= 0) (void)hipGetLastError();
   f.blocks_per_cu = 1;
   return f;
@@ -427,6 +427,10 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
     if (!sinks->data || sinks->ndim != 1 || sinks->dtype != PKVD_F32 || sinks->shape[0] != s.Hq ||
         (s.Hq > 1 && sinks->strides[0] != 1))
       return fail(PKVD_ERR_INVALID_ARG, "sinks must be a contiguous float32 (num_heads_qo,) tensor");
+    // the decode kernel stages the sink logits in LDS
+    if (s.Hq > pkvd::kMaxSinkHeads)
+      return fail(PKVD_ERR_UNSUPPORTED, "sinks with num_heads_qo=%lld > %d", (long long)s.Hq,
+                  pkvd::kMaxSinkHeads);
   }
   if (out->ndim != 3 || out->dtype != q->dtype || out->shape[0] != s.R || out->shape[1] != s.Hq ||
       out->shape[2] != s.D || !contiguous(out))

@@ -9,6 +9,7 @@
 namespace pkvd {
 
 constexpr int kBlockKeys = 16;   // keys per block: the unit a wave loads and scores
+constexpr int kMaxSinkHeads = 4096;   // sink logits the decode kernel stages in LDS
 constexpr int kSimdsPerCu = 4;   // a decode workgroup holds WPE waves on each SIMD of a CU
 constexpr int kMaxBatch = 8192;        // requests per call (the schedule keeps a prefix in LDS)
 
@@ -61,8 +62,9 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool 
 // waves one CU holds at the kernel's register budget, so one workgroup fills
 // a CU and every wave of a CU starts together.
 int decode_group_waves(int path, int rows_per_tile, int head_dim);
-// Dynamic LDS bytes of a launch for B requests, `threads` per workgroup.
-size_t decode_lds_bytes(int B, int threads);
+// Dynamic LDS bytes of a launch for B requests, `threads` per workgroup and
+// `sinks` sink logits staged in LDS.
+size_t decode_lds_bytes(int B, int threads, int sinks);
 // Workgroups of the decode kernel that fit on one CU at once (0 on error).
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool page_pow2,
                          size_t lds_bytes);

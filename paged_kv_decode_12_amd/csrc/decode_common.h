@@ -222,12 +222,13 @@ __device__ __forceinline__ UnitRange unit_range(const DecodeArgs& a, int b) {
 // lse = M + log2 L (keys only).  An empty row (L = 0) gives out = 0 and
 // lse = -inf.  M and L are in base-2 units (Parameters / sinks; Note / LSE
 // convention).
+// `sink` is the row's sink logit (sinks[h], unscaled) when has_sink.
 template <bool BF16>
-__device__ __forceinline__ float final_value(const DecodeArgs& a, int qhead, float M, float L,
+__device__ __forceinline__ float final_value(bool has_sink, float sink, float M, float L,
                                              float O) {
   if (!(L > 0.f)) return 0.f;
   float Z = L;
-  if (a.sinks) Z += fast_exp2(a.sinks[qhead] * kLog2e - M);
+  if (has_sink) Z += fast_exp2(sink * kLog2e - M);
   return O / Z;
 }
 
@@ -380,16 +381,18 @@ __device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
 // the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
 // (carve-up) both take the offsets from here.
 struct LdsLayout {
-  int scan, vscan, pref, vpref, nlen, total;
+  int scan, vscan, pref, vpref, nlen, sink, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int B, int NT) {
+// NS: sink logits staged in LDS (Hq when they are, else 0).
+__host__ __device__ inline LdsLayout lds_layout(int B, int NT, int NS) {
   LdsLayout l;
   l.scan = 0;
   l.vscan = l.scan + NT;
   l.pref = l.vscan + NT;
   l.vpref = l.pref + B + 1;
   l.nlen = l.vpref + B + 1;
-  l.total = l.nlen + B;
+  l.sink = l.nlen + B;
+  l.total = l.sink + NS;
   return l;
 }
 
@@ -405,12 +408,13 @@ struct Prefix {
   int TV;   // virtual blocks
 };
 
-// Builds pref[0..B], vpref[0..B] and the raw lengths nlen[0..B-1] in LDS
-// (one workgroup, ends with a barrier).  Requests with no visible key get
+// Builds pref[0..B], vpref[0..B], the raw lengths nlen[0..B-1] and (when
+// staged) the sink logits in LDS (one workgroup, ends with a barrier).  Requests with no visible key get
 // out = 0, lse = -inf here, written by workgroup b % gridDim.x.
 template <bool BF16, int NT>
 __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref, int* s_vpref,
-                                               int* s_nlen, int* s_scan, int* s_vscan) {
+                                               int* s_nlen, int* s_scan, int* s_vscan,
+                                               float* s_sink) {
   const int B = a.B;
   const int per_req = a.Hkv * a.row_tiles;
   const int c = a.seg_cost;
@@ -433,6 +437,8 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
         }
     }
   }
+  if (a.sinks)
+    for (int h = t; h < a.Hq; h += NT) s_sink[h] = a.sinks[h];
   s_scan[t] = sum;
   s_vscan[t] = vsum;
   __syncthreads();
@@ -463,16 +469,27 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
   return p;
 }
 
-// Largest b with pref[b] <= pos (the request holding linear block pos).
-// LDS reads here are wave-uniform (readfirstlane keeps the schedule in SGPRs).
+// Largest b with pref[b] <= pos (the request holding linear block pos), for
+// a nondecreasing pref with pref[0] <= pos.  A 64-way search: each lane
+// reads one sample of the range and a ballot picks the last sample <= pos,
+// so B <= 64 takes one LDS read (a binary search takes log2 B dependent
+// reads).  Called by all lanes of a wave with a wave-uniform pos.
 __device__ __forceinline__ int find_request(const int* s_pref, int B, int pos) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= pos) lo = mid;
-    else hi = mid - 1;
+  const int lane = __lane_id();
+  int base = 0, span = B;   // the answer lies in [base, base + span)
+  while (span > 64) {
+    const int stride = (span + 63) >> 6;
+    const int idx = base + lane * stride;
+    const bool ok = idx < base + span && s_pref[idx] <= pos;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok);   // lane 0 is always set
+    const int k = 63 - __builtin_clzll(m);
+    const int nb = base + k * stride;
+    span = min(stride, base + span - nb);
+    base = nb;
   }
-  return lo;
+  const bool ok = lane < span && s_pref[base + lane] <= pos;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+  return base + (63 - __builtin_clzll(m));
 }
 
 // A unit's slice of one wave's range.

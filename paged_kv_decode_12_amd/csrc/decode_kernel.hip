@@ -60,13 +60,19 @@ using namespace dev;
 // Writes one output item (N = 8 or 4 consecutive dims from d0) and, from the
 // row's lead lane, its LSE.
 template <int D, int N, bool BF16>
-__device__ __forceinline__ void store_item(const DecodeArgs& a, int64_t rowhead, int qhead, int d0,
-                                           bool lead, float M, float L, const float (&O)[8]) {
+__device__ __forceinline__ void store_item(const DecodeArgs& a, const float* s_sink,
+                                           int64_t rowhead, int qhead, int d0, bool lead, float M,
+                                           float L, const float (&O)[8]) {
+  // the decode kernel keeps the sink logits in LDS: a global load here would
+  // make the wave wait for every K/V load still in flight
+  const bool has_sink = a.sinks != nullptr;
+  float sink = 0.f;
+  if (has_sink) sink = s_sink[qhead];
   uint32_t w[4];
 #pragma unroll
   for (int u = 0; u < N / 2; ++u)
-    w[u] = Fmt<BF16>::pack2(final_value<BF16>(a, qhead, M, L, O[2 * u]),
-                            final_value<BF16>(a, qhead, M, L, O[2 * u + 1]));
+    w[u] = Fmt<BF16>::pack2(final_value<BF16>(has_sink, sink, M, L, O[2 * u]),
+                            final_value<BF16>(has_sink, sink, M, L, O[2 * u + 1]));
   if constexpr (N == 8)
     *reinterpret_cast<u32x4*>(a.out + (int64_t)rowhead * D + d0) = u32x4{w[0], w[1], w[2], w[3]};
   else
@@ -97,9 +103,9 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
 // (every item's loads in flight), raising the running maximum once per
 // group.
 template <class Eng, int D, bool BF16>
-__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl_, int unit,
-                                           int vs, int nblk, const typename Eng::Lane& ln,
-                                           int lane, int R) {
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const float* s_sink,
+                                           const Slices& sl_, int unit, int vs, int nblk,
+                                           const typename Eng::Lane& ln, int lane, int R) {
   constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
   const int per_req = a.Hkv * a.row_tiles;
@@ -170,8 +176,8 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const Slices& sl
     const int r = rr[it], row = tile * RT + r;
     if (!(r < RT && row < R)) continue;
     const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
-    store_item<D, N, BF16>(a, ((int64_t)b * a.Lq + ti) * a.Hq + qhead, qhead, dd[it], dd[it] == 0,
-                           Mx[it], W[it], acc[it]);
+    store_item<D, N, BF16>(a, s_sink, ((int64_t)b * a.Lq + ti) * a.Hq + qhead, qhead, dd[it],
+                           dd[it] == 0, Mx[it], W[it], acc[it]);
   }
 }
 
@@ -185,12 +191,13 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int kWindow = 128;                        // block-table columns per chunk
   constexpr int GPB = Eng::kGroupsPerBlock, KPG = Eng::kKeysPerGroup;
   extern __shared__ int lds[];
-  const LdsLayout L = lds_layout(a.B, kThreads);
+  const LdsLayout L = lds_layout(a.B, kThreads, a.sinks ? a.Hq : 0);
   int* s_scan = lds + L.scan;
   int* s_vscan = lds + L.vscan;
   int* s_pref = lds + L.pref;
   int* s_vpref = lds + L.vpref;
   int* s_nlen = lds + L.nlen;
+  float* s_sink = reinterpret_cast<float*>(lds + L.sink);
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -199,7 +206,7 @@ void decode_kernel(const DecodeArgs a) {
 #ifdef PKVD_TRACE
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 #endif
-  Prefix pf = build_prefix<BF16, kThreads>(a, s_pref, s_vpref, s_nlen, s_scan, s_vscan);
+  Prefix pf = build_prefix<BF16, kThreads>(a, s_pref, s_vpref, s_nlen, s_scan, s_vscan, s_sink);
   pf.T = uniform(pf.T);
   pf.TV = uniform(pf.TV);
   const int T = pf.T;
@@ -378,7 +385,8 @@ void decode_kernel(const DecodeArgs a) {
           if (sg.whole) {
             if (ok && row < R) {
               const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
-              store_item<D, Eng::kItemDims, BF16>(a, ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
+              store_item<D, Eng::kItemDims, BF16>(a, s_sink,
+                                                  ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
                                                   qhead, d0, d0 == 0, M, Lsum, O);
             }
           } else if (ok) {
@@ -420,7 +428,8 @@ void decode_kernel(const DecodeArgs a) {
         if (pend_unit[k] < 0) continue;
         if (uniform(prev[k]) + pend_n[k] != pend_nb[k]) continue;
         if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-        merge_unit<Eng, D, BF16>(a, sl_, pend_unit[k], pend_vs[k], pend_nb[k], ln, lane, R);
+        merge_unit<Eng, D, BF16>(a, s_sink, sl_, pend_unit[k], pend_vs[k], pend_nb[k], ln, lane,
+                                 R);
       }
     }
   }
@@ -536,13 +545,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (written < 2) return;   // whole in one slice: written by the decode kernel
   const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
   const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
+  const bool has_sink = a.sinks != nullptr;
+  const float sink = has_sink ? a.sinks[qhead] : 0.f;
   // acc / W is the merged normalised output; final_value divides by W + sink
   if constexpr (NDL == 2) {
     *reinterpret_cast<uint32_t*>(a.out + rowhead * D + 2 * lane) =
-        Fmt<BF16>::pack2(final_value<BF16>(a, qhead, M, W, acc[0]),
-                         final_value<BF16>(a, qhead, M, W, acc[1]));
+        Fmt<BF16>::pack2(final_value<BF16>(has_sink, sink, M, W, acc[0]),
+                         final_value<BF16>(has_sink, sink, M, W, acc[1]));
   } else {
-    a.out[rowhead * D + lane] = Fmt<BF16>::encode(final_value<BF16>(a, qhead, M, W, acc[0]));
+    a.out[rowhead * D + lane] = Fmt<BF16>::encode(final_value<BF16>(has_sink, sink, M, W, acc[0]));
   }
   if (a.lse && lane == 0) a.lse[rowhead] = W > 0.f ? M + log2f(W) : -INFINITY;
 }
@@ -645,8 +656,8 @@ int decode_group_waves(int path, int rows_per_tile, int head_dim) {
   return kSimdsPerCu * wpe;
 }
 
-size_t decode_lds_bytes(int B, int threads) {
-  return sizeof(int) * (size_t)lds_layout(B, threads).total;
+size_t decode_lds_bytes(int B, int threads, int sinks) {
+  return sizeof(int) * (size_t)lds_layout(B, threads, sinks).total;
 }
 
 int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
@@ -668,7 +679,9 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool 
   const int waves = decode_group_waves(path, rows_per_tile, a.D);
   if (!waves || (int64_t)a.groups * waves < a.num_waves) return hipErrorInvalidValue;
   const dim3 grid(a.groups);
-  hipLaunchKernelGGL(k, grid, dim3(64 * waves), decode_lds_bytes(a.B, 64 * waves), stream, a);
+  hipLaunchKernelGGL(k, grid, dim3(64 * waves), decode_lds_bytes(a.B, 64 * waves,
+                                                                a.sinks ? a.Hq : 0),
+                     stream, a);
   if (!a.merge_kernel) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

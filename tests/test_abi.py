@@ -140,3 +140,13 @@ def test_plans_of_the_workloads():
         assert p["workgroups"] * 16 >= p["waves"] >= 1
         ws = pk.workspace_bytes(q, k, bt, w.q_len_per_req, w.window_left)
         assert ws >= 2 * p["waves"] * p["rows_per_tile"] * (w.D + 1) * 4
+
+
+def test_sinks_beyond_lds_staging_unsupported():
+    """The decode kernel stages the sink logits in LDS (at most 4096 heads)."""
+    Hq = 4104
+    inp = base_inputs()
+    q = torch.zeros(2, Hq, 64, dtype=torch.bfloat16)
+    st = FakeDev(inp).call(q=q, out=torch.zeros_like(q), lse=None, sinks=torch.zeros(Hq))
+    assert st == 2, pk._lib.pkvd_last_error()
+    assert b"sinks" in pk._lib.pkvd_last_error()
