@@ -103,7 +103,8 @@ typedef struct {
  *   stream       hipStream_t (passed as void*); NULL = the default stream.
  *
  * Supported: D in {64, 128}; 1 <= page_size <= 256; Hq % Hkv == 0;
- * B <= 8192 requests.
+ * B <= 8192 requests; with sinks, Hq <= 4096 (the kernel keeps the sink
+ * logits in on-chip memory).  Others return PKVD_ERR_UNSUPPORTED.
  * Work is only enqueued; the call never synchronises and never reads device
  * data on the host: one persistent kernel splits the total work evenly over
  * its waves from seq_lens_kv on the device.  A workspace for the partial
