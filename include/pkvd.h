@@ -158,6 +158,34 @@ const char* pkvd_status_string(int status);
 /* Library version, e.g. "0.1.0". */
 const char* pkvd_version(void);
 
+/*
+ * pkvd_merge_states -- the cascade merge: combine S partial attention states
+ * of the same (row, head), each computed over its own disjoint set of keys,
+ * into the state over their union.  A state is the pair this library's
+ * decode writes: a normalised output and its base-2 log-sum-exp, the form the
+ * cascade-merge kernels consume (cudnn_batch_decode_with_kv_cache, Note /
+ * LSE convention).  For every row r and head h:
+ *   v_out[r, h, :] = sum_s 2^{s[s, r, h]} v[s, r, h, :]
+ *                    / (sum_s 2^{s[s, r, h]} + e^{sinks[h]})
+ *   s_out[r, h]    = log2 sum_s 2^{s[s, r, h]}
+ * with every exponent taken relative to the largest.  A state with
+ * s = -inf is empty and weighs 0 (its v is never read into the sum); rows
+ * whose states are all empty give v_out = 0, s_out = -inf.
+ *
+ *   v      (S, R, H, D) bf16, fp16 or fp32, contiguous, device memory
+ *   s      (S, R, H) fp32 contiguous: base-2 LSE of each state
+ *   sinks  NULL, or fp32 (H,) contiguous: a logit added to the denominator
+ *          only (Parameters / sinks)
+ *   v_out  (R, H, D), v's dtype, contiguous; caller-owned
+ *   s_out  NULL, or fp32 (R, H) contiguous; caller-owned
+ *   stream hipStream_t (passed as void*); NULL = the default stream
+ * S >= 1; D >= 1.  The library allocates nothing for this call and never
+ * synchronises.  Errors: PKVD_ERR_INVALID_ARG before any HIP call;
+ * PKVD_ERR_HIP when the launch fails (message from pkvd_last_error()).
+ */
+int pkvd_merge_states(const pkvd_tensor* v, const pkvd_tensor* s, const pkvd_tensor* sinks,
+                      pkvd_tensor* v_out, pkvd_tensor* s_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["decode", "bind_decode", "plan", "workspace_bytes", "reserve_workspace",
-           "library_path", "PkvdError"]
+__all__ = ["decode", "bind_decode", "merge_states", "plan", "workspace_bytes",
+           "reserve_workspace", "library_path", "PkvdError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PKVD_LIBRARY selects another build of the same library (A/B comparisons)
@@ -61,6 +61,8 @@ def _load():
     lib.pkvd_status_string.restype = ctypes.c_char_p
     lib.pkvd_status_string.argtypes = [ctypes.c_int]
     lib.pkvd_version.restype = ctypes.c_char_p
+    lib.pkvd_merge_states.restype = ctypes.c_int
+    lib.pkvd_merge_states.argtypes = [P, P, P, P, P, ctypes.c_void_p]
     return lib
 
 
@@ -201,6 +203,36 @@ def bind_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     return BoundDecode(q, k_cache, v_cache, block_tables, seq_lens_kv, float(scale),
                        int(q_len_per_req), int(window_left), sinks, out, lse)
+
+
+def merge_states(v: torch.Tensor, s: torch.Tensor, sinks: Optional[torch.Tensor] = None,
+                 v_out: Optional[torch.Tensor] = None, s_out: Optional[torch.Tensor] = None,
+                 return_lse: bool = True, stream=None):
+    """Cascade merge of S partial states over disjoint key sets (pkvd_merge_states).
+
+    v (S, rows, heads, D) bf16/fp16/fp32 and s (S, rows, heads) fp32 base-2
+    LSEs, both contiguous; sinks optional (heads,) fp32 logits added to the
+    denominator only.  Returns v_out (rows, heads, D), or (v_out, s_out) when
+    return_lse.  Enqueued on torch's current stream of v's device.
+    """
+    dev = v.device
+    for name, t in (("v", v), ("s", s), ("sinks", sinks), ("v_out", v_out), ("s_out", s_out)):
+        if t is not None and (t.device.type != "cuda" or t.device != dev):
+            raise ValueError(f"{name} must be a GPU tensor on v's device ({dev})")
+    if v_out is None:
+        v_out = torch.empty(v.shape[1:], dtype=v.dtype, device=dev)
+    if return_lse and s_out is None:
+        s_out = torch.empty(v.shape[1:3], dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    with torch.cuda.device(dev):
+        st = _lib.pkvd_merge_states(_ref(_desc(v)), _ref(_desc(s)), _ref(_desc(sinks)),
+                                    _ref(_desc(v_out)), _ref(_desc(s_out)),
+                                    ctypes.c_void_p(stream))
+    _check(st)
+    return (v_out, s_out) if s_out is not None else v_out
 
 
 def plan(q, k_cache, block_tables, q_len_per_req: int = 1, window_left: int = -1) -> dict:

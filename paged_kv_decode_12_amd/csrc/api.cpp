@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include "decode_args.h"
+#include "merge_states.h"
 
 namespace {
 
@@ -501,6 +502,52 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PKVD_OK;
+}
+
+int pkvd_merge_states(const pkvd_tensor* v, const pkvd_tensor* s, const pkvd_tensor* sinks,
+                      pkvd_tensor* v_out, pkvd_tensor* s_out, void* stream) {
+  g_last_error.clear();
+  if (!v || !s || !v_out) return fail(PKVD_ERR_INVALID_ARG, "v, s and v_out are required");
+  if (v->ndim != 4) return fail(PKVD_ERR_INVALID_ARG, "v must be 4-D (S, rows, heads, D)");
+  if (v->dtype != PKVD_BF16 && v->dtype != PKVD_F16 && v->dtype != PKVD_F32)
+    return fail(PKVD_ERR_INVALID_ARG, "v must be bf16, fp16 or fp32");
+  const int64_t S = v->shape[0], R = v->shape[1], H = v->shape[2], D = v->shape[3];
+  if (S < 1 || R < 0 || H < 1 || D < 1)
+    return fail(PKVD_ERR_INVALID_ARG, "need S >= 1, heads >= 1, D >= 1");
+  if (H > INT32_MAX || D > INT32_MAX || S > (1LL << 40) || R * H > (1LL << 40))
+    return fail(PKVD_ERR_UNSUPPORTED, "merge dimensions exceed the built index ranges");
+  if (!contiguous(v)) return fail(PKVD_ERR_INVALID_ARG, "v must be contiguous");
+  if (s->ndim != 3 || s->dtype != PKVD_F32 || s->shape[0] != S || s->shape[1] != R ||
+      s->shape[2] != H || !contiguous(s))
+    return fail(PKVD_ERR_INVALID_ARG, "s must be contiguous float32 (S, rows, heads)");
+  if (v_out->ndim != 3 || v_out->dtype != v->dtype || v_out->shape[0] != R ||
+      v_out->shape[1] != H || v_out->shape[2] != D || !contiguous(v_out))
+    return fail(PKVD_ERR_INVALID_ARG, "v_out must be contiguous (rows, heads, D) with v's dtype");
+  if (s_out && (s_out->ndim != 2 || s_out->dtype != PKVD_F32 || s_out->shape[0] != R ||
+                s_out->shape[1] != H || !contiguous(s_out)))
+    return fail(PKVD_ERR_INVALID_ARG, "s_out must be contiguous float32 (rows, heads)");
+  if (sinks && (sinks->ndim != 1 || sinks->dtype != PKVD_F32 || sinks->shape[0] != H ||
+                !contiguous(sinks)))
+    return fail(PKVD_ERR_INVALID_ARG, "sinks must be a contiguous float32 (heads,) tensor");
+  const bool empty = R == 0;
+  if (!empty && (!v->data || !s->data || !v_out->data || (s_out && !s_out->data) ||
+                 (sinks && !sinks->data)))
+    return fail(PKVD_ERR_INVALID_ARG, "NULL data pointer");
+  if (empty) return PKVD_OK;
+  pkvd::MergeArgs a{};
+  a.v = v->data;
+  a.s = static_cast<const float*>(s->data);
+  a.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
+  a.v_out = v_out->data;
+  a.s_out = s_out ? static_cast<float*>(s_out->data) : nullptr;
+  a.S = S;
+  a.items = R * H;
+  a.H = (int32_t)H;
+  a.D = (int32_t)D;
+  const int dt = v->dtype == PKVD_BF16 ? 0 : (v->dtype == PKVD_F16 ? 1 : 2);
+  hipError_t e = pkvd::launch_merge_states(a, dt, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKVD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   return PKVD_OK;
 }
 

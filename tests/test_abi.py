@@ -150,3 +150,36 @@ def test_sinks_beyond_lds_staging_unsupported():
     st = FakeDev(inp).call(q=q, out=torch.zeros_like(q), lse=None, sinks=torch.zeros(Hq))
     assert st == 2, pk._lib.pkvd_last_error()
     assert b"sinks" in pk._lib.pkvd_last_error()
+
+
+MERGE_BAD = [
+    ("v_rank", dict(v=(2, 3, 4))),
+    ("v_dtype", dict(v_dtype=torch.float64)),
+    ("s_shape", dict(s=(2, 3, 5))),
+    ("s_dtype", dict(s_dtype=torch.float16)),
+    ("out_shape", dict(v_out=(3, 4, 8))),
+    ("out_dtype", dict(out_dtype=torch.float32)),
+    ("s_out_shape", dict(s_out=(3, 5))),
+    ("sinks_len", dict(sinks=(5,))),
+    ("zero_states", dict(v=(0, 3, 4, 16), s=(0, 3, 4))),
+]
+
+
+@pytest.mark.parametrize("name,kw", MERGE_BAD, ids=[b[0] for b in MERGE_BAD])
+def test_merge_states_invalid_arguments(name, kw):
+    """pkvd_merge_states rejects bad descriptors before any HIP call."""
+    def t(shape, dtype):
+        return torch.zeros(shape, dtype=dtype)
+    v = t(kw.get("v", (2, 3, 4, 16)), kw.get("v_dtype", torch.bfloat16))
+    s = t(kw.get("s", (2, 3, 4)), kw.get("s_dtype", torch.float32))
+    vo = t(kw.get("v_out", (3, 4, 16)), kw.get("out_dtype", torch.bfloat16))
+    so = t(kw.get("s_out", (3, 4)), torch.float32)
+    sk = t(kw["sinks"], torch.float32) if "sinks" in kw else None
+    descs = [pk._desc(x) for x in (v, s, sk, vo, so)]
+    for i, d in enumerate(descs):
+        if d is not None:
+            d.data = 0x100000 * (i + 1)   # never dereferenced
+    r = lambda x: None if x is None else ctypes.byref(x)
+    st = pk._lib.pkvd_merge_states(*[r(d) for d in descs], None)
+    assert st == 1, (name, st, pk._lib.pkvd_last_error())
+    assert pk._lib.pkvd_last_error()

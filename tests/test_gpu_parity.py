@@ -374,3 +374,76 @@ def test_bound_decode():
     e2 = pk.decode(*args, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out2, e2)
+
+
+# ----------------------------------------------------------------------------
+# cascade merge (pkvd_merge_states)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("S,D,sinks", [(1, 64, False), (2, 128, True), (5, 100, False),
+                                       (70, 128, True)])
+def test_merge_states_parity(dtype, S, D, sinks):
+    """pkvd_merge_states against the oracle's merge of the same states (the
+    states' rounded values), with empty states (lse = -inf, v = NaN)."""
+    pk = _pk()
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+    g = torch.Generator().manual_seed(100 + S + D)
+    R, H = 3, 4
+    v = torch.randn(S, R, H, D, generator=g).to(tdt)
+    s = (torch.randn(S, R, H, generator=g) * 3 + 5).float()
+    if S > 1:
+        s[0, 1, :] = -float("inf")           # an empty state in some rows
+        v[0, 1, :, :] = float("nan")         # ... whose values are never read
+    s[:, 2, 1] = -float("inf")               # a row with no state at all
+    sk = (torch.randn(H, generator=g) * 2).float() if sinks else None
+    log(f"[merge] dtype={dtype} S={S} D={D} sinks={sinks}")
+    out, lse = pk.merge_states(v.cuda(), s.cuda(), sinks=None if sk is None else sk.cuda())
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    # an empty state weighs 0: its (NaN) values take no part in the definition
+    vv = np.nan_to_num(v.double().numpy(), nan=0.0)
+    ss = s.double().numpy()
+    tol = 1e-5 if dtype == "fp32" else OUT_ATOL
+    for r in range(R):
+        for h in range(H):
+            ref_o, ref_l = oracle.merge_states(vv[:, r, h, :], ss[:, r, h],
+                                               None if sk is None else float(sk[h]))
+            if ref_l == -np.inf:
+                assert lse[r, h] == -np.inf and np.all(out[r, h] == 0), (r, h)
+                continue
+            assert np.isfinite(out[r, h]).all(), (r, h)
+            assert np.abs(out[r, h] - ref_o).max() <= tol, (r, h, np.abs(out[r, h] - ref_o).max())
+            assert abs(lse[r, h] - ref_l) <= LSE_ATOL, (r, h, lse[r, h], ref_l)
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_cascade_merge_equals_full_decode(sinks):
+    """Decoding a request's keys as two requests (the first k pages, the
+    rest) and merging the two states with pkvd_merge_states (the sink only in
+    the merge) equals decoding all keys at once."""
+    pk = _pk()
+    inp = workloads.make_case(B=1, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(1000,),
+                              sinks=sinks, seed=21)
+    ref_out, ref_lse, _ = oracle.decode(inp)
+    d = to_dev(inp)
+    n, k = 1000, 20                            # split after 20 pages = 320 keys
+    bt = d["block_tables"]
+    ncol = -(-n // 16)
+    two_bt = torch.zeros(2, ncol, dtype=torch.int32, device="cuda")
+    two_bt[0, :k] = bt[0, :k]
+    two_bt[1, :ncol - k] = bt[0, k:ncol]
+    lens = torch.tensor([16 * k, n - 16 * k], dtype=torch.int32, device="cuda")
+    q2 = d["q"].repeat(2, 1, 1).contiguous()
+    part_out, part_lse = pk.decode(q2, d["k_cache"], d["v_cache"], two_bt, lens,
+                                   scale=d["scale"], return_lse=True)
+    v = part_out.view(2, 1, *part_out.shape[1:]).contiguous()
+    s = part_lse.view(2, 1, part_lse.shape[1]).contiguous()
+    out, lse = pk.merge_states(v, s, sinks=d.get("sinks"))
+    full_out, full_lse = pk.decode(d["q"], d["k_cache"], d["v_cache"], bt, d["seq_lens_kv"],
+                                   scale=d["scale"], sinks=d.get("sinks"), return_lse=True)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().reshape(-1, out.shape[-1])
+    compare("cascade", o, lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
+    assert (out.float() - full_out.float()).abs().max().item() <= OUT_ATOL
+    assert (lse - full_lse).abs().max().item() <= LSE_ATOL
