@@ -104,6 +104,52 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
           flush=True)
 
 
+def bench_merge_states(args):
+    """The cascade merge (pkvd_merge_states) on S = 16 bf16 states of the
+    llama3_8b batch's 64 x 32 (row, head) pairs, D = 128, with sinks: HBM
+    bytes per call = S (D elt + 4) read + (D elt + 4) written per pair."""
+    import numpy as np
+    import torch
+    import oracle
+    import paged_kv_decode_12_amd as pk
+
+    S, R, H, D = 16, 64, 32, 128
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = torch.Generator().manual_seed(2024)
+    v_cpu = torch.randn(S, R, H, D, generator=g).to(torch.bfloat16)
+    s_cpu = (torch.randn(S, R, H, generator=g) * 3 + 5).float()
+    sk_cpu = torch.randn(H, generator=g).float()
+    v, s, sk = v_cpu.to(dev), s_cpu.to(dev), sk_cpu.to(dev)
+    out = torch.empty(R, H, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(R, H, dtype=torch.float32, device=dev)
+    nbytes = R * H * (S * (D * 2 + 4) + D * 2 + 4)
+    step = lambda: pk.merge_states(v, s, sinks=sk, v_out=out, s_out=lse)
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    # spot check of a few (row, head) pairs against the oracle's merge
+    o = out.float().cpu().numpy()
+    err = 0.0
+    for r, h in ((0, 0), (17, 5), (63, 31)):
+        ref, _ = oracle.merge_states(v_cpu[:, r, h].double().numpy(),
+                                     s_cpu[:, r, h].double().numpy(), float(sk_cpu[h]))
+        err = max(err, float(np.abs(o[r, h] - ref).max()))
+    print(json.dumps({"op": "merge_states", "us_per_call": round(us, 3),
+                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 2), "bytes_per_call": nbytes,
+                      "config": {"S": S, "rows": R, "heads": H, "D": D, "dtype": "bf16",
+                                 "sinks": True},
+                      "steps": args.steps, "max_abs_err_sampled": err}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +160,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU-baseline leg (0 disables it)")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--op", choices=("decode", "merge_states"), default="decode",
+                    help="merge_states: time the cascade merge on 16 states of the "
+                         "llama3_8b batch's rows instead of the decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -125,6 +174,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "merge_states":
+        bench_merge_states(args)
         return
 
     import numpy as np

@@ -13,9 +13,9 @@
 // s = -inf.
 //
 // One wave per (row, head): the lanes reduce the S LSEs (64 at a time) to
-// their maximum, then each lane accumulates its dims over the states in
-// order, four states' loads in flight.  HBM-bound: S (D elt + 4) bytes read
-// and D elt + 4 written per (row, head).
+// their maximum, then each lane accumulates up to four of its dims over the
+// states in order, eight states' loads in flight.  HBM-bound: S (D elt + 4)
+// bytes read and D elt + 4 written per (row, head).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,6 +70,8 @@ struct Elem<2> {   // fp32
 
 template <int DT>
 __global__ __launch_bounds__(64 * kMsWaves) void merge_states_kernel(const MergeArgs a) {
+  constexpr int kDl = 4;       // dims per lane per pass (256 dims per pass)
+  constexpr int kDepth = 8;    // states whose loads are in flight together
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * kMsWaves + (threadIdx.x >> 6);   // row * H + head
   if (item >= a.items) return;
@@ -87,34 +89,39 @@ __global__ __launch_bounds__(64 * kMsWaves) void merge_states_kernel(const Merge
     return;
   }
   const float top = fmaxf(M, sink2);
-  for (int d0 = 0; d0 < a.D; d0 += 64) {
-    const int d = d0 + lane;
-    const bool on = d < a.D;
-    float acc = 0.f, W = 0.f;
-    int64_t s0 = 0;
-    for (; s0 + 4 <= S; s0 += 4) {   // four states' loads in flight
-      float l[4], x[4];
+  for (int d0 = 0; d0 < a.D; d0 += 64 * kDl) {
+    // lane holds dims d0 + lane + 64 e (coalesced across the wave)
+    float acc[kDl], W = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        l[u] = a.s[(s0 + u) * a.items + item];
-        x[u] = on ? Elem<DT>::load(a.v, ((s0 + u) * a.items + item) * a.D + d) : 0.f;
+    for (int e = 0; e < kDl; ++e) acc[e] = 0.f;
+    for (int64_t s0 = 0; s0 < S; s0 += kDepth) {
+      float l[kDepth], x[kDepth][kDl];
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const bool live = s0 + u < S;
+        const int64_t st = live ? s0 + u : s0;   // padding entries re-read a live state
+        l[u] = live ? a.s[st * a.items + item] : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kDl; ++e) {
+          const int d = d0 + lane + 64 * e;
+          x[u][e] = d < a.D ? Elem<DT>::load(a.v, (st * a.items + item) * a.D + d) : 0.f;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kDepth; ++u) {
         const float w = l[u] == -INFINITY ? 0.f : exp2f(l[u] - top);
         W += w;
-        acc = w == 0.f ? acc : fmaf(w, x[u], acc);   // select: an empty state's v is never used
+#pragma unroll
+        for (int e = 0; e < kDl; ++e)   // select: an empty state's v is never used
+          acc[e] = w == 0.f ? acc[e] : fmaf(w, x[u][e], acc[e]);
       }
     }
-    for (; s0 < S; ++s0) {
-      const float l = a.s[s0 * a.items + item];
-      const float x = on ? Elem<DT>::load(a.v, (s0 * a.items + item) * a.D + d) : 0.f;
-      const float w = l == -INFINITY ? 0.f : exp2f(l - top);
-      W += w;
-      acc = w == 0.f ? acc : fmaf(w, x, acc);
-    }
     const float Z = W + (has_sink ? exp2f(sink2 - top) : 0.f);
-    if (on) Elem<DT>::store(a.v_out, item * a.D + d, acc / Z);
+#pragma unroll
+    for (int e = 0; e < kDl; ++e) {
+      const int d = d0 + lane + 64 * e;
+      if (d < a.D) Elem<DT>::store(a.v_out, item * a.D + d, acc[e] / Z);
+    }
     if (d0 == 0 && lane == 0 && a.s_out) a.s_out[item] = top + log2f(W);
   }
 }
