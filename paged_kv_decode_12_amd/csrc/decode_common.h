@@ -439,18 +439,29 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
   }
   if (a.sinks)
     for (int h = t; h < a.Hq; h += NT) s_sink[h] = a.sinks[h];
-  s_scan[t] = sum;
-  s_vscan[t] = vsum;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {      // inclusive Hillis-Steele scans
-    const int v = t >= off ? s_scan[t - off] : 0;
-    const int vv = t >= off ? s_vscan[t - off] : 0;
-    __syncthreads();
-    s_scan[t] += v;
-    s_vscan[t] += vv;
-    __syncthreads();
+  // inclusive scans: within each wave by lane shuffles, then across the
+  // NT / 64 wave totals (two barriers in all)
+  const int lane = t & 63, wv = t >> 6;
+  int x = sum, vx = vsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o), vy = __shfl_up(vx, o);
+    if (lane >= o) {
+      x += y;
+      vx += vy;
+    }
   }
-  int excl = s_scan[t] - sum, vexcl = s_vscan[t] - vsum;
+  if (lane == 63) {
+    s_scan[wv] = x;
+    s_vscan[wv] = vx;
+  }
+  __syncthreads();
+  int base = 0, vbase = 0;
+  for (int w = 0; w < wv; ++w) {
+    base += s_scan[w];
+    vbase += s_vscan[w];
+  }
+  int excl = base + x - sum, vexcl = vbase + vx - vsum;
   for (int b = lo; b < hi; ++b) {
     s_pref[b] = excl;
     s_vpref[b] = vexcl;
@@ -459,8 +470,8 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
     vexcl += (nb > 0 ? nb + c : 0) * per_req;
   }
   if (t == NT - 1) {
-    s_pref[B] = s_scan[t];
-    s_vpref[B] = s_vscan[t];
+    s_pref[B] = base + x;
+    s_vpref[B] = vbase + vx;
   }
   __syncthreads();
   Prefix p;
