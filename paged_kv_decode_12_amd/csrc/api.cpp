@@ -166,10 +166,11 @@ DeviceFit device_fit(int path, int rt, const Shapes& s) {
 }
 
 // Virtual blocks ahead of each unit in the sliced block space (see make_plan),
-// per engine, measured on MI355X (llama3_8b-shaped batch, VALU engine:
-// 0 -> 114.3 us, 2 -> 109.9, 3 -> 108.3, 4 -> 106.7, 6 -> 107.1; MFMA engine,
+// per engine, measured on MI355X (llama3_8b-shaped batch, VALU engine with a
+// 6-deep ring: 0 -> 114.3 us, 2 -> 109.9, 3 -> 108.3, 4 -> 106.7, 6 -> 107.1;
+// with the 3-deep ring: 5 -> 103.1, 6 -> 103.4, 7 -> 104.5.  MFMA engine,
 // spec_verify: 0 -> 118.5 us, 6 -> 116.6).
-int default_seg_cost(int path) { return path == pkvd::kPathMfma ? 6 : 4; }
+int default_seg_cost(int path) { return path == pkvd::kPathMfma ? 6 : 5; }
 
 // Default slice weight of the waves at position `slot` on their SIMD.  Equal
 // weights measured fastest for the default engines on MI355X (the MFMA

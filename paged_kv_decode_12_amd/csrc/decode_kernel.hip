@@ -561,7 +561,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 // blocks in flight ahead of the scoring, and waves per SIMD the register
 // budget is fitted to, per engine
 #ifndef PKVD_PF4
-#define PKVD_PF4 6
+#define PKVD_PF4 3
 #endif
 #ifndef PKVD_WPE4
 #define PKVD_WPE4 1
