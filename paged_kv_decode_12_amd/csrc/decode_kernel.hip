@@ -573,7 +573,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #define PKVD_WPE8 2
 #endif
 #ifndef PKVD_PF16
-#define PKVD_PF16 3
+#define PKVD_PF16 2
 #endif
 #ifndef PKVD_WPE16
 #define PKVD_WPE16 1
