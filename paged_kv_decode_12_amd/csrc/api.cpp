@@ -220,7 +220,10 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   int64_t nw = (int64_t)f.cus * f.blocks_per_cu * f.group_waves;
   const int forced = env_int("PKVD_WAVES", 0);
   if (forced > 0) nw = forced;
-  p.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 8));
+  // at least 2 blocks per participating wave: short batches then spread
+  // over many waves (tiny 4-request batch: 24.2 us at 8 blocks, 16.2 us at
+  // 2), while long ones use every resident wave anyway
+  p.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 2));
   // no more waves than the largest possible work can occupy
   nw = std::min<int64_t>(nw, (p.units * max_blocks + p.min_wave_blocks - 1) / p.min_wave_blocks);
   nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
