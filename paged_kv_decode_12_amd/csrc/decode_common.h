@@ -183,13 +183,13 @@ __device__ __forceinline__ float rescale(float m, float M) {
 }
 
 // ---------------------------------------------------------------------------
-// key range of one request and its split
+// key range of one request
 // ---------------------------------------------------------------------------
 // Keys some row of request b may see: [lo(row 0), n - 1], where row 0 has the
 // lowest diagonal n - Lq (Parameters / q_len_per_req) and the window keeps
 // window_left keys before the diagonal (Parameters / window_left).  The range
-// is cut into 16-key blocks aligned to the absolute key index; splits take
-// consecutive runs of split_blocks blocks.
+// is cut into 16-key blocks aligned to the absolute key index; the waves'
+// slices are runs of these blocks.
 struct UnitRange {
   int n;          // sequence length, clamped to the block table's capacity
   int key_lo;     // first key some row sees
