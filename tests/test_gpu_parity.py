@@ -447,3 +447,21 @@ def test_cascade_merge_equals_full_decode(sinks):
     compare("cascade", o, lse.cpu().numpy().reshape(-1), ref_out, ref_lse)
     assert (out.float() - full_out.float()).abs().max().item() <= OUT_ATOL
     assert (lse - full_lse).abs().max().item() <= LSE_ATOL
+
+
+@pytest.mark.parametrize("B,sched", [(3000, "auto"), (8192, "auto"), (3000, "mk_segcost"),
+                                     (8192, "cut64")])
+def test_large_batches_with_empty_requests(B, sched):
+    """Thousands of short requests, some empty (n = 0: no visible key, out = 0,
+    lse = -inf): the request search takes two or three 64-way levels and the
+    empty requests hold no (virtual) blocks; 8192 is the largest batch built."""
+    g = torch.Generator().manual_seed(B)
+    lens = torch.randint(0, 41, (B,), generator=g)
+    lens[::97] = 0
+    inp = workloads.make_case(B=B, Hq=4, Hkv=2, D=64, page_size=16, seq_lens=tuple(lens.tolist()),
+                              seed=B + 1)
+    ref_out, ref_lse, _ = oracle.decode(inp)
+    log(f"[large] B={B} schedule={sched} empty={(lens == 0).sum().item()}")
+    with schedule(sched):
+        out, lse = run_gpu(to_dev(inp))
+    compare(f"large_B{B}_{sched}", out, lse, ref_out, ref_lse)
