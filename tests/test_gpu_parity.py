@@ -269,6 +269,12 @@ EDGE.append(dict(dtype="fp16", value_std=0.5, seq_lens=(7, 500), Hq=8, Hkv=1, D=
 EDGE.append(dict(q_pad_heads=8, bt_pad=3, seq_lens=(9, 70, 129), Hq=8, Hkv=2, D=128))
 EDGE.append(dict(value_std=3.0, seq_lens=(64, 1000), Hq=4, Hkv=1, D=128))   # wide score range
 EDGE.append(dict(C=40, seq_lens=(640, 17), Hq=4, Hkv=4, D=64, page_size=16))
+# the largest pages built (256) and a large non-power-of-two page size
+EDGE.append(dict(D=128, page_size=256, seq_lens=(1, 255, 256, 257, 1300), Hq=8, Hkv=2))
+EDGE.append(dict(D=64, page_size=128, seq_lens=(3, 128, 129, 700), Hq=16, Hkv=2,
+                 q_len_per_req=2, window_left=150))
+EDGE.append(dict(D=128, page_size=200, seq_lens=(199, 200, 201, 999), Hq=4, Hkv=1,
+                 sinks=True))
 
 
 def _edge_id(c):
