@@ -13,7 +13,8 @@ Parity status of each function:
   decode          pinned (tests/test_oracle.py: brute force, closed forms,
                   logsumexp, sink, window, causal prefix, GQA, page permutation,
                   page-size repack, merge of disjoint ranges, hand-worked
-                  golden cases)
+                  golden cases; packed rows, dense rows and the output scale
+                  against the brute force and hand-worked cases)
   merge_states    pinned (merge of disjoint key ranges equals the union)
   decode, lse with sinks present: the keys-only reading of the LSE is a
                   reading, not fixed by the pages -> parity unpinned for that
@@ -61,6 +62,7 @@ def _load():
             ctypes.c_int, i64, i64, i64, i64, i64, i64,
             p, i64, i64,                 # block tables
             p, ctypes.c_double, i64, i64,
+            p, ctypes.c_int, ctypes.c_double,   # qo_indptr, causal, out_scale
             p, i64, i64,                 # sinks, key range
             p, i64,                      # sel
             p, p, p, ctypes.c_int]
@@ -96,12 +98,19 @@ def decode(inputs: dict, sel=None, key_range=None, nthreads: int = 0,
            sinks="inputs"):
     """Reference attention for an inputs dict (see ``workloads``).
 
+    Optional keys: ``qo_indptr`` ((B + 1,) int32 cumulative row offsets of
+    packed query rows), ``mask_type`` ("causal", the default, or "dense") and
+    ``out_scale`` (factor on the output, default 1).  q may be (rows, Hq, D)
+    or token-major (B, SQ, Hq, D).
+
     Returns (out [count, D], lse [count], lse_with_sink [count]) as float64
-    numpy arrays; ``count`` is B*Lq*Hq in row-major (row, head) order, or
+    numpy arrays; ``count`` is rows*Hq in row-major (row, head) order, or
     len(sel) for an explicit list of flat indices row*Hq + head.
     """
     lib = _load()
     q, k, v = inputs["q"], inputs["k_cache"], inputs["v_cache"]
+    if q.dim() == 4:
+        q = q.reshape(q.shape[0] * q.shape[1], q.shape[2], q.shape[3])
     qb, code = _bits(q)
     kb, kcode = _bits(k)
     vb, vcode = _bits(v)
@@ -117,7 +126,15 @@ def decode(inputs: dict, sel=None, key_range=None, nthreads: int = 0,
     R, Hq, D = q.shape
     B = bt.shape[0]
     Lq = int(inputs["q_len_per_req"])
-    assert R == B * Lq
+    qo = inputs.get("qo_indptr")
+    qo_arr = None if qo is None else np.ascontiguousarray(_i32(qo))
+    if qo_arr is None:
+        assert R == B * Lq
+    else:
+        assert qo_arr.shape == (B + 1,) and int(qo_arr[-1]) == R
+        Lq = max(1, Lq)
+    causal = {"causal": 1, "dense": 0}[inputs.get("mask_type", "causal")]
+    out_scale = float(inputs.get("out_scale", 1.0))
     P, Hkv, ps, Dk = k.shape
     assert Dk == D and tuple(v.shape) == tuple(k.shape)
     if sel is None:
@@ -137,6 +154,7 @@ def decode(inputs: dict, sel=None, key_range=None, nthreads: int = 0,
         code, B, Hq, Hkv, D, ps, P,
         ptr(bt), bt.strides[0] // 4, bt.shape[1],
         ptr(n), float(inputs["scale"]), Lq, int(inputs["window_left"]),
+        ptr(qo_arr), causal, out_scale,
         ptr(s_arr), int(klo), int(khi),
         ptr(sel_arr), count,
         ptr(out), ptr(lse), ptr(lse_ws), int(nthreads))

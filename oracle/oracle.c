@@ -26,6 +26,19 @@
  *       row's visible keys (the row's own masked score row); the key-value head
  *       of query head h is h / (Hq / Hkv).  The exported lse excludes the sink;
  *       lse_with_sink also counts it (diagnostic).
+ *   flashinfer.attention.prims_ts.batch_decode_with_paged_kv_cache
+ *     - summary and Parameters / qo_indptr, max_seq_len_q: with cumulative
+ *       query offsets qo_indptr (B + 1 entries) the query rows are packed:
+ *       request b owns rows qo_indptr[b] .. qo_indptr[b + 1] - 1, so its
+ *       query length Lq_b varies per request and row r is its
+ *       i = r - qo_indptr[b]-th token.  Without them every request has the
+ *       fixed length Lq (a [B, SQ, Hq, D] token-major tensor is the same
+ *       memory as the (B * SQ, Hq, D) rows above).
+ *     - Parameters / mask_type: "causal" is the bottom-right diagonal above;
+ *       "dense" lets every row see every key j < n (a window, if any, still
+ *       starts window_left keys before the row's diagonal position p_i).
+ *     - Parameters / bmm2_scale (and batch_prefill's output_scale): the
+ *       output is multiplied by this factor; the LSE is not.
  *
  * The softmax is the plain two-pass form: first every visible score and their
  * maximum, then the exponentials, their sum and the weighted sum of V.
@@ -88,22 +101,41 @@ typedef struct {
   const int32_t* bt;  int64_t bt_sr, C;              /* bt[b*bt_sr + c] */
   const int32_t* seq_lens;
   double scale;
-  int64_t Lq, wl;
+  int64_t Lq, wl;                                    /* Lq: fixed query length */
+  const int32_t* qo_indptr;                          /* NULL, or packed rows: (B + 1,) */
+  int causal;                                        /* 1: bottom-right causal, 0: dense */
+  double out_scale;                                  /* factor on the output */
   const float* sinks;                                /* may be NULL */
   int64_t key_lo, key_hi;                            /* extra key restriction [lo, hi) */
 } problem_t;
+
+/* Request b, its query length and the token index i of query row r. */
+static void row_owner(const problem_t* pb, int64_t r, int64_t* b, int64_t* lq, int64_t* i) {
+  if (!pb->qo_indptr) {
+    *b = r / pb->Lq;
+    *lq = pb->Lq;
+    *i = r % pb->Lq;
+    return;
+  }
+  int64_t bb = 0;   /* the request whose row range [qo[b], qo[b + 1]) holds r */
+  while (bb + 1 < pb->B && pb->qo_indptr[bb + 1] <= r) ++bb;
+  *b = bb;
+  *lq = pb->qo_indptr[bb + 1] - pb->qo_indptr[bb];
+  *i = r - pb->qo_indptr[bb];
+}
 
 /* One (row r, head h).  Returns ORACLE_OK or ORACLE_BAD_PAGE. */
 static int one_row(const problem_t* pb, int64_t r, int64_t h, double* s_buf,
                    double* out, double* lse, double* lse_ws) {
   const int64_t D = pb->D;
-  const int64_t b = r / pb->Lq, i = r % pb->Lq;
+  int64_t b, lq, i;
+  row_owner(pb, r, &b, &lq, &i);
   const int64_t g = pb->Hq / pb->Hkv, kvh = h / g;
   const int64_t n = pb->seq_lens[b];
 
   /* visible keys: lo <= j <= hi, 0 <= j < n */
-  const int64_t diag = n - pb->Lq + i;
-  int64_t hi = diag;
+  const int64_t diag = n - lq + i;
+  int64_t hi = pb->causal ? diag : n - 1;
   int64_t lo = (pb->wl < 0) ? 0 : diag - pb->wl;
   if (lo < 0) lo = 0;
   if (hi > n - 1) hi = n - 1;
@@ -153,7 +185,7 @@ static int one_row(const problem_t* pb, int64_t r, int64_t h, double* s_buf,
     for (int64_t d = 0; d < D; ++d) out[d] += w * decode(vrow[d], pb->dtype);
   }
   const double Z = S + (has_sink ? exp(sink - m_all) : 0.0);
-  for (int64_t d = 0; d < D; ++d) out[d] /= Z;
+  for (int64_t d = 0; d < D; ++d) out[d] = pb->out_scale * (out[d] / Z);
   *lse = (m_all + log(S)) / log(2.0);
   *lse_ws = (m_all + log(Z)) / log(2.0);
   return ORACLE_OK;
@@ -166,6 +198,10 @@ static int one_row(const problem_t* pb, int64_t r, int64_t h, double* s_buf,
  *   out   : [count, D] doubles;  lse, lse_with_sink : [count] doubles.
  *   key_lo, key_hi : additionally restrict keys to [key_lo, key_hi)
  *           (pass 0 and INT64_MAX for none); used to build partial states.
+ *   qo_indptr : NULL (every request has Lq rows) or (B + 1,) cumulative row
+ *           offsets of packed rows (Lq is then unused).
+ *   causal : 1 bottom-right causal rows, 0 dense rows.
+ *   out_scale : factor on the output (1 for none).
  *   nthreads : OpenMP threads (<= 0: library default).
  */
 int oracle_decode(const uint16_t* q, int64_t q_sr, int64_t q_sh,
@@ -175,6 +211,7 @@ int oracle_decode(const uint16_t* q, int64_t q_sr, int64_t q_sh,
                   int64_t ps, int64_t P,
                   const int32_t* block_tables, int64_t bt_sr, int64_t C,
                   const int32_t* seq_lens, double scale, int64_t Lq, int64_t window_left,
+                  const int32_t* qo_indptr, int causal, double out_scale,
                   const float* sinks, int64_t key_lo, int64_t key_hi,
                   const int64_t* sel, int64_t nsel,
                   double* out, double* lse, double* lse_with_sink, int nthreads) {
@@ -184,14 +221,22 @@ int oracle_decode(const uint16_t* q, int64_t q_sr, int64_t q_sh,
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || ps < 1 || P < 1 || C < 1 || Lq < 1)
     return ORACLE_BAD_ARG;
   if (Hq % Hkv != 0 || window_left < -1) return ORACLE_BAD_ARG;
+  int64_t rows = B * Lq;
+  if (qo_indptr) {
+    if (qo_indptr[0] != 0) return ORACLE_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b)
+      if (qo_indptr[b + 1] < qo_indptr[b]) return ORACLE_BAD_ARG;
+    rows = qo_indptr[B];
+  }
 
   problem_t pb = {q, q_sr, q_sh, k, k_sp, k_sh, k_ss, v, v_sp, v_sh, v_ss, dtype,
                   B, Hq, Hkv, D, ps, P, block_tables, bt_sr, C, seq_lens, scale,
-                  Lq, window_left, sinks, key_lo, key_hi};
+                  Lq, window_left, qo_indptr, causal ? 1 : 0, out_scale,
+                  sinks, key_lo, key_hi};
   int64_t nmax = 0;
   for (int64_t b = 0; b < B; ++b)
     if (seq_lens[b] > nmax) nmax = seq_lens[b];
-  const int64_t count = sel ? nsel : B * Lq * Hq;
+  const int64_t count = sel ? nsel : rows * Hq;
   int status = ORACLE_OK;
 
 #ifdef _OPENMP
@@ -212,6 +257,11 @@ int oracle_decode(const uint16_t* q, int64_t q_sr, int64_t q_sh,
       if (!buf) continue;
       int64_t idx = sel ? sel[t] : t;
       int64_t r = idx / Hq, h = idx % Hq;
+      if (r < 0 || r >= rows) {
+#pragma omp atomic write
+        status = ORACLE_BAD_ARG;
+        continue;
+      }
       int st = one_row(&pb, r, h, buf, out + t * D, lse + t, lse_with_sink + t);
       if (st != ORACLE_OK) {
 #pragma omp atomic write

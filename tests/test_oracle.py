@@ -6,7 +6,9 @@ documentation's statements, closed forms, textbook identities, library routines
 brute force on tiny inputs.  The passages are those of
 flashinfer.cudnn.cudnn_batch_decode_with_kv_cache (Parameters, Note) and
 flashinfer.attention.prims_ts.batch_prefill (summary: causal is bottom-right
-aligned, a window keeps at most window_left + 1 keys per causal row).
+aligned, a window keeps at most window_left + 1 keys per causal row) and
+flashinfer.attention.prims_ts.batch_decode_with_paged_kv_cache (summary:
+packed query rows through qo_indptr; Parameters: mask_type, bmm2_scale).
 """
 import json
 import math
@@ -30,21 +32,33 @@ LOG2E = 1.0 / math.log(2.0)
 def dense_reference(inp, with_sinks=True):
     """Gather each request's K/V densely with torch indexing, then fp64
     torch.softmax over an explicit boolean mask (plus an appended sink logit
-    column whose value row is zero) and torch.logsumexp * log2(e)."""
+    column whose value row is zero) and torch.logsumexp * log2(e).  Packed
+    rows (``qo_indptr``), dense rows (``mask_type``) and the output factor
+    (``out_scale``) are honoured when the inputs carry them."""
     q = inp["q"].double()
+    if q.dim() == 4:
+        q = q.reshape(-1, q.shape[2], q.shape[3])
     k = inp["k_cache"].double()
     v = inp["v_cache"].double()
     bt = inp["block_tables"].long()
     n_all = inp["seq_lens_kv"].long()
     Lq, wl, scale = inp["q_len_per_req"], inp["window_left"], inp["scale"]
+    causal = inp.get("mask_type", "causal") == "causal"
+    out_scale = float(inp.get("out_scale", 1.0))
+    B = bt.shape[0]
+    if inp.get("qo_indptr") is not None:
+        qo = [int(x) for x in inp["qo_indptr"].tolist()]
+    else:
+        qo = [b * Lq for b in range(B + 1)]
     sinks = inp["sinks"] if with_sinks else None
     R, Hq, D = q.shape
     P, Hkv, ps, _ = k.shape
     g = Hq // Hkv
     outs = torch.zeros(R, Hq, D, dtype=torch.float64)
     lses = torch.full((R, Hq), -math.inf, dtype=torch.float64)
-    for b in range(bt.shape[0]):
+    for b in range(B):
         n = int(n_all[b])
+        lq = qo[b + 1] - qo[b]
         j = torch.arange(n)
         pages = bt[b, j // ps]
         slots = j % ps
@@ -52,10 +66,10 @@ def dense_reference(inp, with_sinks=True):
             kvh = h // g
             Kd = k[pages, kvh, slots]            # [n, D]
             Vd = v[pages, kvh, slots]
-            for i in range(Lq):
-                r = b * Lq + i
-                diag = n - Lq + i
-                mask = j <= diag
+            for i in range(lq):
+                r = qo[b] + i
+                diag = n - lq + i
+                mask = (j <= diag) if causal else torch.ones(n, dtype=torch.bool)
                 if wl >= 0:
                     mask &= j >= diag - wl
                 s = scale * (Kd @ q[r, h])
@@ -69,7 +83,7 @@ def dense_reference(inp, with_sinks=True):
                 else:
                     Vx = Vd
                 p = torch.softmax(s, 0)
-                outs[r, h] = p @ Vx
+                outs[r, h] = out_scale * (p @ Vx)
     return outs.reshape(R * Hq, D).numpy(), lses.reshape(-1).numpy()
 
 
@@ -428,5 +442,151 @@ def test_poison_never_read():
     bad = workloads.make_config("tiny", poison=True)
     o1, l1, _ = run(clean)
     o2, l2, _ = run(bad)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# packed query rows, dense rows, output scale
+# (batch_decode_with_paged_kv_cache: summary; Parameters qo_indptr,
+#  max_seq_len_q, mask_type, bmm2_scale)
+# ----------------------------------------------------------------------------
+def _packed_golden():
+    gold = json.load(open(os.path.join(GOLD, "hand_worked_packed.json")))
+    c = gold["common"]
+    dt = torch.bfloat16
+    base = dict(q=torch.tensor(c["q"], dtype=torch.float32).to(dt),
+                k_cache=torch.tensor(c["k_cache"], dtype=torch.float32).to(dt),
+                v_cache=torch.tensor(c["v_cache"], dtype=torch.float32).to(dt),
+                block_tables=torch.tensor(c["block_tables"], dtype=torch.int32),
+                seq_lens_kv=torch.tensor(c["seq_lens_kv"], dtype=torch.int32),
+                qo_indptr=torch.tensor(c["qo_indptr"], dtype=torch.int32),
+                sinks=None, scale=1.0, q_len_per_req=2)
+    return gold, base
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLD, "hand_worked_packed.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_hand_worked_packed(case):
+    _, base = _packed_golden()
+    inp = dict(base, mask_type=case["mask_type"], window_left=case["window_left"],
+               out_scale=case["out_scale"])
+    out, lse, _ = run(inp)
+    env = {"__builtins__": {}, "e": math.e, "log2": math.log2, "ln": math.log}
+    want_out = np.array([[eval(x, env) for x in row] for row in case["out"]], dtype=np.float64)
+    want_lse = np.array([eval(x, env) for x in case["lse"]], dtype=np.float64)
+    np.testing.assert_allclose(out, want_out, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-13)
+    ref_out, ref_lse = dense_reference(inp)
+    np.testing.assert_allclose(ref_out, want_out, rtol=0, atol=1e-14)
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(B=st.integers(1, 4), g=st.sampled_from([1, 2, 3]), Hkv=st.integers(1, 2),
+       D=st.sampled_from([1, 3, 8]), ps=st.sampled_from([1, 2, 5]),
+       wl=st.sampled_from([-1, 0, 1, 4]), mask=st.sampled_from(["causal", "dense"]),
+       sinks=st.booleans(), out_scale=st.sampled_from([1.0, 0.5, -2.0]),
+       seed=st.integers(0, 10_000), data=st.data())
+def test_brute_force_packed(B, g, Hkv, D, ps, wl, mask, sinks, out_scale, seed, data):
+    """Packed rows of varying length (zero included), both masks and an
+    output factor against the dense torch brute force."""
+    qls = data.draw(st.lists(st.integers(0, 4), min_size=B, max_size=B))
+    lens = [data.draw(st.integers(max(q, 1), 12)) for q in qls]
+    if sum(qls) == 0:
+        qls[0] = 1
+    inp = workloads.make_case(B=B, Hq=g * Hkv, Hkv=Hkv, D=D, page_size=ps, seq_lens=lens,
+                              q_lens=qls, window_left=wl, sinks=sinks, mask_type=mask,
+                              out_scale=out_scale, seed=seed, extra_pages=2, bt_pad=1,
+                              q_pad_heads=1)
+    out, lse, _ = run(inp)
+    ref_out, ref_lse = dense_reference(inp)
+    np.testing.assert_allclose(out, ref_out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_packed_equals_per_request_fixed_calls():
+    """A packed batch equals, row for row, fixed-length calls on each request
+    alone (its block-table row, its length, its rows of q)."""
+    qls = (3, 0, 1, 4)
+    lens = (9, 5, 14, 20)
+    for mask in ("causal", "dense"):
+        for wl in (-1, 2):
+            inp = _case(B=4, seq_lens=lens, q_lens=qls, mask_type=mask, window_left=wl,
+                        sinks=True, out_scale=1.5)
+            o, l, _ = run(inp)
+            qo = inp["qo_indptr"].tolist()
+            for b, lq in enumerate(qls):
+                if lq == 0:
+                    continue
+                one = dict(inp, q=inp["q"][qo[b]:qo[b + 1]], qo_indptr=None,
+                           q_len_per_req=lq, block_tables=inp["block_tables"][b:b + 1],
+                           seq_lens_kv=inp["seq_lens_kv"][b:b + 1])
+                ob, lb, _ = run(one)
+                np.testing.assert_array_equal(o[qo[b] * 4:qo[b + 1] * 4], ob)
+                np.testing.assert_array_equal(l[qo[b] * 4:qo[b + 1] * 4], lb)
+
+
+def test_fixed_lengths_through_qo_indptr_equal_fixed_rows():
+    """qo_indptr = [0, Lq, 2 Lq, ...] is the fixed layout."""
+    fixed = _case(B=3, seq_lens=(6, 9, 13), q_len_per_req=3, window_left=3, sinks=True)
+    packed = dict(fixed, qo_indptr=torch.arange(0, 10, 3, dtype=torch.int32))
+    o1, l1, _ = run(fixed)
+    o2, l2, _ = run(packed)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_dense_row_equals_full_one_token_decode():
+    """mask_type dense without a window: every row of a request sees all n
+    keys, so each row equals a one-token decode of that row over n keys."""
+    multi = _case(B=2, seq_lens=(9, 14), q_len_per_req=3, mask_type="dense", sinks=True)
+    om, lm, _ = run(multi)
+    for r in range(6):
+        b = r // 3
+        single = dict(multi, q=multi["q"][r:r + 1], q_len_per_req=1, mask_type="causal",
+                      block_tables=multi["block_tables"][b:b + 1],
+                      seq_lens_kv=multi["seq_lens_kv"][b:b + 1])
+        os_, ls, _ = run(single)
+        np.testing.assert_array_equal(om[r * 4:(r + 1) * 4], os_)
+        np.testing.assert_array_equal(lm[r * 4:(r + 1) * 4], ls)
+
+
+def test_one_token_rows_ignore_the_mask_type():
+    """With one token per request the diagonal is the last key: both masks agree."""
+    a = _case(seq_lens=(7, 13), window_left=4, sinks=True, mask_type="causal")
+    b = dict(a, mask_type="dense")
+    oa, la, _ = run(a)
+    ob, lb, _ = run(b)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_output_scale_is_a_factor_on_the_output_only():
+    """bmm2_scale: q = 0 gives out_scale x the mean of the visible V rows and
+    an LSE of log2(#visible), whatever the scale."""
+    for s in (0.25, -3.0):
+        inp = _case(seq_lens=(7, 13), q_len_per_req=2, window_left=3, out_scale=s)
+        inp["q"] = torch.zeros_like(inp["q"])
+        out, lse, _ = run(inp)
+        bt = inp["block_tables"].long()
+        v = inp["v_cache"].double()
+        for b, n in enumerate((7, 13)):
+            for i in range(2):
+                diag = n - 2 + i
+                cnt = min(4, diag + 1)
+                j = torch.arange(diag + 1 - cnt, diag + 1)
+                for h in range(4):
+                    vd = v[bt[b, j // 4], h // 2, j % 4]
+                    r = (b * 2 + i) * 4 + h
+                    np.testing.assert_allclose(out[r], s * vd.mean(0).numpy(), atol=1e-14, rtol=0)
+                    assert abs(lse[r] - math.log2(cnt)) < 1e-13
+
+
+def test_token_major_query_is_the_row_layout():
+    """Fixed seq_len_q > 1: a [B, SQ, Hq, D] query is read as B * SQ rows."""
+    inp = _case(B=2, seq_lens=(9, 14), q_len_per_req=3)
+    o1, l1, _ = run(inp)
+    tm = dict(inp, q=inp["q"].reshape(2, 3, 4, 8))
+    o2, l2, _ = run(tm)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)

@@ -170,13 +170,24 @@ def make_case(B: int = 2, Hq: int = 4, Hkv: int = 2, D: int = 64, page_size: int
               window_left: int = -1, sinks: bool = False, dtype: str = "bf16",
               value_std: float = 1.0, extra_pages: int = 3, C: Optional[int] = None,
               bt_pad: int = 0, seed: int = 0, q_pad_heads: int = 0,
-              sink_std: float = 1.0) -> dict:
+              sink_std: float = 1.0, q_lens: Optional[Sequence[int]] = None,
+              mask_type: str = "causal", out_scale: float = 1.0) -> dict:
     """A small explicit case for edge sweeps.
 
     ``extra_pages`` unused pages are added to the pool; ``bt_pad`` extra int32
     columns separate block-table rows (row stride C + bt_pad); ``q_pad_heads``
     makes q a head-slice of a wider tensor (arbitrary head/batch strides).
+    ``q_lens`` packs the query rows: request b gets q_lens[b] rows and the
+    case carries ``qo_indptr`` (cumulative offsets, B + 1 entries) with
+    ``q_len_per_req`` = max(q_lens) as the per-request capacity.
+    ``mask_type`` ("causal" or "dense") and ``out_scale`` are passed through.
     """
+    qo_indptr = None
+    if q_lens is not None:
+        assert len(q_lens) == B
+        qo_indptr = torch.zeros(B + 1, dtype=torch.int32)
+        qo_indptr[1:] = torch.cumsum(torch.tensor(list(q_lens), dtype=torch.int64), 0).to(torch.int32)
+        q_len_per_req = max(1, max(q_lens))
     gen = torch.Generator().manual_seed(seed)
     dt = _DTYPES[dtype]
     ps = page_size
@@ -194,7 +205,8 @@ def make_case(B: int = 2, Hq: int = 4, Hkv: int = 2, D: int = 64, page_size: int
         bt_full[b, :npg] = perm[off:off + npg]
         off += npg
     block_tables = bt_full[:, :C]
-    qw = torch.randn((B * q_len_per_req, Hq + q_pad_heads, D), generator=gen) * value_std
+    rows = B * q_len_per_req if qo_indptr is None else int(qo_indptr[-1])
+    qw = torch.randn((rows, Hq + q_pad_heads, D), generator=gen) * value_std
     q = qw.to(dt)[:, q_pad_heads:, :]
     k = (torch.randn((P, Hkv, ps, D), generator=gen) * value_std).to(dt)
     v = (torch.randn((P, Hkv, ps, D), generator=gen) * value_std).to(dt)
@@ -205,5 +217,6 @@ def make_case(B: int = 2, Hq: int = 4, Hkv: int = 2, D: int = 64, page_size: int
                  sinks=sinks, return_lse=True, seed=seed)
     return dict(workload=w, q=q, k_cache=k, v_cache=v, block_tables=block_tables,
                 seq_lens_kv=n, sinks=s, scale=1.0 / math.sqrt(D),
-                q_len_per_req=q_len_per_req, window_left=window_left, return_lse=True)
+                q_len_per_req=q_len_per_req, window_left=window_left, return_lse=True,
+                qo_indptr=qo_indptr, mask_type=mask_type, out_scale=out_scale)
 
