@@ -1,9 +1,10 @@
 // api.cpp -- C ABI of the paged-KV decode library: argument validation,
 // shape-only launch planning, the split-KV workspace and kernel launches.
 //
-// Planning never reads device data (sequence lengths stay on the device), so
-// a call is safe to capture in a HIP graph once its workspace exists; this is
-// the capture-safe alternative to a planner that reads the lengths on the host
+// Planning never reads device data (sequence lengths and packed query offsets
+// stay on the device), so a call is safe to capture in a HIP graph once its
+// workspace exists; this is the capture-safe alternative to a planner that
+// reads the lengths on the host
 // (flashinfer.attention.prims_ts.batch_decode_with_paged_kv_cache, summary).
 #include "pkvd.h"
 
@@ -16,11 +17,13 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
 #include "decode_args.h"
 #include "merge_states.h"
+#include "schedule.h"
 
 namespace {
 
@@ -36,230 +39,46 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS a workgroup may hold on gfx950
+
+// ---------------------------------------------------------------------------
+// tuning overrides (measurement and test knobs), read from the environment
+// once, and again on pkvd_reload_tuning()
+// ---------------------------------------------------------------------------
+struct Tuning {
+  int force_path = -1;       // PKVD_FORCE_PATH: 0 VALU, 1 MFMA
+  int waves = 0;             // PKVD_WAVES: waves of the persistent grid
+  int min_wave_blocks = 2;   // PKVD_MIN_WAVE_BLOCKS
+  int seg_cost = -1;         // PKVD_SEG_COST: virtual blocks ahead of each unit
+  int groups = 0;            // PKVD_GROUPS: workgroups
+  int merge_kernel = -1;     // PKVD_MERGE_KERNEL: 0 in place, 1 second kernel
+  int unit_mode = -1;        // PKVD_UNIT_MODE: 0 block slices, 1 whole units
+  int slot_w[4] = {0, 0, 0, 0};   // PKVD_SLOT_W="w0,w1,w2,w3" (0: default)
+  int log = 0;               // PKVD_LOG: print each plan to stderr
+};
+
+std::mutex g_tuning_mutex;
+Tuning g_tuning;
+bool g_tuning_loaded = false;
+
 int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
   if (!s || !*s) return dflt;
   return atoi(s);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-
-struct Shapes {
-  int64_t R, Hq, D, P, Hkv, ps, B, C;
-  bool bf16;
-};
-
-struct Plan {
-  int path;             // pkvd::kPathValu or pkvd::kPathMfma; -1: not plannable
-  int rows_per_tile;
-  int row_tiles;
-  int num_waves;        // waves of the persistent grid
-  int min_wave_blocks;  // minimum 16-key blocks per participating wave
-  int64_t workgroups;
-  int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
-  int merge_kernel;      // 1: cut units are merged by a second kernel
-  int seg_cost;          // virtual blocks ahead of each unit in the sliced block space
-  int slot_w[4];         // slice weights of the waves at position 0..3 on their SIMD
-  int64_t slots;         // partial-state slots: two per wave
-  // Workspace: one allocation whose first eighth (int_area) holds int32
-  // state that is zero when allocated and that every call leaves at zero:
-  // the arrival counters (at 0).  The
-  // partial LSEs, outputs and the request prefix follow the int area.  The
-  // int area's size belongs to the allocation, not the plan, so floats of
-  // one plan never lie where another plan keeps int state.  Offsets are
-  // relative to each area's start; ws_bytes is the allocation size needed.
-  size_t int_bytes;
-  size_t ws_lse, ws_o, ws_pref, ws_vpref, float_bytes;
-  size_t ws_bytes;
-};
-
-// Bytes of the int area of an allocation of `bytes`.
-size_t int_area(size_t bytes) { return bytes / 8 / 256 * 256; }
-
-// Shape checks shared by every entry point.  Returns PKVD_OK or an error.
-int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* bt,
-                 int32_t Lq, int32_t wl, Shapes* s) {
-  if (!q || !k || !bt) return fail(PKVD_ERR_INVALID_ARG, "q, k_cache and block_tables are required");
-  if (q->ndim != 3) return fail(PKVD_ERR_INVALID_ARG, "q must be 3-D (B*q_len_per_req, Hq, D)");
-  if (q->dtype != PKVD_BF16 && q->dtype != PKVD_F16)
-    return fail(PKVD_ERR_INVALID_ARG, "q must be bf16 or fp16");
-  if (k->ndim != 4) return fail(PKVD_ERR_INVALID_ARG, "k_cache must be 4-D (pages, Hkv, page_size, D)");
-  if (bt->ndim != 2 || bt->dtype != PKVD_I32)
-    return fail(PKVD_ERR_INVALID_ARG, "block_tables must be a 2-D int32 tensor (B, C)");
-  if (Lq < 1) return fail(PKVD_ERR_INVALID_ARG, "q_len_per_req must be >= 1");
-  if (wl < -1) return fail(PKVD_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
-  s->R = q->shape[0];
-  s->Hq = q->shape[1];
-  s->D = q->shape[2];
-  s->P = k->shape[0];
-  s->Hkv = k->shape[1];
-  s->ps = k->shape[2];
-  s->B = bt->shape[0];
-  s->C = bt->shape[1];
-  s->bf16 = q->dtype == PKVD_BF16;
-  if (s->R < 1 || s->Hq < 1 || s->D < 1 || s->P < 1 || s->Hkv < 1 || s->ps < 1 || s->B < 1 ||
-      s->C < 1)
-    return fail(PKVD_ERR_INVALID_ARG, "every dimension must be >= 1");
-  if (k->shape[3] != s->D) return fail(PKVD_ERR_INVALID_ARG, "k_cache head_dim differs from q");
-  if (s->R != s->B * Lq)
-    return fail(PKVD_ERR_INVALID_ARG, "q.shape[0]=%lld is not B*q_len_per_req=%lld",
-                (long long)s->R, (long long)(s->B * Lq));
-  if (s->Hq % s->Hkv)
-    return fail(PKVD_ERR_INVALID_ARG, "num_heads_qo=%lld is not a multiple of num_heads_kv=%lld",
-                (long long)s->Hq, (long long)s->Hkv);
-  if (s->D != 64 && s->D != 128)
-    return fail(PKVD_ERR_UNSUPPORTED, "head_dim=%lld not built (64 and 128 are)", (long long)s->D);
-  if (s->ps > 256) return fail(PKVD_ERR_UNSUPPORTED, "page_size=%lld > 256", (long long)s->ps);
-  if (s->B > pkvd::kMaxBatch)
-    return fail(PKVD_ERR_UNSUPPORTED, "batch of %lld requests > %d", (long long)s->B,
-                pkvd::kMaxBatch);
-  if (s->P > INT32_MAX || s->C * s->ps > (1LL << 30) || s->R * s->Hq > (1LL << 30) ||
-      s->Hq > 65535)
-    return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
-  return PKVD_OK;
-}
-
-// CUs of the current device, waves per workgroup and resident workgroups per
-// CU for a kernel; an MI355X (256 CUs, one workgroup per CU) is assumed when
-// no device answers.
-struct DeviceFit {
-  int cus = 256;
-  int group_waves = 8;
-  int blocks_per_cu = 1;
-};
-
-DeviceFit device_fit(int path, int rt, const Shapes& s) {
-  DeviceFit f;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return f;
-  }
-  static std::mutex mu;
-  static int cached_cus[64] = {0};
-  std::lock_guard<std::mutex> lock(mu);
-  if (dev >= 0 && dev < 64) {
-    if (!cached_cus[dev]) {
-      int n = 0;
-      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-          n > 0)
-        cached_cus[dev] = n;
-      else
-        (void)hipGetLastError();
-    }
-    if (cached_cus[dev]) f.cus = cached_cus[dev];
-  }
-  const bool pow2 = s.ps >= pkvd::kBlockKeys && (s.ps & (s.ps - 1)) == 0;
-  const int gw = pkvd::decode_group_waves(path, rt, (int)s.D);
-  if (gw > 0) f.group_waves = gw;
-  // One workgroup per CU, holding the WPE waves per SIMD the kernel's
-  // register budget was fitted to.  The occupancy query can report room for
-  // a second workgroup when the kernel needs fewer registers than that
-  // budget, but on MI355X the second one did not become resident alongside
-  // (per-wave start stamps: half the waves began only when the first half
-  // was done), so the grid is never sized for more than one.
-  const int n = pkvd::decode_blocks_per_cu(path, rt, (int)s.D, s.bf16, pow2,
-                                           pkvd::decode_lds_bytes((int)s.B, 64 * f.group_waves, 0));
-  if (n <= 0) (void)hipGetLastError();
-  f.blocks_per_cu = 1;
-  return f;
-}
-
-// Virtual blocks ahead of each unit in the sliced block space (see make_plan),
-// per engine, measured on MI355X (llama3_8b-shaped batch, VALU engine with a
-// 6-deep ring: 0 -> 114.3 us, 2 -> 109.9, 3 -> 108.3, 4 -> 106.7, 6 -> 107.1;
-// with the 3-deep ring: 5 -> 103.1, 6 -> 103.4, 7 -> 104.5.  MFMA engine,
-// spec_verify: 0 -> 118.5 us, 6 -> 116.6).
-int default_seg_cost(int path) { return path == pkvd::kPathMfma ? 6 : 5; }
-
-// Default slice weight of the waves at position `slot` on their SIMD.  Equal
-// weights measured fastest for the default engines on MI355X (the MFMA
-// engine at D = 128 runs one wave per SIMD; for the others the second wave
-// finishes last with equal slices, but a CU's waves share one memory pipe,
-// so moving blocks to the first wave did not shorten the call).
-int default_slot_weight(int path, int rows_per_tile, int slot) {
-  (void)path;
-  (void)rows_per_tile;
-  (void)slot;
-  return 100;
-}
-
-Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
-  Plan p{};
-  const int64_t g = s.Hq / s.Hkv;
-  const int64_t R = g * Lq;
-  // Groups of more than 4 query rows per kv head run on MFMA in 16-row tiles
-  // (a group of 8 leaves half of each tile as padding rows); groups of up to
-  // 4 use VALU dot products.  The VALU engine issues about 27 vector
-  // instructions per (key, kv head) at 4 rows and more at 8, so past 4 rows
-  // the vector units, not HBM, set the pace, while the matrix cores are idle.
-  // Measured on MI355X: 8 rows, D = 128 (131k-key requests) 248 -> 217 us;
-  // 8 rows, D = 64 (window of 128) 50 -> 36 us; 4 rows, D = 128 (2k keys)
-  // 118 us VALU vs 135 us MFMA.
-  // PKVD_FORCE_PATH=0/1 overrides the choice (for measurements and tests).
-  const int forced_path = env_int("PKVD_FORCE_PATH", -1);
-  p.path = forced_path == pkvd::kPathValu || forced_path == pkvd::kPathMfma
-               ? forced_path
-               : (R > 4 ? pkvd::kPathMfma : pkvd::kPathValu);
-  p.rows_per_tile = p.path == pkvd::kPathMfma ? 16 : (R <= 4 ? 4 : 8);
-  p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
-  p.units = s.B * s.Hkv * p.row_tiles;
-
-  // the linear block space must fit int32: units * blocks per unit
-  int64_t kcap = s.C * s.ps;
-  if (wl >= 0) kcap = std::min<int64_t>(kcap, (int64_t)wl + Lq);
-  const int64_t max_blocks = (kcap + pkvd::kBlockKeys - 1) / pkvd::kBlockKeys + 1;
-  // Each unit is preceded by seg_cost virtual blocks in the space the waves'
-  // slices divide, so a slice that starts a unit (a segment switch costs the
-  // wave about as long as streaming a few blocks) holds that many fewer real
-  // blocks.  PKVD_SEG_COST overrides the default (0 turns it off).
-  int seg_default = default_seg_cost(p.path);
-  p.seg_cost = 0;   // set below, once the grid size is known
-  if (p.units * (max_blocks + 64) >= INT32_MAX) return Plan{-1};
-
-  const DeviceFit f = device_fit(p.path, p.rows_per_tile, s);
-  int64_t nw = (int64_t)f.cus * f.blocks_per_cu * f.group_waves;
-  const int forced = env_int("PKVD_WAVES", 0);
-  if (forced > 0) nw = forced;
-  // at least 2 blocks per participating wave: short batches then spread
-  // over many waves (tiny 4-request batch: 24.2 us at 8 blocks, 16.2 us at
-  // 2), while long ones use every resident wave anyway
-  p.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 2));
-  // no more waves than the largest possible work can occupy
-  nw = std::min<int64_t>(nw, (p.units * max_blocks + p.min_wave_blocks - 1) / p.min_wave_blocks);
-  nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
-  p.num_waves = (int)nw;
-  // Short units (a window keeps at most 32 blocks) that are at least half as
-  // many as the waves: virtual blocks as long as a unit snap every slice
-  // boundary to a unit start, so each unit is streamed whole by one wave and
-  // none needs a merge (sink + window batch, 1024 units of 9 blocks over
-  // 2048 waves: 27.5 -> 23.6 us).  With few units (a 4-request batch) cutting
-  // them over more waves is faster.
-  if (max_blocks <= 32 && 2 * p.units >= nw) seg_default = (int)max_blocks;
-  p.seg_cost = std::min(64, std::max(0, env_int("PKVD_SEG_COST", seg_default)));
-  // one workgroup per resident slot (one per CU) even when waves are few,
-  // so that they spread over the CUs; more if the waves need more
-  p.workgroups = std::max<int64_t>((nw + f.group_waves - 1) / f.group_waves,
-                                   std::min<int64_t>((int64_t)f.cus * f.blocks_per_cu, nw));
-  // PKVD_GROUPS forces fewer, fuller workgroups (tests reach several waves
-  // per SIMD, and so the slot weights, with small grids)
-  const int forced_groups = env_int("PKVD_GROUPS", 0);
-  if (forced_groups > 0)
-    p.workgroups = std::max<int64_t>(forced_groups, (nw + f.group_waves - 1) / f.group_waves);
-  // Where cut units leave large partial states (many pieces per unit or wide
-  // tiles: over 32 KB per unit) one wave merging a unit at the end would be
-  // slow; a second kernel merges them all in parallel instead.  Estimated
-  // from shapes only (pieces per unit ~ waves / units + 1).
-  const int64_t pieces = nw / std::max<int64_t>(p.units, 1) + 1;
-  const int64_t unit_bytes = pieces * p.rows_per_tile * s.D * 4;
-  p.merge_kernel = env_int("PKVD_MERGE_KERNEL", unit_bytes > 32768 ? 1 : 0) ? 1 : 0;
-  // Slice weights by position on the SIMD: of the two waves a SIMD holds,
-  // the first issues ahead of the second and streams faster (per-wave
-  // timestamps: about 1.2x the blocks per microsecond, and it starts
-  // earlier), so with equal slices the second waves finish last.  Weight
-  // W[s] goes to the waves at position s on their SIMD.
-  // PKVD_SLOT_W="w0,w1,w2,w3" (1..1024, max/min <= 4) overrides the default.
-  for (int r = 0; r < 4; ++r) p.slot_w[r] = default_slot_weight(p.path, p.rows_per_tile, r);
+Tuning read_tuning() {
+  Tuning t;
+  t.force_path = env_int("PKVD_FORCE_PATH", -1);
+  t.waves = env_int("PKVD_WAVES", 0);
+  t.min_wave_blocks = std::max(1, env_int("PKVD_MIN_WAVE_BLOCKS", 2));
+  t.seg_cost = env_int("PKVD_SEG_COST", -1);
+  t.groups = env_int("PKVD_GROUPS", 0);
+  t.merge_kernel = env_int("PKVD_MERGE_KERNEL", -1);
+  t.unit_mode = env_int("PKVD_UNIT_MODE", -1);
+  t.log = env_int("PKVD_LOG", 0);
   if (const char* e = getenv("PKVD_SLOT_W")) {
     int w[4] = {0, 0, 0, 0};
     const int n = sscanf(e, "%d,%d,%d,%d", &w[0], &w[1], &w[2], &w[3]);
@@ -271,8 +90,221 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
       hi = std::max(hi, w[r]);
     }
     if (n > 0 && hi <= 4 * lo)
-      for (int r = 0; r < 4; ++r) p.slot_w[r] = w[r];
+      for (int r = 0; r < 4; ++r) t.slot_w[r] = w[r];
   }
+  return t;
+}
+
+Tuning tuning() {
+  std::lock_guard<std::mutex> lock(g_tuning_mutex);
+  if (!g_tuning_loaded) {
+    g_tuning = read_tuning();
+    g_tuning_loaded = true;
+  }
+  return g_tuning;
+}
+
+// ---------------------------------------------------------------------------
+// shapes and plan
+// ---------------------------------------------------------------------------
+struct Shapes {
+  int64_t rows, Hq, D, P, Hkv, ps, B, C;
+  int64_t Lq;      // fixed rows per request, or the packed capacity
+  bool packed;
+  bool bf16;
+};
+
+struct Plan {
+  int path;             // pkvd::kPathValu or pkvd::kPathMfma; -1: not plannable
+  int rows_per_tile;
+  int row_tiles;
+  int num_waves;        // waves of the persistent grid
+  int min_wave_blocks;  // minimum 16-key blocks per participating wave
+  int64_t workgroups;
+  int64_t units;        // (request, kv head, row tile) triples: one arrival counter each
+  int merge_kernel;     // 1: cut units are merged by a second kernel
+  int unit_mode;        // 1: slice bounds snap to unit starts (no unit is cut)
+  int seg_cost;         // virtual blocks ahead of each unit in the sliced block space
+  int slot_w[4];        // slice weights of the waves at position 0..3 on their SIMD
+  int64_t slots;        // partial-state slots: two per wave
+  int group_waves;      // waves per workgroup
+  size_t lds_bytes;     // dynamic LDS of the decode kernel
+  // Workspace: one allocation whose first eighth (int_area) holds int32
+  // state that is zero when allocated and that every call leaves at zero:
+  // the arrival counters.  The partial LSEs, outputs and the request
+  // prefixes follow the int area.  The int area's size belongs to the
+  // allocation, not the plan, so floats of one plan never lie where another
+  // plan keeps int state.  Offsets are relative to each area's start;
+  // ws_bytes is the allocation size needed.
+  size_t int_bytes;
+  size_t ws_lse, ws_o, ws_pref, ws_vpref, float_bytes;
+  size_t ws_bytes;
+};
+
+// Bytes of the int area of an allocation of `bytes`.
+size_t int_area(size_t bytes) { return bytes / 8 / 256 * 256; }
+
+// Shape checks shared by every entry point: q (rows, Hq, D) or token-major
+// (B, SQ, Hq, D), k_cache (pages, Hkv, page_size, D), block_tables (B, C).
+int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* bt,
+                 const pkvd_tensor* qo, int32_t Lq, int32_t wl, Shapes* s) {
+  if (!q || !k || !bt) return fail(PKVD_ERR_INVALID_ARG, "q, k_cache and block_tables are required");
+  if (q->ndim != 3 && q->ndim != 4)
+    return fail(PKVD_ERR_INVALID_ARG, "q must be 3-D (rows, Hq, D) or 4-D (B, SQ, Hq, D)");
+  if (q->dtype != PKVD_BF16 && q->dtype != PKVD_F16)
+    return fail(PKVD_ERR_INVALID_ARG, "q must be bf16 or fp16");
+  if (k->ndim != 4) return fail(PKVD_ERR_INVALID_ARG, "k_cache must be 4-D (pages, Hkv, page_size, D)");
+  if (bt->ndim != 2 || bt->dtype != PKVD_I32)
+    return fail(PKVD_ERR_INVALID_ARG, "block_tables must be a 2-D int32 tensor (B, C)");
+  if (Lq < 1) return fail(PKVD_ERR_INVALID_ARG, "q_len_per_req must be >= 1");
+  if (wl < -1) return fail(PKVD_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
+  const int o = q->ndim - 3;   // a 4-D q is (B, SQ) rows
+  s->rows = o ? q->shape[0] * q->shape[1] : q->shape[0];
+  s->Hq = q->shape[o + 1];
+  s->D = q->shape[o + 2];
+  s->P = k->shape[0];
+  s->Hkv = k->shape[1];
+  s->ps = k->shape[2];
+  s->B = bt->shape[0];
+  s->C = bt->shape[1];
+  s->Lq = Lq;
+  s->packed = qo != nullptr;
+  s->bf16 = q->dtype == PKVD_BF16;
+  if (s->rows < 1 || s->Hq < 1 || s->D < 1 || s->P < 1 || s->Hkv < 1 || s->ps < 1 || s->B < 1 ||
+      s->C < 1)
+    return fail(PKVD_ERR_INVALID_ARG, "every dimension must be >= 1");
+  if (k->shape[3] != s->D) return fail(PKVD_ERR_INVALID_ARG, "k_cache head_dim differs from q");
+  if (o && q->shape[0] != s->B)
+    return fail(PKVD_ERR_INVALID_ARG, "a 4-D q must be (B, SQ, Hq, D) with B = block_tables rows");
+  if (!s->packed && s->rows != s->B * Lq)
+    return fail(PKVD_ERR_INVALID_ARG, "q holds %lld rows, not B*q_len_per_req=%lld",
+                (long long)s->rows, (long long)(s->B * Lq));
+  if (s->packed) {
+    if (o) return fail(PKVD_ERR_INVALID_ARG, "packed rows (qo_indptr) need a 3-D q (total_q, Hq, D)");
+    if (qo->ndim != 1 || qo->dtype != PKVD_I32 || qo->shape[0] != s->B + 1 ||
+        qo->strides[0] != 1 || !qo->data)
+      return fail(PKVD_ERR_INVALID_ARG, "qo_indptr must be a contiguous int32 (B + 1,) tensor");
+  }
+  if (s->Hq % s->Hkv)
+    return fail(PKVD_ERR_INVALID_ARG, "num_heads_qo=%lld is not a multiple of num_heads_kv=%lld",
+                (long long)s->Hq, (long long)s->Hkv);
+  if (s->D != 64 && s->D != 128)
+    return fail(PKVD_ERR_UNSUPPORTED, "head_dim=%lld not built (64 and 128 are)", (long long)s->D);
+  if (s->ps > 256) return fail(PKVD_ERR_UNSUPPORTED, "page_size=%lld > 256", (long long)s->ps);
+  if (s->B > pkvd::kMaxBatch)
+    return fail(PKVD_ERR_UNSUPPORTED, "batch of %lld requests > %d", (long long)s->B,
+                pkvd::kMaxBatch);
+  if (s->P > INT32_MAX || s->C * s->ps > (1LL << 30) || s->rows * s->Hq > (1LL << 30) ||
+      s->Hq > 65535 || (s->Hq / s->Hkv) * Lq > 65535)
+    return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
+  return PKVD_OK;
+}
+
+// CUs of the current device (cached per device); an MI355X (256 CUs) is
+// assumed when no device answers.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  static std::mutex mu;
+  static int cached[64] = {0};
+  if (dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached[dev] = n;
+    else
+      (void)hipGetLastError();
+  }
+  return cached[dev] ? cached[dev] : 256;
+}
+
+// Virtual blocks ahead of each unit in the sliced block space, per engine,
+// measured on MI355X (llama3_8b-shaped batch, VALU engine with a 6-deep ring:
+// 0 -> 114.3 us, 2 -> 109.9, 3 -> 108.3, 4 -> 106.7, 6 -> 107.1; with the
+// 3-deep ring: 5 -> 103.1, 6 -> 103.4, 7 -> 104.5.  MFMA engine, spec_verify:
+// 0 -> 118.5 us, 6 -> 116.6).
+int default_seg_cost(int path) { return path == pkvd::kPathMfma ? 6 : 5; }
+
+Plan make_plan(const Shapes& s, int32_t wl, const Tuning& tu) {
+  Plan p{};
+  const int64_t g = s.Hq / s.Hkv;
+  const int64_t R = g * s.Lq;
+  // Groups of more than 4 query rows per kv head run on MFMA in 16-row tiles
+  // (a group of 8 leaves half of each tile as padding rows); groups of up to
+  // 4 use VALU dot products.  The VALU engine issues about 27 vector
+  // instructions per (key, kv head) at 4 rows and more at 8, so past 4 rows
+  // the vector units, not HBM, set the pace, while the matrix cores are idle.
+  // Measured on MI355X: 8 rows, D = 128 (131k-key requests) 248 -> 217 us;
+  // 8 rows, D = 64 (window of 128) 50 -> 36 us; 4 rows, D = 128 (2k keys)
+  // 118 us VALU vs 135 us MFMA.
+  p.path = tu.force_path == pkvd::kPathValu || tu.force_path == pkvd::kPathMfma
+               ? tu.force_path
+               : (R > 4 ? pkvd::kPathMfma : pkvd::kPathValu);
+  p.rows_per_tile = p.path == pkvd::kPathMfma ? 16 : (R <= 4 ? 4 : 8);
+  p.row_tiles = (int)((R + p.rows_per_tile - 1) / p.rows_per_tile);
+  p.units = s.B * s.Hkv * p.row_tiles;
+  p.group_waves = pkvd::decode_group_waves(p.path, p.rows_per_tile, (int)s.D);
+  if (p.group_waves <= 0) return Plan{-1};
+
+  // the linear block space must fit int32: units * blocks per unit
+  int64_t kcap = s.C * s.ps;
+  if (wl >= 0) kcap = std::min<int64_t>(kcap, (int64_t)wl + s.Lq);
+  const int64_t max_blocks = (kcap + pkvd::kBlockKeys - 1) / pkvd::kBlockKeys + 1;
+  if (p.units * (max_blocks + 64) >= INT32_MAX) return Plan{-1};
+
+  // One workgroup per CU, holding the waves per SIMD the kernel's register
+  // budget was fitted to.  (The occupancy calculator can report room for a
+  // second workgroup when the kernel needs fewer registers than that budget,
+  // but on MI355X the second one did not become resident alongside: per-wave
+  // start stamps showed half the waves beginning only when the first half
+  // was done.)
+  const int cus = device_cus();
+  int64_t nw = (int64_t)cus * p.group_waves;
+  if (tu.waves > 0) nw = tu.waves;
+  // at least 2 blocks per participating wave: short batches then spread
+  // over many waves (tiny 4-request batch: 24.2 us at 8 blocks, 16.2 us at
+  // 2), while long ones use every resident wave anyway
+  p.min_wave_blocks = tu.min_wave_blocks;
+  // no more waves than the largest possible work can occupy
+  nw = std::min<int64_t>(nw, (p.units * max_blocks + p.min_wave_blocks - 1) / p.min_wave_blocks);
+  nw = std::max<int64_t>(1, std::min<int64_t>(nw, 1 << 20));
+  // Short units (a window keeps at most 32 blocks) that are at least half as
+  // many as the waves are streamed whole, one wave per unit: the slice
+  // bounds snap to unit starts, so no unit is cut and nothing is merged.
+  // (Cutting 1024 window units of 9 blocks over 2048 waves wrote 9 MB of
+  // partial states per call.)  With few units (a 4-request batch) cutting
+  // them over more waves is faster.
+  p.unit_mode = max_blocks <= 32 && 2 * p.units >= nw ? 1 : 0;
+  if (tu.unit_mode == 0 || tu.unit_mode == 1) p.unit_mode = tu.unit_mode;
+  if (p.unit_mode && tu.waves <= 0) nw = std::min<int64_t>(nw, p.units);
+  p.num_waves = (int)nw;
+  p.seg_cost = p.unit_mode ? 0
+                           : std::min(64, std::max(0, tu.seg_cost >= 0 ? tu.seg_cost
+                                                                      : default_seg_cost(p.path)));
+  // one workgroup per resident slot (one per CU) even when waves are few,
+  // so that they spread over the CUs; more if the waves need more
+  p.workgroups = std::max<int64_t>((nw + p.group_waves - 1) / p.group_waves,
+                                   std::min<int64_t>((int64_t)cus, nw));
+  // PKVD_GROUPS forces fewer, fuller workgroups (tests reach several waves
+  // per SIMD, and so the slot weights, with small grids)
+  if (tu.groups > 0)
+    p.workgroups = std::max<int64_t>(tu.groups, (nw + p.group_waves - 1) / p.group_waves);
+  // Where cut units leave large partial states (many pieces per unit or wide
+  // tiles: over 32 KB per unit) one wave merging a unit at the end would be
+  // slow; a second kernel merges them all in parallel instead.  Estimated
+  // from shapes only (pieces per unit ~ waves / units + 1).
+  const int64_t pieces = nw / std::max<int64_t>(p.units, 1) + 1;
+  const int64_t unit_bytes = pieces * p.rows_per_tile * s.D * 4;
+  p.merge_kernel = tu.merge_kernel >= 0 ? (tu.merge_kernel ? 1 : 0) : (unit_bytes > 32768 ? 1 : 0);
+  if (p.unit_mode) p.merge_kernel = 0;   // nothing to merge
+  // Slice weights by position on the SIMD (equal by default: they measured
+  // fastest for the default engines).
+  for (int r = 0; r < 4; ++r) p.slot_w[r] = tu.slot_w[0] > 0 ? tu.slot_w[r] : 100;
+  p.lds_bytes = pkvd::decode_lds_bytes((int)s.B, 64 * p.group_waves, 0, s.packed);
   // two partial slots per wave (its slice's first and last segments)
   p.slots = (int64_t)2 * nw;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -291,41 +323,95 @@ Plan make_plan(const Shapes& s, int32_t Lq, int32_t wl) {
   return p;
 }
 
-// Library-owned workspace, one per device (layout in Plan).  It is zeroed
-// when allocated, and every call leaves its int32 state at zero again.
-struct Workspace {
+// ---------------------------------------------------------------------------
+// workspaces
+// ---------------------------------------------------------------------------
+// Library-owned, one per device.  It is zeroed when allocated, and every call
+// leaves its int32 state at zero again.  It only grows; a buffer it replaces
+// is kept (never freed) until the process ends, because a HIP graph captured
+// earlier may still launch kernels on it.  It never grows while the stream is
+// capturing (the call fails with PKVD_ERR_WORKSPACE instead).
+struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;
+  void* bound = nullptr;     // pkvd_set_workspace: the caller's buffer (not owned)
+  size_t bound_bytes = 0;
 };
 std::mutex g_ws_mutex;
-Workspace g_ws[64];
+DeviceWorkspace g_ws[64];
 
-int ensure_workspace(size_t bytes, void** out, size_t* size) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+int current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= 64) return fail(PKVD_ERR_HIP, "device id %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& w = g_ws[dev];
-  if (w.bytes < bytes) {
-    if (w.ptr) {
-      e = hipFree(w.ptr);   // waits for work that may still use the old buffer
-      w.ptr = nullptr;
-      w.bytes = 0;
-      if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return fail(PKVD_ERR_WORKSPACE, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
-    e = hipMemset(p, 0, bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      return fail(PKVD_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
-    }
-    w.ptr = p;
-    w.bytes = bytes;
+  if (*dev < 0 || *dev >= 64) return fail(PKVD_ERR_HIP, "device id %d out of range", *dev);
+  return PKVD_OK;
+}
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
   }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// Grows the library-owned workspace of the current device to >= bytes.
+int grow_library_workspace(int dev, size_t bytes, hipStream_t stream, bool may_capture) {
+  DeviceWorkspace& w = g_ws[dev];
+  if (w.bytes >= bytes) return PKVD_OK;
+  if (may_capture && stream_capturing(stream))
+    return fail(PKVD_ERR_WORKSPACE,
+                "the workspace needs %zu bytes (it holds %zu) and the stream is capturing a "
+                "graph: call pkvd_reserve_workspace (or pass a workspace) before the capture",
+                bytes, w.bytes);
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKVD_ERR_WORKSPACE, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  }
+  e = hipMemset(p, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return fail(PKVD_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
+  }
+  if (w.ptr) w.retired.push_back(w.ptr);
+  w.ptr = p;
+  w.bytes = bytes;
+  return PKVD_OK;
+}
+
+// The workspace of one call: the caller's per-call buffer, else the buffer
+// bound to the device with pkvd_set_workspace, else the library's own.
+int resolve_workspace(void* call_ws, size_t call_bytes, size_t need, hipStream_t stream,
+                      void** out, size_t* size) {
+  if (call_ws) {
+    if (call_bytes < need)
+      return fail(PKVD_ERR_WORKSPACE, "workspace of %zu bytes is too small: this call needs %zu",
+                  call_bytes, need);
+    *out = call_ws;
+    *size = call_bytes;
+    return PKVD_OK;
+  }
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != PKVD_OK) return st;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace& w = g_ws[dev];
+  if (w.bound) {
+    if (w.bound_bytes < need)
+      return fail(PKVD_ERR_WORKSPACE,
+                  "the bound workspace of %zu bytes is too small: this call needs %zu",
+                  w.bound_bytes, need);
+    *out = w.bound;
+    *size = w.bound_bytes;
+    return PKVD_OK;
+  }
+  st = grow_library_workspace(dev, need, stream, true);
+  if (st != PKVD_OK) return st;
   *out = w.ptr;
   *size = w.bytes;
   return PKVD_OK;
@@ -340,83 +426,30 @@ bool contiguous(const pkvd_tensor* t) {
   return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pkvd_version(void) { return "0.1.0"; }
-
-const char* pkvd_last_error(void) { return g_last_error.c_str(); }
-
-const char* pkvd_status_string(int status) {
-  switch (status) {
-    case PKVD_OK: return "ok";
-    case PKVD_ERR_INVALID_ARG: return "invalid argument";
-    case PKVD_ERR_UNSUPPORTED: return "unsupported";
-    case PKVD_ERR_WORKSPACE: return "workspace allocation failed";
-    case PKVD_ERR_HIP: return "HIP error";
-    default: return "unknown status";
-  }
-}
-
-int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
-                     const pkvd_tensor* block_tables, int32_t q_len_per_req, int32_t window_left,
-                     int64_t out[6]) {
-  Shapes s;
-  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
-  if (st != PKVD_OK) return st;
-  if (!out) return fail(PKVD_ERR_INVALID_ARG, "out is NULL");
-  Plan p = make_plan(s, q_len_per_req, window_left);
-  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
-  out[0] = p.path;
-  out[1] = p.rows_per_tile;
-  out[2] = p.row_tiles;
-  out[3] = p.num_waves;
-  out[4] = p.min_wave_blocks;
-  out[5] = p.workgroups;
-  return PKVD_OK;
-}
-
-int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache,
-                                const pkvd_tensor* block_tables, int32_t q_len_per_req,
-                                int32_t window_left, size_t* bytes) {
-  Shapes s;
-  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
-  if (st != PKVD_OK) return st;
-  if (!bytes) return fail(PKVD_ERR_INVALID_ARG, "bytes is NULL");
-  const Plan p = make_plan(s, q_len_per_req, window_left);
-  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
-  *bytes = p.ws_bytes;
-  return PKVD_OK;
-}
-
-int pkvd_reserve_workspace(size_t bytes) {
-  void* p = nullptr;
-  size_t size = 0;
-  g_last_error.clear();
-  if (bytes == 0) return PKVD_OK;
-  return ensure_workspace(bytes, &p, &size);
-}
-
-int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_tensor* v_cache,
-                const pkvd_tensor* block_tables, const pkvd_tensor* seq_lens_kv, float scale,
-                int32_t q_len_per_req, int32_t window_left, const pkvd_tensor* sinks,
-                pkvd_tensor* out, pkvd_tensor* lse, void* stream) {
-  g_last_error.clear();
-  Shapes s;
-  int st = check_shapes(q, k_cache, block_tables, q_len_per_req, window_left, &s);
-  if (st != PKVD_OK) return st;
-  const pkvd_tensor* k = k_cache;
-  const pkvd_tensor* v = v_cache;
-  if (!v || !seq_lens_kv || !out) return fail(PKVD_ERR_INVALID_ARG, "v_cache, seq_lens_kv and out are required");
-  if (!q->data || !k->data || !v->data || !block_tables->data || !seq_lens_kv->data || !out->data)
+// Checks of everything a decode call reads or writes beyond the shapes.
+int check_call(const pkvd_decode_args* x, const Shapes& s) {
+  const pkvd_tensor* q = x->q;
+  const pkvd_tensor* k = x->k_cache;
+  const pkvd_tensor* v = x->v_cache;
+  if (!v || !x->seq_lens_kv || !x->out)
+    return fail(PKVD_ERR_INVALID_ARG, "v_cache, seq_lens_kv and out are required");
+  if (!q->data || !k->data || !v->data || !x->block_tables->data || !x->seq_lens_kv->data ||
+      !x->out->data)
     return fail(PKVD_ERR_INVALID_ARG, "NULL data pointer");
-  if (!isfinite(scale)) return fail(PKVD_ERR_INVALID_ARG, "scale must be finite");
-  // q: head_dim innermost and dense, rows 16-byte aligned
-  if (q->strides[2] != 1) return fail(PKVD_ERR_INVALID_ARG, "q must have head_dim innermost and dense");
-  if (!aligned16(q->data) || q->strides[0] % 8 || q->strides[1] % 8)
+  if (!isfinite(x->scale)) return fail(PKVD_ERR_INVALID_ARG, "scale must be finite");
+  if (!isfinite(x->out_scale)) return fail(PKVD_ERR_INVALID_ARG, "out_scale must be finite");
+  if (x->mask != PKVD_MASK_CAUSAL && x->mask != PKVD_MASK_DENSE)
+    return fail(PKVD_ERR_INVALID_ARG, "mask must be PKVD_MASK_CAUSAL or PKVD_MASK_DENSE");
+  // q: head_dim innermost and dense, rows 16-byte aligned; a 4-D q must
+  // step its SQ rows evenly (stride[0] = SQ * stride[1]) so that it is a
+  // (B * SQ, Hq, D) row tensor
+  const int o = q->ndim - 3;
+  if (q->strides[o + 2] != 1) return fail(PKVD_ERR_INVALID_ARG, "q must have head_dim innermost and dense");
+  if (o && q->shape[1] > 1 && q->strides[0] != q->shape[1] * q->strides[1])
+    return fail(PKVD_ERR_INVALID_ARG, "a 4-D q must hold its SQ rows at one stride");
+  const int64_t q_sr = o ? q->strides[1] : q->strides[0], q_sh = q->strides[o + 1];
+  if (!aligned16(q->data) || q_sr % 8 || q_sh % 8)
     return fail(PKVD_ERR_INVALID_ARG, "q rows must start 16-byte aligned");
-  // K / V
   for (const pkvd_tensor* t : {k, v}) {
     const char* nm = t == k ? "k_cache" : "v_cache";
     if (t->ndim != 4 || t->dtype != q->dtype)
@@ -430,73 +463,132 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
     if (t->strides[0] < 0 || t->strides[1] < 0)
       return fail(PKVD_ERR_INVALID_ARG, "%s strides must be non-negative", nm);
   }
-  if (s.Hq / s.Hkv < 1) return fail(PKVD_ERR_INVALID_ARG, "num_heads_qo < num_heads_kv");
-  // tables
-  if (block_tables->strides[1] != 1 || block_tables->strides[0] < s.C)
+  const pkvd_tensor* bt = x->block_tables;
+  if (bt->strides[1] != 1 || bt->strides[0] < s.C)
     return fail(PKVD_ERR_INVALID_ARG, "block_tables rows must be contiguous and not overlap");
-  if (seq_lens_kv->ndim != 1 || seq_lens_kv->dtype != PKVD_I32 || seq_lens_kv->shape[0] != s.B ||
-      (s.B > 1 && seq_lens_kv->strides[0] != 1))
+  const pkvd_tensor* sl = x->seq_lens_kv;
+  if (sl->ndim != 1 || sl->dtype != PKVD_I32 || sl->shape[0] != s.B ||
+      (s.B > 1 && sl->strides[0] != 1))
     return fail(PKVD_ERR_INVALID_ARG, "seq_lens_kv must be a contiguous int32 (B,) tensor");
-  if (sinks) {
-    if (!sinks->data || sinks->ndim != 1 || sinks->dtype != PKVD_F32 || sinks->shape[0] != s.Hq ||
-        (s.Hq > 1 && sinks->strides[0] != 1))
+  if (x->sinks) {
+    const pkvd_tensor* sk = x->sinks;
+    if (!sk->data || sk->ndim != 1 || sk->dtype != PKVD_F32 || sk->shape[0] != s.Hq ||
+        (s.Hq > 1 && sk->strides[0] != 1))
       return fail(PKVD_ERR_INVALID_ARG, "sinks must be a contiguous float32 (num_heads_qo,) tensor");
     // the decode kernel stages the sink logits in LDS
     if (s.Hq > pkvd::kMaxSinkHeads)
       return fail(PKVD_ERR_UNSUPPORTED, "sinks with num_heads_qo=%lld > %d", (long long)s.Hq,
                   pkvd::kMaxSinkHeads);
   }
-  if (out->ndim != 3 || out->dtype != q->dtype || out->shape[0] != s.R || out->shape[1] != s.Hq ||
-      out->shape[2] != s.D || !contiguous(out))
-    return fail(PKVD_ERR_INVALID_ARG, "out must be contiguous (B*q_len_per_req, Hq, D) with q's dtype");
-  if (lse) {
-    if (!lse->data || lse->ndim != 2 || lse->dtype != PKVD_F32 || lse->shape[0] != s.R ||
-        lse->shape[1] != s.Hq || !contiguous(lse))
-      return fail(PKVD_ERR_INVALID_ARG, "lse must be contiguous float32 (B*q_len_per_req, Hq)");
+  // out: q's shape (3-D rows or 4-D token-major), contiguous, bf16 / fp16 / fp32
+  const pkvd_tensor* out = x->out;
+  if (out->ndim != q->ndim || !contiguous(out))
+    return fail(PKVD_ERR_INVALID_ARG, "out must be contiguous with q's shape");
+  for (int i = 0; i < q->ndim; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PKVD_ERR_INVALID_ARG, "out must have q's shape");
+  if (out->dtype != PKVD_BF16 && out->dtype != PKVD_F16 && out->dtype != PKVD_F32)
+    return fail(PKVD_ERR_INVALID_ARG, "out must be bf16, fp16 or fp32");
+  if (!aligned16(out->data)) return fail(PKVD_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (x->lse) {
+    const pkvd_tensor* l = x->lse;
+    const bool two_d = l->ndim == 2 && l->shape[0] == s.rows && l->shape[1] == s.Hq;
+    const bool three_d = o && l->ndim == 3 && l->shape[0] == q->shape[0] &&
+                         l->shape[1] == q->shape[1] && l->shape[2] == s.Hq;
+    if (!l->data || l->dtype != PKVD_F32 || !(two_d || three_d) || !contiguous(l))
+      return fail(PKVD_ERR_INVALID_ARG, "lse must be contiguous float32 (rows, Hq)");
   }
+  if (x->workspace && (reinterpret_cast<uintptr_t>(x->workspace) & 255))
+    return fail(PKVD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return PKVD_OK;
+}
 
-  const Plan p = make_plan(s, q_len_per_req, window_left);
-  if (p.path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
+int shapes_of(const pkvd_decode_args* x, Shapes* s) {
+  if (!x) return fail(PKVD_ERR_INVALID_ARG, "args is NULL");
+  return check_shapes(x->q, x->k_cache, x->block_tables, x->qo_indptr, x->q_len, x->window_left, s);
+}
+
+int plan_of(const Shapes& s, int32_t wl, Plan* p) {
+  *p = make_plan(s, wl, tuning());
+  if (p->path < 0) return fail(PKVD_ERR_UNSUPPORTED, "block-table capacity C * page_size too large");
+  return PKVD_OK;
+}
+
+// The kernel arguments of a call (everything but the workspace).
+void fill_args(const pkvd_decode_args* x, const Shapes& s, const Plan& p, pkvd::DecodeArgs* out) {
+  const pkvd_tensor* q = x->q;
+  const int o = q->ndim - 3;
   pkvd::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
-  a.q_sr = q->strides[0];
-  a.q_sh = q->strides[1];
-  a.k = static_cast<const uint16_t*>(k->data);
-  a.k_sp = k->strides[0];
-  a.k_sh = k->strides[1];
-  a.v = static_cast<const uint16_t*>(v->data);
-  a.v_sp = v->strides[0];
-  a.v_sh = v->strides[1];
-  a.bt = static_cast<const int32_t*>(block_tables->data);
-  a.bt_sr = block_tables->strides[0];
-  a.seq_lens = static_cast<const int32_t*>(seq_lens_kv->data);
-  a.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
-  a.out = static_cast<uint16_t*>(out->data);
-  a.lse = lse ? static_cast<float*>(lse->data) : nullptr;
+  a.q_sr = o ? q->strides[1] : q->strides[0];
+  a.q_sh = q->strides[o + 1];
+  a.k = static_cast<const uint16_t*>(x->k_cache->data);
+  a.k_sp = x->k_cache->strides[0];
+  a.k_sh = x->k_cache->strides[1];
+  a.v = x->v_cache ? static_cast<const uint16_t*>(x->v_cache->data) : nullptr;
+  a.v_sp = x->v_cache ? x->v_cache->strides[0] : 0;
+  a.v_sh = x->v_cache ? x->v_cache->strides[1] : 0;
+  a.bt = static_cast<const int32_t*>(x->block_tables->data);
+  a.bt_sr = x->block_tables->strides[0];
+  a.seq_lens = x->seq_lens_kv ? static_cast<const int32_t*>(x->seq_lens_kv->data) : nullptr;
+  a.qo = x->qo_indptr ? static_cast<const int32_t*>(x->qo_indptr->data) : nullptr;
+  a.sinks = x->sinks ? static_cast<const float*>(x->sinks->data) : nullptr;
+  a.out = x->out ? x->out->data : nullptr;
+  const int od = x->out ? x->out->dtype : x->q->dtype;
+  a.out_type = od == PKVD_BF16 ? pkvd::kOutBf16 : od == PKVD_F16 ? pkvd::kOutF16 : pkvd::kOutF32;
+  a.lse = x->lse ? static_cast<float*>(x->lse->data) : nullptr;
   a.B = (int32_t)s.B;
   a.Hq = (int32_t)s.Hq;
   a.Hkv = (int32_t)s.Hkv;
   a.g = (int32_t)(s.Hq / s.Hkv);
-  a.Lq = q_len_per_req;
+  a.Lq = x->q_len;
+  a.rows = (int32_t)s.rows;
   a.ps = (int32_t)s.ps;
   a.P = (int32_t)s.P;
   a.C = (int32_t)s.C;
-  a.window_left = window_left;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.window_left = x->window_left;
+  a.causal = x->mask == PKVD_MASK_CAUSAL ? 1 : 0;
+  a.scale_log2 = (float)((double)x->scale * 1.4426950408889634);
+  a.out_scale = x->out_scale;
   a.D = (int32_t)s.D;
   a.row_tiles = p.row_tiles;
+  a.rows_per_tile = p.rows_per_tile;
   a.num_waves = p.num_waves;
   a.groups = (int32_t)p.workgroups;
   a.min_wave_blocks = p.min_wave_blocks;
+  a.seg_cost = p.seg_cost;
+  a.unit_mode = p.unit_mode;
+  a.merge_kernel = p.merge_kernel;
+  for (int r = 0; r < 4; ++r) a.slot_w[r] = p.slot_w[r];
+  *out = a;
+}
+
+int run_decode(const pkvd_decode_args* x, void* stream) {
+  g_last_error.clear();
+  Shapes s;
+  int st = shapes_of(x, &s);
+  if (st != PKVD_OK) return st;
+  st = check_call(x, s);
+  if (st != PKVD_OK) return st;
+  Plan p;
+  st = plan_of(s, x->window_left, &p);
+  if (st != PKVD_OK) return st;
+  const size_t lds = pkvd::decode_lds_bytes((int)s.B, 64 * p.group_waves,
+                                            x->sinks ? (int)s.Hq : 0, s.packed);
+  if (lds > kMaxLdsBytes)
+    return fail(PKVD_ERR_UNSUPPORTED, "%lld requests with these options need %zu bytes of LDS",
+                (long long)s.B, lds);
+  pkvd::DecodeArgs a;
+  fill_args(x, s, p, &a);
 #ifdef PKVD_TRACE
   {
     const char* t = getenv("PKVD_TRACE_PTR");   // device buffer of >= waves * 16 uint64
     a.trace = t ? reinterpret_cast<uint64_t*>(strtoull(t, nullptr, 0)) : nullptr;
   }
 #endif
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
   size_t ws_size = 0;
-  st = ensure_workspace(p.ws_bytes, &ws, &ws_size);
+  st = resolve_workspace(x->workspace, x->workspace_bytes, p.ws_bytes, hs, &ws, &ws_size);
   if (st != PKVD_OK) return st;
   char* wi = static_cast<char*>(ws);            // int area
   char* wf = wi + int_area(ws_size);            // floats follow it
@@ -505,16 +597,258 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
   a.ws_o = reinterpret_cast<float*>(wf + p.ws_o);
   a.ws_pref = reinterpret_cast<int32_t*>(wf + p.ws_pref);
   a.ws_vpref = reinterpret_cast<int32_t*>(wf + p.ws_vpref);
-  a.seg_cost = p.seg_cost;
-  a.merge_kernel = p.merge_kernel;
-  for (int r = 0; r < 4; ++r) a.slot_w[r] = p.slot_w[r];
-  if (env_int("PKVD_LOG", 0))
+  if (tuning().log)
     fprintf(stderr,
-            "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d\n",
-            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+            "pkvd: path=%d rows/tile=%d tiles=%d waves=%d min_wave_blocks=%d merge=%d unit=%d "
+            "seg_cost=%d\n",
+            p.path, p.rows_per_tile, p.row_tiles, p.num_waves, p.min_wave_blocks, p.merge_kernel,
+            p.unit_mode, p.seg_cost);
   hipError_t e = pkvd::launch_decode(a, p.path, p.rows_per_tile, s.bf16, hs);
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PKVD_OK;
+}
+
+pkvd_decode_args fixed_args(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                            const pkvd_tensor* v_cache, const pkvd_tensor* block_tables,
+                            const pkvd_tensor* seq_lens_kv, float scale, int32_t q_len_per_req,
+                            int32_t window_left, const pkvd_tensor* sinks, pkvd_tensor* out,
+                            pkvd_tensor* lse) {
+  pkvd_decode_args x;
+  memset(&x, 0, sizeof x);
+  x.q = q;
+  x.k_cache = k_cache;
+  x.v_cache = v_cache;
+  x.block_tables = block_tables;
+  x.seq_lens_kv = seq_lens_kv;
+  x.qo_indptr = nullptr;
+  x.q_len = q_len_per_req;
+  x.mask = PKVD_MASK_CAUSAL;
+  x.window_left = window_left;
+  x.scale = scale;
+  x.out_scale = 1.0f;
+  x.sinks = sinks;
+  x.out = out;
+  x.lse = lse;
+  x.workspace = nullptr;
+  x.workspace_bytes = 0;
+  return x;
+}
+
+void plan_array(const Plan& p, int64_t* out, int n) {
+  const int64_t v[8] = {p.path,       p.rows_per_tile,   p.row_tiles,    p.num_waves,
+                        p.min_wave_blocks, p.workgroups, p.merge_kernel, p.unit_mode};
+  for (int i = 0; i < n && i < 8; ++i) out[i] = v[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkvd_version(void) { return "0.2.0"; }
+
+const char* pkvd_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkvd_status_string(int status) {
+  switch (status) {
+    case PKVD_OK: return "ok";
+    case PKVD_ERR_INVALID_ARG: return "invalid argument";
+    case PKVD_ERR_UNSUPPORTED: return "unsupported";
+    case PKVD_ERR_WORKSPACE: return "workspace missing, too small or not allocatable";
+    case PKVD_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+void pkvd_reload_tuning(void) {
+  std::lock_guard<std::mutex> lock(g_tuning_mutex);
+  g_tuning = read_tuning();
+  g_tuning_loaded = true;
+}
+
+int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                     const pkvd_tensor* block_tables, int32_t q_len_per_req, int32_t window_left,
+                     int64_t out[6]) {
+  g_last_error.clear();
+  Shapes s;
+  int st = check_shapes(q, k_cache, block_tables, nullptr, q_len_per_req, window_left, &s);
+  if (st != PKVD_OK) return st;
+  if (!out) return fail(PKVD_ERR_INVALID_ARG, "out is NULL");
+  Plan p;
+  st = plan_of(s, window_left, &p);
+  if (st != PKVD_OK) return st;
+  plan_array(p, out, 6);
+  return PKVD_OK;
+}
+
+int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                                const pkvd_tensor* block_tables, int32_t q_len_per_req,
+                                int32_t window_left, size_t* bytes) {
+  g_last_error.clear();
+  Shapes s;
+  int st = check_shapes(q, k_cache, block_tables, nullptr, q_len_per_req, window_left, &s);
+  if (st != PKVD_OK) return st;
+  if (!bytes) return fail(PKVD_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  st = plan_of(s, window_left, &p);
+  if (st != PKVD_OK) return st;
+  *bytes = p.ws_bytes;
+  return PKVD_OK;
+}
+
+int pkvd_decode_ex_plan(const pkvd_decode_args* args, int64_t plan[8], size_t* workspace_bytes) {
+  g_last_error.clear();
+  Shapes s;
+  int st = shapes_of(args, &s);
+  if (st != PKVD_OK) return st;
+  Plan p;
+  st = plan_of(s, args->window_left, &p);
+  if (st != PKVD_OK) return st;
+  if (plan) plan_array(p, plan, 8);
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return PKVD_OK;
+}
+
+int pkvd_reserve_workspace(size_t bytes) {
+  g_last_error.clear();
+  if (bytes == 0) return PKVD_OK;
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != PKVD_OK) return st;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  return grow_library_workspace(dev, bytes, nullptr, false);
+}
+
+int pkvd_set_workspace(void* dev_ptr, size_t bytes) {
+  g_last_error.clear();
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != PKVD_OK) return st;
+  if (dev_ptr && (reinterpret_cast<uintptr_t>(dev_ptr) & 255))
+    return fail(PKVD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (dev_ptr && bytes < 4096)
+    return fail(PKVD_ERR_INVALID_ARG, "workspace of %zu bytes is below the 4096-byte minimum", bytes);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace& w = g_ws[dev];
+  if (!dev_ptr) {
+    w.bound = nullptr;
+    w.bound_bytes = 0;
+    return PKVD_OK;
+  }
+  // the int area must start at zero; every call leaves it at zero again
+  hipError_t e = hipMemset(dev_ptr, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
+  w.bound = dev_ptr;
+  w.bound_bytes = bytes;
+  return PKVD_OK;
+}
+
+int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_tensor* v_cache,
+                const pkvd_tensor* block_tables, const pkvd_tensor* seq_lens_kv, float scale,
+                int32_t q_len_per_req, int32_t window_left, const pkvd_tensor* sinks,
+                pkvd_tensor* out, pkvd_tensor* lse, void* stream) {
+  const pkvd_decode_args x = fixed_args(q, k_cache, v_cache, block_tables, seq_lens_kv, scale,
+                                        q_len_per_req, window_left, sinks, out, lse);
+  if (out && q && out->dtype != q->dtype) {
+    g_last_error.clear();
+    return fail(PKVD_ERR_INVALID_ARG, "out must have q's dtype (pkvd_decode_ex takes others)");
+  }
+  return run_decode(&x, stream);
+}
+
+int pkvd_decode_ex(const pkvd_decode_args* args, void* stream) { return run_decode(args, stream); }
+
+int pkvd_schedule_stats(const pkvd_decode_args* args, const int32_t* seq_lens,
+                        const int32_t* qo_indptr, int64_t stats[8]) {
+  using namespace pkvd::dev;
+  g_last_error.clear();
+  Shapes s;
+  int st = shapes_of(args, &s);
+  if (st != PKVD_OK) return st;
+  if (!seq_lens || !stats || (s.packed && !qo_indptr))
+    return fail(PKVD_ERR_INVALID_ARG, "seq_lens, stats (and qo_indptr for packed rows) are required");
+  Plan p;
+  st = plan_of(s, args->window_left, &p);
+  if (st != PKVD_OK) return st;
+  pkvd::DecodeArgs a;
+  fill_args(args, s, p, &a);
+  a.qo = s.packed ? qo_indptr : nullptr;   // the host copy: the helpers below read it
+  const int B = (int)s.B;
+  // the block prefixes, as the kernel's prologue builds them
+  std::vector<int64_t> pref(B + 1), vpref(B + 1);
+  std::vector<int> nblk(B), units(B);
+  int64_t T = 0, TV = 0;
+  for (int b = 0; b < B; ++b) {
+    const int c0 = s.packed ? clamp_row(a, qo_indptr[b]) : 0;
+    const int c1 = s.packed ? clamp_row(a, qo_indptr[b + 1]) : 0;
+    req_blocks(a, b, seq_lens[b], c0, c1, nblk[b], units[b]);
+    pref[b] = T;
+    vpref[b] = TV;
+    T += (int64_t)nblk[b] * units[b];
+    TV += (int64_t)unit_vspan(a, nblk[b]) * units[b];
+  }
+  pref[B] = T;
+  vpref[B] = TV;
+  if (TV >= INT32_MAX) return fail(PKVD_ERR_UNSUPPORTED, "block space beyond int32");
+  const int NW = wave_count(a, (int)T);
+  const Slices sl = make_slices(a, (int)TV, NW);
+  // the real block at virtual block v: the request holding v is the last one
+  // whose virtual prefix is <= v (as the kernel's search finds it)
+  auto real_at = [&](int64_t v) -> int64_t {
+    if (v >= TV) return T;
+    const int b = (int)(std::upper_bound(vpref.begin(), vpref.begin() + B, v) - vpref.begin()) - 1;
+    return real_block(a, (int)pref[b], (int)vpref[b], nblk[b], (int)v);
+  };
+  std::vector<int64_t> lo(NW + 1);
+  int64_t errors = 0;
+  for (int w = 0; w <= NW; ++w) lo[w] = T ? real_at(slice_begin(sl, w)) : 0;
+  if (lo[0] != 0 || lo[NW] != T) ++errors;
+  for (int w = 0; w < NW; ++w)
+    if (lo[w] > lo[w + 1]) ++errors;
+  // every unit: the waves whose slices hold its blocks, and whether the
+  // merge's bookkeeping (unit_pieces, candidate_slot) names exactly those
+  int64_t live = 0, cut = 0, pieces = 0, max_pieces = 0;
+  for (int b = 0; b < B; ++b) {
+    if (nblk[b] == 0) continue;
+    for (int u = 0; u < units[b]; ++u) {
+      ++live;
+      const int64_t us = pref[b] + (int64_t)u * nblk[b], ue = us + nblk[b];
+      const int64_t vs = vpref[b] + (int64_t)u * unit_vspan(a, nblk[b]);
+      // first wave whose slice ends after us
+      int w = (int)(std::upper_bound(lo.begin(), lo.end(), us) - lo.begin()) - 1;
+      int n = 0;
+      std::vector<int> holders;
+      for (; w < NW && lo[w] < ue; ++w)
+        if (lo[w + 1] > us && lo[w + 1] > lo[w]) holders.push_back(w);
+      n = (int)holders.size();
+      if (n == 0) ++errors;   // a unit nobody streams
+      if (n > 1) {
+        ++cut;
+        pieces += n;
+        max_pieces = std::max<int64_t>(max_pieces, n);
+        const UnitPieces up = unit_pieces(sl, vs, a.seg_cost, nblk[b]);
+        std::vector<int> named;
+        for (int c = 0; c < up.n; ++c) {
+          bool written = false;
+          const int slot = candidate_slot(up, sl, vs, c, written);
+          if (!written) continue;
+          const int ww = up.w0 + c;
+          named.push_back(ww);
+          // side 0 exactly when the wave's slice starts inside this unit
+          if ((slot & 1) != (lo[ww] >= us ? 0 : 1)) ++errors;
+        }
+        if (named != holders) ++errors;
+      }
+    }
+  }
+  stats[0] = T;
+  stats[1] = NW;
+  stats[2] = live;
+  stats[3] = cut;
+  stats[4] = pieces;
+  stats[5] = max_pieces;
+  stats[6] = errors;
+  stats[7] = TV;
   return PKVD_OK;
 }
 

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "decode_args.h"
+#include "schedule.h"
 
 namespace pkvd {
 namespace dev {
@@ -182,218 +183,58 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return m == -INFINITY ? 0.f : fast_exp2(m - M);
 }
 
-// ---------------------------------------------------------------------------
-// key range of one request
-// ---------------------------------------------------------------------------
-// Keys some row of request b may see: [lo(row 0), n - 1], where row 0 has the
-// lowest diagonal n - Lq (Parameters / q_len_per_req) and the window keeps
-// window_left keys before the diagonal (Parameters / window_left).  The range
-// is cut into 16-key blocks aligned to the absolute key index; the waves'
-// slices are runs of these blocks.
-struct UnitRange {
-  int n;          // sequence length, clamped to the block table's capacity
-  int key_lo;     // first key some row sees
-  int first_blk;  // block holding key_lo
-  int nblk;       // blocks covering [key_lo, n)
-};
-
-__device__ __forceinline__ UnitRange unit_range_n(const DecodeArgs& a, int n_raw) {
-  UnitRange u;
-  const int cap = a.C * a.ps;
-  const int n = n_raw < 0 ? 0 : (n_raw > cap ? cap : n_raw);
-  u.n = n;
-  const int lo = (a.window_left < 0) ? 0 : n - a.Lq - a.window_left;
-  u.key_lo = lo < 0 ? 0 : lo;
-  if (u.key_lo >= n) {
-    u.first_blk = 0;
-    u.nblk = 0;
-  } else {
-    u.first_blk = u.key_lo / kBlockKeys;
-    u.nblk = (n - 1) / kBlockKeys - u.first_blk + 1;
-  }
-  return u;
+// From global memory (kernels that stage nothing).
+__device__ __forceinline__ ReqRows req_rows(const DecodeArgs& a, int b) {
+  if (!a.qo) return {b * a.Lq, a.Lq};
+  return rows_of(a, clamp_row(a, a.qo[b]), clamp_row(a, a.qo[b + 1]), b);
 }
-
-__device__ __forceinline__ UnitRange unit_range(const DecodeArgs& a, int b) {
-  return unit_range_n(a, a.seq_lens[b]);
-}
-
-// Final value of one output element: out = O / (L + e^{sink}) and, for d == 0,
-// lse = M + log2 L (keys only).  An empty row (L = 0) gives out = 0 and
-// lse = -inf.  M and L are in base-2 units (Parameters / sinks; Note / LSE
-// convention).
+// Final value of one output element: out = out_scale * O / (L + e^{sink})
+// (Parameters / sinks, bmm2_scale) and, for d == 0, lse = M + log2 L (keys
+// only).  An empty row (L = 0) gives out = 0 and lse = -inf.  M and L are in
+// base-2 units (Note / LSE convention).
 // `sink` is the row's sink logit (sinks[h], unscaled) when has_sink.
-template <bool BF16>
 __device__ __forceinline__ float final_value(bool has_sink, float sink, float M, float L,
-                                             float O) {
+                                             float O, float out_scale) {
   if (!(L > 0.f)) return 0.f;
   float Z = L;
   if (has_sink) Z += fast_exp2(sink * kLog2e - M);
-  return O / Z;
+  return O * (out_scale / Z);
 }
 
-// floor(n / d) for 0 <= n < 2^62, 0 < d < 2^62, and a quotient below 2^31.
-// The fp64 quotient has a relative error of about 2^-52 (the rounding of n
-// and of the division), so it is within one of the true quotient; integer
-// corrections make it exact.  About a tenth of the instructions of a generic
-// 64-bit integer division, which matters in the prologue every wave runs.
-__device__ __forceinline__ int64_t qdiv(int64_t n, int64_t d) {
-  int64_t q = (int)((double)n / (double)d);
-  int64_t r = n - q * d;
-  if (r < 0) { --q; r += d; }
-  if (r < 0) { --q; r += d; }
-  if (r >= d) { ++q; r -= d; }
-  if (r >= d) ++q;
-  return q;
-}
-
-// ---------------------------------------------------------------------------
-// balanced persistent schedule
-// ---------------------------------------------------------------------------
-// The work is the linear block space [0, T) of all units (request b, kv head,
-// row tile) in that order: request b owns blocks [pref[b], pref[b + 1]) and
-// each of its Hkv * row_tiles units holds nblk(b) consecutive blocks.  The
-// NW waves split it into consecutive slices, wave w's in proportion to its
-// weight.  Waves are numbered group by group, PER = ceil(NW / groups) per
-// group, and a group's wave i runs on SIMD i % 4 as the (i / 4)-th wave
-// there; W[s] is the weight of the waves at position s = min(i / 4, 3) on
-// their SIMD.  (Of two waves sharing a SIMD the first issues ahead of the
-// second and streams faster, so it may be given more blocks.)  Equal weights
-// give [w T / NW, (w + 1) T / NW): every wave streams the same number of
-// blocks (to within one) whatever the mix of sequence lengths.  The slice
-// sizes never depend on the lengths, only on T.
-struct Slices {
-  int T, NW;
-  int uniform;   // all weights in use equal: closed forms
-  int PER;       // waves per group
-  int W[4];
-  int64_t SP;    // total weight of one group's PER waves
-  int64_t S;     // total weight of the NW waves
-  int n_min;     // blocks of the shortest slice (a lower bound)
-};
-// Total weight of the first m waves of a group (0 <= m <= PER).
-__device__ __forceinline__ int64_t group_weight(const Slices& s, int m) {
-  int64_t acc = 0;
+// Stores N consecutive output elements (N even) at element offset `off` of
+// out in the call's output type (bf16 / fp16 rounded to nearest even, or
+// fp32).  The type is uniform over the launch.
+template <int N>
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t off, const float (&x)[N]) {
+  if (a.out_type == kOutF32) {
+    float* p = static_cast<float*>(a.out) + off;
+    if constexpr (N % 4 == 0) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int lo = r * kSimdsPerCu;
-    int n = m - lo;
-    n = n < 0 ? 0 : (r < 3 && n > kSimdsPerCu ? kSimdsPerCu : n);
-    acc += (int64_t)n * s.W[r];
-  }
-  return acc;
-}
-// Total weight of waves [0, w).
-__device__ __forceinline__ int64_t weight_before(const Slices& s, int w) {
-  const int full = w / s.PER;
-  return (int64_t)full * s.SP + group_weight(s, w - full * s.PER);
-}
-__device__ __forceinline__ Slices make_slices(const DecodeArgs& a, int T, int NW) {
-  Slices s;
-  s.T = T;
-  s.NW = NW;
-  const int groups = a.groups > 0 ? a.groups : 1;
-  s.PER = (NW + groups - 1) / groups;
-  int wmin = 1 << 30;
-  s.uniform = 1;
+      for (int u = 0; u < N / 4; ++u)
+        reinterpret_cast<float4*>(p)[u] = make_float4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]);
+    } else {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s.W[r] = a.slot_w[r];
-    if (r * kSimdsPerCu < s.PER) {
-      if (s.W[r] != s.W[0]) s.uniform = 0;
-      if (s.W[r] < wmin) wmin = s.W[r];
+      for (int u = 0; u < N / 2; ++u) reinterpret_cast<float2*>(p)[u] = make_float2(x[2 * u], x[2 * u + 1]);
     }
+    return;
   }
-  s.SP = group_weight(s, s.PER);
-  s.S = weight_before(s, NW);
-  s.n_min = s.uniform ? T / NW : (int)qdiv((int64_t)T * wmin, s.S);
-  return s;
-}
-// First block of wave w's slice (w <= NW).
-__device__ __forceinline__ int slice_begin(const Slices& s, int w) {
-  if (s.uniform) return (int)qdiv((int64_t)s.T * w, s.NW);
-  return (int)qdiv((int64_t)s.T * weight_before(s, w), s.S);
-}
-// The wave whose slice holds block x (0 <= x < T): the largest w with
-// slice_begin(w) <= x, i.e. with weight_before(w) <= ((x + 1) S - 1) / T.
-// That weight is inverted in closed form: whole groups first, then the
-// group's waves slot by slot (weights are positive).
-__device__ __forceinline__ int slice_of(const Slices& s, int64_t x) {
-  if (s.uniform) return (int)qdiv((x + 1) * s.NW - 1, s.T);
-  const int64_t target = qdiv((x + 1) * s.S - 1, s.T);
-  const int64_t full = qdiv(target, s.SP);
-  int64_t rem = target - full * s.SP;
-  int m = 0;
+  uint32_t w[N / 2];
+  if (a.out_type == kOutBf16) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int lo = r * kSimdsPerCu;
-    int cap = s.PER - lo;
-    cap = cap < 0 ? 0 : (r < 3 && cap > kSimdsPerCu ? kSimdsPerCu : cap);
-    int64_t n = rem / s.W[r];
-    n = n > cap ? cap : n;
-    if (m == lo) {   // earlier slots full: this slot's waves follow
-      m += (int)n;
-      rem -= n * s.W[r];
-    }
+    for (int u = 0; u < N / 2; ++u) w[u] = Fmt<true>::pack2(x[2 * u], x[2 * u + 1]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < N / 2; ++u) w[u] = Fmt<false>::pack2(x[2 * u], x[2 * u + 1]);
   }
-  const int64_t w = full * s.PER + m;
-  return (int)(w < s.NW - 1 ? w : s.NW - 1);
-}
-
-// Where the partial states of a cut unit are.  Wave w writes the partial
-// state of each unit its slice cuts into slot 2 w + side: side 0 for the
-// slice's first segment, 1 for its last (a slice cuts at most those two).
-// Slices are taken in the virtual block space: the unit starts at virtual
-// block vs and its real blocks sit at [vs + seg_cost, vs + seg_cost + nblk).
-// The candidates are the waves w0 .. w1 whose slices hold those blocks; wave
-// w's piece is its first segment exactly when its slice starts at or after
-// vs (a slice that starts among the unit's virtual blocks starts at the
-// unit's first real block).  Every candidate with a non-empty slice holds
-// real blocks of the unit and wrote a partial state; a unit with a single
-// non-empty candidate was whole in that slice and written directly.
-struct UnitPieces {
-  int w0;      // first wave holding a block of the unit
-  int n;       // candidates: waves w0 .. w0 + n - 1
-};
-__device__ __forceinline__ UnitPieces unit_pieces(const Slices& s, int64_t vs, int seg_cost,
-                                                  int nblk) {
-  UnitPieces p;
-  p.w0 = slice_of(s, vs + seg_cost);
-  p.n = slice_of(s, vs + seg_cost + nblk - 1) - p.w0 + 1;
-  return p;
-}
-// Slot of candidate c, and whether it holds a partial state of this call.
-__device__ __forceinline__ int candidate_slot(const UnitPieces& p, const Slices& s, int64_t vs,
-                                              int c, bool& written) {
-  const int w = p.w0 + c;
-  const int b0 = slice_begin(s, w);
-  written = b0 < slice_begin(s, w + 1);
-  return 2 * w + (b0 >= vs ? 0 : 1);
-}
-
-// Waves that take part: at most one per min_wave_blocks blocks, and >= 1.
-__device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
-  int nw = T / a.min_wave_blocks;
-  return nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
-}
-
-// Dynamic LDS of a workgroup of NT threads, in 32-bit words: the scan scratch (NT),
-// the prefix (B + 1) and the raw lengths (B).  Host (launch size) and kernel
-// (carve-up) both take the offsets from here.
-struct LdsLayout {
-  int scan, vscan, pref, vpref, nlen, sink, total;
-};
-// NS: sink logits staged in LDS (Hq when they are, else 0).
-__host__ __device__ inline LdsLayout lds_layout(int B, int NT, int NS) {
-  LdsLayout l;
-  l.scan = 0;
-  l.vscan = l.scan + NT;
-  l.pref = l.vscan + NT;
-  l.vpref = l.pref + B + 1;
-  l.nlen = l.vpref + B + 1;
-  l.sink = l.nlen + B;
-  l.total = l.sink + NS;
-  return l;
+  uint16_t* p = static_cast<uint16_t*>(a.out) + off;
+  if constexpr (N == 8) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+  } else if constexpr (N == 4) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < N / 2; ++u) reinterpret_cast<uint32_t*>(p)[u] = w[u];
+  }
 }
 
 // The slices divide a virtual block space in which every unit with blocks
@@ -403,39 +244,74 @@ __host__ __device__ inline LdsLayout lds_layout(int B, int NT, int NS) {
 // starts at real block pref[b] + u nblk(b) and virtual block
 // vpref[b] + u (nblk(b) + seg_cost); its real blocks sit at virtual offsets
 // seg_cost .. seg_cost + nblk(b) - 1.  With seg_cost = 0 both spaces agree.
+// Request b holds Hkv * tiles(b) units, tiles(b) = its row tiles.
 struct Prefix {
   int T;    // real blocks
   int TV;   // virtual blocks
 };
 
-// Builds pref[0..B], vpref[0..B], the raw lengths nlen[0..B-1] and (when
-// staged) the sink logits in LDS (one workgroup, ends with a barrier).  Requests with no visible key get
-// out = 0, lse = -inf here, written by workgroup b % gridDim.x.
-template <bool BF16, int NT>
+// The staged per-request facts, read back from LDS with a wave-uniform b.
+struct ReqInfo {
+  ReqRows rows;
+  UnitRange u;
+  int units;   // Hkv * row tiles
+};
+__device__ __forceinline__ ReqInfo req_info(const DecodeArgs& a, const int* s_nlen,
+                                            const int* s_qo, int b) {
+  ReqInfo r;
+  const int c0 = a.qo ? __builtin_amdgcn_readfirstlane(s_qo[b]) : 0;
+  const int c1 = a.qo ? __builtin_amdgcn_readfirstlane(s_qo[b + 1]) : 0;
+  r.rows = rows_of(a, c0, c1, b);
+  r.u = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[b]), r.rows.lq);
+  r.units = a.qo ? a.Hkv * tiles_of(a, r.rows.lq) : a.Hkv * a.row_tiles;
+  return r;
+}
+
+// Zeroes the output rows (and sets the LSE of) a request that has query rows
+// but no visible key: out = 0, lse = -inf.
+__device__ __forceinline__ void write_empty_request(const DecodeArgs& a, ReqRows rr) {
+  for (int r = rr.row0; r < rr.row0 + rr.lq; ++r)
+    for (int h = 0; h < a.Hq; ++h) {
+      const int64_t rowhead = (int64_t)r * a.Hq + h;
+      if (a.out_type == kOutF32) {
+        for (int d = 0; d < a.D; ++d) static_cast<float*>(a.out)[rowhead * a.D + d] = 0.f;
+      } else {
+        for (int d = 0; d < a.D; ++d) static_cast<uint16_t*>(a.out)[rowhead * a.D + d] = 0;
+      }
+      if (a.lse) a.lse[rowhead] = -INFINITY;
+    }
+}
+
+// Builds pref[0..B], vpref[0..B], the raw lengths nlen[0..B-1], (packed rows)
+// the clamped query offsets qo[0..B] and (when staged) the sink logits in
+// LDS (one workgroup, ends with a barrier).  Requests with query rows but no
+// visible key get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
+template <int NT>
 __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref, int* s_vpref,
-                                               int* s_nlen, int* s_scan, int* s_vscan,
+                                               int* s_nlen, int* s_qo, int* s_scan, int* s_vscan,
                                                float* s_sink) {
   const int B = a.B;
-  const int per_req = a.Hkv * a.row_tiles;
-  const int c = a.seg_cost;
   const int CH = (B + NT - 1) / NT;
   const int t = threadIdx.x;
   const int lo = min(B, t * CH), hi = min(B, lo + CH);
   int sum = 0, vsum = 0;
+  int c_next = (a.qo && lo < hi) ? clamp_row(a, a.qo[lo]) : 0;
   for (int b = lo; b < hi; ++b) {
     const int nraw = a.seq_lens[b];
     s_nlen[b] = nraw;
-    const int nb = unit_range_n(a, nraw).nblk;
-    sum += nb * per_req;
-    vsum += (nb > 0 ? nb + c : 0) * per_req;
-    if (nb == 0 && b % (int)gridDim.x == (int)blockIdx.x) {
-      for (int r = b * a.Lq; r < (b + 1) * a.Lq; ++r)
-        for (int h = 0; h < a.Hq; ++h) {
-          const int rowhead = r * a.Hq + h;
-          for (int d = 0; d < a.D; ++d) a.out[(int64_t)rowhead * a.D + d] = 0;
-          if (a.lse) a.lse[rowhead] = -INFINITY;
-        }
+    int c0 = 0, c1 = 0;
+    if (a.qo) {
+      c0 = c_next;
+      c1 = clamp_row(a, a.qo[b + 1]);
+      c_next = c1;
+      s_qo[b] = c0;
+      if (b + 1 == B) s_qo[B] = c1;
     }
+    int nb, units;
+    const ReqRows rr = req_blocks(a, b, nraw, c0, c1, nb, units);
+    sum += nb * units;
+    vsum += unit_vspan(a, nb) * units;
+    if (nb == 0 && rr.lq > 0 && b % (int)gridDim.x == (int)blockIdx.x) write_empty_request(a, rr);
   }
   if (a.sinks)
     for (int h = t; h < a.Hq; h += NT) s_sink[h] = a.sinks[h];
@@ -465,9 +341,10 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
   for (int b = lo; b < hi; ++b) {
     s_pref[b] = excl;
     s_vpref[b] = vexcl;
-    const int nb = unit_range_n(a, s_nlen[b]).nblk;
-    excl += nb * per_req;
-    vexcl += (nb > 0 ? nb + c : 0) * per_req;
+    int nb, units;   // this thread's own LDS writes: no barrier needed
+    req_blocks(a, b, s_nlen[b], a.qo ? s_qo[b] : 0, a.qo ? s_qo[b + 1] : 0, nb, units);
+    excl += nb * units;
+    vexcl += unit_vspan(a, nb) * units;
   }
   if (t == NT - 1) {
     s_pref[B] = base + x;
@@ -507,6 +384,7 @@ __device__ __forceinline__ int find_request(const int* s_pref, int B, int pos) {
 struct Segment {
   int b, kvh, tile;
   UnitRange u;
+  int row0, lq, R;           // the request's query rows, and R = g * lq live rows
   int blk_begin, blk_end;    // absolute 16-key blocks [blk_begin, blk_end)
   int ustart, uend;          // the unit's linear block range (the block space fits int32)
   int vstart;                // the unit's first virtual block
@@ -515,23 +393,28 @@ struct Segment {
 };
 
 __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
-                                          const int* s_vpref, const int* s_nlen, int pos,
-                                          int wave_lo, int wave_hi) {
+                                          const int* s_vpref, const int* s_nlen, const int* s_qo,
+                                          int pos, int wave_lo, int wave_hi) {
   Segment g;
   g.b = find_request(s_pref, a.B, pos);
-  g.u = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[g.b]));
+  const ReqInfo ri = req_info(a, s_nlen, s_qo, g.b);
+  g.u = ri.u;
+  g.row0 = ri.rows.row0;
+  g.lq = ri.rows.lq;
+  g.R = a.g * g.lq;
   const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[g.b]);
   const int vpref_b = __builtin_amdgcn_readfirstlane(s_vpref[g.b]);
   const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
   const int off = pos - pref_b;
-  const int per_req = a.Hkv * a.row_tiles;
+  const int per_req = ri.units > 0 ? ri.units : 1;
+  const int tiles = per_req / a.Hkv > 0 ? per_req / a.Hkv : 1;
   int uidx = off / nb;
   uidx = uidx < 0 ? 0 : (uidx >= per_req ? per_req - 1 : uidx);
-  g.kvh = uidx / a.row_tiles;
-  g.tile = uidx - g.kvh * a.row_tiles;
+  g.kvh = uidx / tiles;
+  g.tile = uidx - g.kvh * tiles;
   g.ustart = pref_b + uidx * nb;
   g.uend = g.ustart + nb;
-  g.vstart = vpref_b + uidx * (nb + a.seg_cost);
+  g.vstart = vpref_b + uidx * unit_vspan(a, nb);
   const int seg_end = wave_hi < g.uend ? wave_hi : g.uend;
   g.blk_begin = g.u.first_blk + (pos - g.ustart);
   g.blk_end = g.blk_begin + (seg_end - pos);
@@ -540,18 +423,15 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
   return g;
 }
 
-// The real block at virtual block v (0 <= v <= TV): the unit's first real
-// block for its virtual blocks, T at the end.
+// The real block at virtual block v (0 <= v <= TV), T at the end (see
+// real_block).
 __device__ __forceinline__ int real_of(const DecodeArgs& a, const int* s_pref, const int* s_vpref,
-                                       const int* s_nlen, const Prefix& p, int v) {
+                                       const int* s_nlen, const int* s_qo, const Prefix& p, int v) {
   if (v >= p.TV) return p.T;
   const int b = find_request(s_vpref, a.B, v);   // a request with blocks
-  const int nb = unit_range_n(a, __builtin_amdgcn_readfirstlane(s_nlen[b])).nblk;
-  const int vu = nb + a.seg_cost;
-  const int off = v - __builtin_amdgcn_readfirstlane(s_vpref[b]);
-  const int ul = off / vu;
-  const int o = off - ul * vu - a.seg_cost;
-  return __builtin_amdgcn_readfirstlane(s_pref[b]) + ul * nb + (o > 0 ? o : 0);
+  const int nb = req_info(a, s_nlen, s_qo, b).u.nblk;
+  return real_block(a, __builtin_amdgcn_readfirstlane(s_pref[b]),
+                    __builtin_amdgcn_readfirstlane(s_vpref[b]), nb, v);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,12 @@
+// decode_inst_d128_bf16.hip -- the decode and merge kernels for head_dim 128,
+// bfloat16 inputs (one translation unit per head_dim and element type, so the
+// instantiations compile in parallel).
+#include "decode_kernel.h"
+
+namespace pkvd {
+
+KernelPair kernels_d128_bf16(int path, int rows_per_tile, bool pow2) {
+  return dev::select_kernels<128, true>(path, rows_per_tile, pow2);
+}
+
+}  // namespace pkvd

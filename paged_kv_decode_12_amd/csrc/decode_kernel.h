@@ -1,4 +1,6 @@
-// decode_kernel.hip -- the persistent paged-KV decode kernel and its launch.
+// decode_kernel.h -- the persistent paged-KV decode kernel and the merge
+// kernel (templates; instantiated per head_dim and element type by the
+// decode_inst_*.hip files, launched from decode_launch.hip).
 //
 // Operation: flashinfer.cudnn.cudnn_batch_decode_with_kv_cache (Parameters,
 // Note / LSE convention).  A unit of work is (request b, kv head, row tile);
@@ -49,17 +51,17 @@
 //  * the page ids of the next 128 block-table columns sit in two registers
 //    (one column per lane), read with readlane / ds_bpermute;
 //  * at a segment's end the KPS streams merge by DPP and lane-pair swaps.
+#pragma once
+
 #include "engine_mfma.h"
 #include "engine_valu.h"
 
 namespace pkvd {
-namespace {
-
-using namespace dev;
+namespace dev {
 
 // Writes one output item (N = 8 or 4 consecutive dims from d0) and, from the
 // row's lead lane, its LSE.
-template <int D, int N, bool BF16>
+template <int D, int N>
 __device__ __forceinline__ void store_item(const DecodeArgs& a, const float* s_sink,
                                            int64_t rowhead, int qhead, int d0, bool lead, float M,
                                            float L, const float (&O)[8]) {
@@ -68,15 +70,10 @@ __device__ __forceinline__ void store_item(const DecodeArgs& a, const float* s_s
   const bool has_sink = a.sinks != nullptr;
   float sink = 0.f;
   if (has_sink) sink = s_sink[qhead];
-  uint32_t w[4];
+  float x[N];
 #pragma unroll
-  for (int u = 0; u < N / 2; ++u)
-    w[u] = Fmt<BF16>::pack2(final_value<BF16>(has_sink, sink, M, L, O[2 * u]),
-                            final_value<BF16>(has_sink, sink, M, L, O[2 * u + 1]));
-  if constexpr (N == 8)
-    *reinterpret_cast<u32x4*>(a.out + (int64_t)rowhead * D + d0) = u32x4{w[0], w[1], w[2], w[3]};
-  else
-    *reinterpret_cast<uint2*>(a.out + (int64_t)rowhead * D + d0) = make_uint2(w[0], w[1]);
+  for (int e = 0; e < N; ++e) x[e] = final_value(has_sink, sink, M, L, O[e], a.out_scale);
+  store_out<N>(a, (int64_t)rowhead * D + d0, x);
   if (a.lse && lead) a.lse[rowhead] = L > 0.f ? M + log2f(L) : -INFINITY;
 }
 
@@ -101,16 +98,18 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
 // are taken 64 at a time (lane c works out whether candidate c wrote a
 // partial state); the written ones are read kDepth at a time in block order
 // (every item's loads in flight), raising the running maximum once per
-// group.
-template <class Eng, int D, bool BF16>
+// group.  rr: the request's query rows; only rows below R = g * lq hold
+// partial states (the rest of a 16-row MFMA tile is padding).
+template <class Eng, int D>
 __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const float* s_sink,
                                            const Slices& sl_, int unit, int vs, int nblk,
-                                           const typename Eng::Lane& ln, int lane, int R) {
+                                           ReqRows rows, const typename Eng::Lane& ln, int lane) {
   constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
   const int per_req = a.Hkv * a.row_tiles;
   const int b = unit / per_req, uidx = unit - b * per_req;
   const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
+  const int R = a.g * rows.lq;
   const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, nblk);
   int rr[NI], dd[NI];
 #pragma unroll
@@ -143,7 +142,8 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const float* s_s
         const int sl = on[u] ? __builtin_amdgcn_readlane(slot, q) : sl0;
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
-          const int r = rr[it] < RT ? rr[it] : 0;
+          // padding rows read row 0's values (loaded by other lanes anyway)
+          const int r = rr[it] < RT && tile * RT + rr[it] < R ? rr[it] : 0;
           lv[u][it] = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
 #pragma unroll
           for (int e = 0; e < N; ++e)
@@ -176,12 +176,12 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, const float* s_s
     const int r = rr[it], row = tile * RT + r;
     if (!(r < RT && row < R)) continue;
     const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
-    store_item<D, N, BF16>(a, s_sink, ((int64_t)b * a.Lq + ti) * a.Hq + qhead, qhead, dd[it],
-                           dd[it] == 0, Mx[it], W[it], acc[it]);
+    store_item<D, N>(a, s_sink, ((int64_t)rows.row0 + ti) * a.Hq + qhead, qhead, dd[it],
+                     dd[it] == 0, Mx[it], W[it], acc[it]);
   }
 }
 
-template <class Eng, int D, bool BF16, bool PAGE_POW2, int PF, int WPE>
+template <class Eng, int D, bool PAGE_POW2, int PF, int WPE>
 __global__ __launch_bounds__(64 * kSimdsPerCu * WPE) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_kernel(const DecodeArgs a) {
   // one workgroup per CU: WPE waves on each of its SIMDs
@@ -191,12 +191,13 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int kWindow = 128;                        // block-table columns per chunk
   constexpr int GPB = Eng::kGroupsPerBlock, KPG = Eng::kKeysPerGroup;
   extern __shared__ int lds[];
-  const LdsLayout L = lds_layout(a.B, kThreads, a.sinks ? a.Hq : 0);
+  const LdsLayout L = lds_layout(a.B, kThreads, a.sinks ? a.Hq : 0, a.qo != nullptr);
   int* s_scan = lds + L.scan;
   int* s_vscan = lds + L.vscan;
   int* s_pref = lds + L.pref;
   int* s_vpref = lds + L.vpref;
   int* s_nlen = lds + L.nlen;
+  int* s_qo = lds + L.qo;
   float* s_sink = reinterpret_cast<float*>(lds + L.sink);
 
   const int lane = threadIdx.x & 63;
@@ -206,7 +207,7 @@ void decode_kernel(const DecodeArgs a) {
 #ifdef PKVD_TRACE
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 #endif
-  Prefix pf = build_prefix<BF16, kThreads>(a, s_pref, s_vpref, s_nlen, s_scan, s_vscan, s_sink);
+  Prefix pf = build_prefix<kThreads>(a, s_pref, s_vpref, s_nlen, s_qo, s_scan, s_vscan, s_sink);
   pf.T = uniform(pf.T);
   pf.TV = uniform(pf.TV);
   const int T = pf.T;
@@ -226,12 +227,11 @@ void decode_kernel(const DecodeArgs a) {
   const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
   // slices of the virtual block space, mapped back to real blocks
   const Slices sl_ = make_slices(a, pf.TV, NW);
-  const int lo = T ? real_of(a, s_pref, s_vpref, s_nlen, pf, slice_begin(sl_, gw)) : 0;
-  const int hi = T ? real_of(a, s_pref, s_vpref, s_nlen, pf, slice_begin(sl_, gw + 1)) : 0;
+  const int lo = T ? real_of(a, s_pref, s_vpref, s_nlen, s_qo, pf, slice_begin(sl_, gw)) : 0;
+  const int hi = T ? real_of(a, s_pref, s_vpref, s_nlen, s_qo, pf, slice_begin(sl_, gw + 1)) : 0;
   if (T == 0 || gw >= NW || lo >= hi) return;   // no slice
   PKVD_COUNT(a, gw, 0, t_start);
   PKVD_COUNT(a, gw, 1, t_prefix);
-  const int R = a.g * a.Lq;
   const int ps_shift = PAGE_POW2 ? __builtin_ctz(a.ps) : 0;
   // blocks per chunk: (blocks * 16 - 1) / ps + 2 <= kWindow columns
   const int chunk_blocks = max(1, ((kWindow - 2) * a.ps + 1) / kBlockKeys);
@@ -275,7 +275,7 @@ void decode_kernel(const DecodeArgs a) {
     if (!c.last) {
       n = make_chunk(c.sg, c.ce);
     } else if (pos < hi) {
-      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, pos, lo, hi);
+      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, s_qo, pos, lo, hi);
       n = make_chunk(sg, sg.blk_begin);
     }
     return n;
@@ -303,7 +303,7 @@ void decode_kernel(const DecodeArgs a) {
     int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_vs[2] = {0, 0}, pend_nb[2] = {0, 0};
     Chunk cur;
     {
-      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, lo, lo, hi);
+      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, s_qo, lo, lo, hi);
       cur = make_chunk(sg, sg.blk_begin);
     }
     PageWindow pw = fetch_pages(cur);
@@ -328,9 +328,9 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) load_group(buf[s], cur, pw, s);
     PKVD_STAMP(a, gw, 4);
-    Eng::fetch_q(a, cur.sg, R, ln, qr);
-    if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qn);
-    Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+    Eng::fetch_q(a, cur.sg, ln, qr);
+    if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, ln, qn);
+    Eng::reset(a, cur.sg, ln, st, max_lo, min_hi);
     PKVD_STAMP(a, gw, 2);
 
     for (;;) {
@@ -382,14 +382,12 @@ void decode_kernel(const DecodeArgs a) {
           float M, Lsum, O[8];
           const bool ok = Eng::item(st, ln, it, r, d0, M, Lsum, O);
           const int row = sg.tile * RT + r;
+          if (!(ok && row < sg.R)) continue;   // padding rows are neither stored nor kept
           if (sg.whole) {
-            if (ok && row < R) {
-              const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
-              store_item<D, Eng::kItemDims, BF16>(a, s_sink,
-                                                  ((int64_t)sg.b * a.Lq + ti) * a.Hq + qhead,
-                                                  qhead, d0, d0 == 0, M, Lsum, O);
-            }
-          } else if (ok) {
+            const int ti = row / a.g, qhead = sg.kvh * a.g + (row - ti * a.g);
+            store_item<D, Eng::kItemDims>(a, s_sink, ((int64_t)sg.row0 + ti) * a.Hq + qhead,
+                                          qhead, d0, d0 == 0, M, Lsum, O);
+          } else {
             store_partial<Eng, D>(a, slot, ln, r, d0, M, Lsum, O);
           }
         }
@@ -407,29 +405,44 @@ void decode_kernel(const DecodeArgs a) {
       if (!nxt.valid) break;
       cur = nxt;
       pw = pwn;
-      if (cur.first) Eng::reset(a, cur.sg, R, ln, st, max_lo, min_hi);
+      if (cur.first) Eng::reset(a, cur.sg, ln, st, max_lo, min_hi);
       nxt = next_chunk(cur);
       if (nxt.valid) pwn = fetch_pages(nxt);
-      if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, R, ln, qn);
+      if (cur.last && nxt.valid) Eng::fetch_q(a, nxt.sg, ln, qn);
     }
     PKVD_STAMP(a, gw, 6);
 
-    if (!a.merge_kernel) {
-      // tickets of the cut units: blocks delivered, after this slice's partial
-      // stores have completed.  The wave that completes a unit merges it.
+    if (!a.merge_kernel && (pend_unit[0] >= 0 || pend_unit[1] >= 0)) {
+      // Tickets of the cut units: blocks delivered, once this slice's
+      // partial states are stored.  The wave whose ticket completes a unit
+      // merges it.  Ordering (agent scope): every partial-state store is an
+      // agent-scope atomic store, which on this hardware writes through to
+      // device-coherent memory; the wave waits until all of its stores have
+      // completed (vmcnt 0, with compiler barriers on both sides so that no
+      // memory access moves across the wait) before lane 0 adds to the
+      // counter.  That is the part of a release fence these stores need; the
+      // fence itself would also write back this XCD's whole L2 (non-atomic
+      // data the merge never reads), which measured 19 us per call on the
+      // 64-request Llama-3-8B batch (128 vs 110 us).  The completing wave
+      // executes an agent-scope acquire fence before its first partial-state
+      // load (measured free), and reads with agent-scope atomic loads.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       int prev[2] = {0, 0};
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         if (pend_unit[k] >= 0 && lane == 0)
-          prev[k] = atomicAdd(&a.counters[pend_unit[k]], pend_n[k]);
+          prev[k] = __hip_atomic_fetch_add(&a.counters[pend_unit[k]], pend_n[k], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         if (pend_unit[k] < 0) continue;
         if (uniform(prev[k]) + pend_n[k] != pend_nb[k]) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-        merge_unit<Eng, D, BF16>(a, s_sink, sl_, pend_unit[k], pend_vs[k], pend_nb[k], ln, lane,
-                                 R);
+        const ReqRows rows = req_info(a, s_nlen, s_qo, pend_unit[k] / (a.Hkv * a.row_tiles)).rows;
+        merge_unit<Eng, D>(a, s_sink, sl_, pend_unit[k], pend_vs[k], pend_nb[k], rows, ln, lane);
       }
     }
   }
@@ -469,7 +482,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <class Eng, int D, bool BF16>
+template <class Eng, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a) {
   constexpr int RT = Eng::kRows, NDL = D / 64;   // dims per lane
   const int lane = threadIdx.x & 63;
@@ -480,14 +493,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (b >= a.B) return;
   const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
   const int row = tile * RT + r;
-  if (row >= a.g * a.Lq) return;
-  const UnitRange u = unit_range(a, b);
+  const ReqRows rows = req_rows(a, b);
+  if (row >= a.g * rows.lq) return;   // a padding row, or a tile the request does not have
+  const UnitRange u = unit_range_n(a, a.seq_lens[b], rows.lq);
   if (u.nblk == 0) return;
+  // the unit's place among its request's units (kv head major, then tiles)
+  const int ub = a.qo ? kvh * tiles_of(a, rows.lq) + tile : uidx;
   const int T = a.ws_pref[a.B];
   const int NW = wave_count(a, T);
   const Slices sl_ = make_slices(a, a.ws_vpref[a.B], NW);
-  const int64_t us = a.ws_pref[b] + (int64_t)uidx * u.nblk, ue = us + u.nblk;
-  const int64_t vs = a.ws_vpref[b] + (int64_t)uidx * (u.nblk + a.seg_cost);
+  const int64_t us = a.ws_pref[b] + (int64_t)ub * u.nblk, ue = us + u.nblk;
+  const int64_t vs = a.ws_vpref[b] + (int64_t)ub * unit_vspan(a, u.nblk);
   if (ue > T) return;
   const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, u.nblk);
   if (up.n == 1) return;   // inside one slice: written whole by the decode kernel
@@ -544,16 +560,20 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   }
   if (written < 2) return;   // whole in one slice: written by the decode kernel
   const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
-  const int64_t rowhead = ((int64_t)b * a.Lq + ti) * a.Hq + qhead;
+  const int64_t rowhead = ((int64_t)rows.row0 + ti) * a.Hq + qhead;
   const bool has_sink = a.sinks != nullptr;
   const float sink = has_sink ? a.sinks[qhead] : 0.f;
   // acc / W is the merged normalised output; final_value divides by W + sink
+  float x[NDL];
+#pragma unroll
+  for (int e = 0; e < NDL; ++e) x[e] = final_value(has_sink, sink, M, W, acc[e], a.out_scale);
   if constexpr (NDL == 2) {
-    *reinterpret_cast<uint32_t*>(a.out + rowhead * D + 2 * lane) =
-        Fmt<BF16>::pack2(final_value<BF16>(has_sink, sink, M, W, acc[0]),
-                         final_value<BF16>(has_sink, sink, M, W, acc[1]));
+    store_out<2>(a, rowhead * D + 2 * lane, x);
   } else {
-    a.out[rowhead * D + lane] = Fmt<BF16>::encode(final_value<BF16>(has_sink, sink, M, W, acc[0]));
+    const int64_t off = rowhead * D + lane;
+    if (a.out_type == kOutF32) static_cast<float*>(a.out)[off] = x[0];
+    else if (a.out_type == kOutBf16) static_cast<uint16_t*>(a.out)[off] = Fmt<true>::encode(x[0]);
+    else static_cast<uint16_t*>(a.out)[off] = Fmt<false>::encode(x[0]);
   }
   if (a.lse && lane == 0) a.lse[rowhead] = W > 0.f ? M + log2f(W) : -INFINITY;
 }
@@ -585,8 +605,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #define PKVD_WPE16_D64 2
 #endif
 
-using KernelFn = void (*)(DecodeArgs);
-
 template <int RT>
 constexpr int valu_pf() { return RT == 4 ? PKVD_PF4 : PKVD_PF8; }
 template <int RT>
@@ -597,100 +615,27 @@ constexpr int mfma_pf() { return D == 64 ? PKVD_PF16_D64 : PKVD_PF16; }
 template <int D>
 constexpr int mfma_wpe() { return D == 64 ? PKVD_WPE16_D64 : PKVD_WPE16; }
 
-template <int D, int RT, bool BF16, bool POW2>
-KernelFn valu_kernel() {
-  return &decode_kernel<ValuEngine<D, RT, BF16>, D, BF16, POW2, valu_pf<RT>(), valu_wpe<RT>()>;
-}
-template <int D, bool BF16, bool POW2>
-KernelFn mfma_kernel() {
-  return &decode_kernel<MfmaEngine<D, BF16>, D, BF16, POW2, mfma_pf<D>(), mfma_wpe<D>()>;
-}
-
-KernelFn select(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2) {
-#define PKVD_SEL(D, BF, P2)                                                          \
-  if (head_dim == D && bf16 == BF && pow2 == P2) {                                  \
-    if (path == kPathMfma) return rows_per_tile == 16 ? mfma_kernel<D, BF, P2>() : nullptr; \
-    if (rows_per_tile == 4) return valu_kernel<D, 4, BF, P2>();                     \
-    if (rows_per_tile == 8) return valu_kernel<D, 8, BF, P2>();                     \
-    return nullptr;                                                                 \
+// The decode and merge kernels of one (head_dim, element type) for a path
+// and tile height (nullptr where none is built).
+template <int D, bool BF16>
+KernelPair select_kernels(int path, int rows_per_tile, bool pow2) {
+  KernelPair k{nullptr, nullptr};
+  if (path == kPathMfma) {
+    if (rows_per_tile != 16) return k;
+    k.decode = pow2 ? &decode_kernel<MfmaEngine<D, BF16>, D, true, mfma_pf<D>(), mfma_wpe<D>()>
+                    : &decode_kernel<MfmaEngine<D, BF16>, D, false, mfma_pf<D>(), mfma_wpe<D>()>;
+    k.merge = &merge_kernel<MfmaEngine<D, BF16>, D>;
+  } else if (rows_per_tile == 4) {
+    k.decode = pow2 ? &decode_kernel<ValuEngine<D, 4, BF16>, D, true, valu_pf<4>(), valu_wpe<4>()>
+                    : &decode_kernel<ValuEngine<D, 4, BF16>, D, false, valu_pf<4>(), valu_wpe<4>()>;
+    k.merge = &merge_kernel<ValuEngine<D, 4, BF16>, D>;
+  } else if (rows_per_tile == 8) {
+    k.decode = pow2 ? &decode_kernel<ValuEngine<D, 8, BF16>, D, true, valu_pf<8>(), valu_wpe<8>()>
+                    : &decode_kernel<ValuEngine<D, 8, BF16>, D, false, valu_pf<8>(), valu_wpe<8>()>;
+    k.merge = &merge_kernel<ValuEngine<D, 8, BF16>, D>;
   }
-  PKVD_SEL(128, true, true)
-  PKVD_SEL(128, true, false)
-  PKVD_SEL(128, false, true)
-  PKVD_SEL(128, false, false)
-  PKVD_SEL(64, true, true)
-  PKVD_SEL(64, true, false)
-  PKVD_SEL(64, false, true)
-  PKVD_SEL(64, false, false)
-#undef PKVD_SEL
-  return nullptr;
+  return k;
 }
 
-using MergeFn = void (*)(DecodeArgs);
-
-MergeFn select_merge(int path, int rows_per_tile, int head_dim, bool bf16) {
-#define PKVD_SELM(D, BF)                                                               \
-  if (head_dim == D && bf16 == BF) {                                                  \
-    if (path == kPathMfma) return rows_per_tile == 16 ? &merge_kernel<MfmaEngine<D, BF>, D, BF> : nullptr; \
-    if (rows_per_tile == 4) return &merge_kernel<ValuEngine<D, 4, BF>, D, BF>;        \
-    if (rows_per_tile == 8) return &merge_kernel<ValuEngine<D, 8, BF>, D, BF>;        \
-    return nullptr;                                                                   \
-  }
-  PKVD_SELM(128, true)
-  PKVD_SELM(128, false)
-  PKVD_SELM(64, true)
-  PKVD_SELM(64, false)
-#undef PKVD_SELM
-  return nullptr;
-}
-
-bool page_pow2(int ps) { return ps >= kBlockKeys && (ps & (ps - 1)) == 0; }
-
-}  // namespace
-
-int decode_group_waves(int path, int rows_per_tile, int head_dim) {
-  int wpe = 0;
-  if (path == kPathMfma) wpe = rows_per_tile != 16 ? 0 : (head_dim == 64 ? mfma_wpe<64>() : mfma_wpe<128>());
-  else if (rows_per_tile == 4) wpe = valu_wpe<4>();
-  else if (rows_per_tile == 8) wpe = valu_wpe<8>();
-  return kSimdsPerCu * wpe;
-}
-
-size_t decode_lds_bytes(int B, int threads, int sinks) {
-  return sizeof(int) * (size_t)lds_layout(B, threads, sinks).total;
-}
-
-int decode_blocks_per_cu(int path, int rows_per_tile, int head_dim, bool bf16, bool pow2,
-                         size_t lds_bytes) {
-  KernelFn k = select(path, rows_per_tile, head_dim, bf16, pow2);
-  const int threads = 64 * decode_group_waves(path, rows_per_tile, head_dim);
-  if (!k || !threads) return 0;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads,
-                                                   lds_bytes) != hipSuccess)
-    return 0;
-  return n;
-}
-
-hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,
-                         hipStream_t stream) {
-  KernelFn k = select(path, rows_per_tile, a.D, bf16, page_pow2(a.ps));
-  if (!k) return hipErrorInvalidValue;
-  const int waves = decode_group_waves(path, rows_per_tile, a.D);
-  if (!waves || (int64_t)a.groups * waves < a.num_waves) return hipErrorInvalidValue;
-  const dim3 grid(a.groups);
-  hipLaunchKernelGGL(k, grid, dim3(64 * waves), decode_lds_bytes(a.B, 64 * waves,
-                                                                a.sinks ? a.Hq : 0),
-                     stream, a);
-  if (!a.merge_kernel) return hipGetLastError();
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  MergeFn m = select_merge(path, rows_per_tile, a.D, bf16);
-  if (!m) return hipErrorInvalidValue;
-  const int pairs = a.B * a.Hkv * a.row_tiles * rows_per_tile;   // (unit, row) pairs
-  hipLaunchKernelGGL(m, dim3((pairs + kMergeWaves - 1) / kMergeWaves), dim3(64 * kMergeWaves), 0,
-                     stream, a);
-  return hipGetLastError();
-}
-
+}  // namespace dev
 }  // namespace pkvd

@@ -123,13 +123,13 @@ struct MfmaEngine {
 
   static __device__ __forceinline__ Lane lane_of(int lane) { return {lane & 15, lane >> 4, lane}; }
 
-  static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg, int R,
+  static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg,
                                                  const Lane& ln, Q& q) {
     const int rr = sg.tile * kRows + ln.j;
-    const bool live = rr < R;
+    const bool live = rr < sg.R;
     const int i = live ? rr / a.g : 0;
     const int hl = live ? rr - i * a.g : 0;
-    const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
+    const uint16_t* qp = a.q + (int64_t)(sg.row0 + i) * a.q_sr +
                          (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.q * 8;
 #pragma unroll
     // padding lanes (rows past R) load row 0 of the unit, which is live,
@@ -138,20 +138,22 @@ struct MfmaEngine {
     for (int c = 0; c < NC; ++c) q.c[c] = load16(qp + c * 32);
   }
 
-  static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg, int R,
+  // Row i of the request sees [max(0, p_i - window_left), p_i] (causal) or
+  // [max(0, p_i - window_left), n - 1] (dense), p_i = n - lq + i.
+  static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg,
                                                const Lane& ln, State& st, int& max_lo,
                                                int& min_hi) {
     // the tile's live rows: tokens (tile*16) / g .. min(R - 1, tile*16 + 15) / g
-    const int r0 = sg.tile * kRows, r1 = min(R, r0 + kRows) - 1;
+    const int r0 = sg.tile * kRows, r1 = min(sg.R, r0 + kRows) - 1;
     const int i0 = r0 / a.g, i1 = r1 / a.g;
-    const int diag0 = sg.u.n - a.Lq + i0, diag1 = sg.u.n - a.Lq + i1;
-    min_hi = min(sg.u.n - 1, diag0);
+    const int diag0 = sg.u.n - sg.lq + i0, diag1 = sg.u.n - sg.lq + i1;
+    min_hi = min(sg.u.n - 1, a.causal ? diag0 : sg.u.n - 1);
     max_lo = max(sg.u.key_lo, a.window_left < 0 ? 0 : max(diag1 - a.window_left, 0));
     const int rr = r0 + ln.j;
-    const bool live = rr < R;
-    const int diag = sg.u.n - a.Lq + (live ? rr / a.g : 0);
+    const bool live = rr < sg.R;
+    const int diag = sg.u.n - sg.lq + (live ? rr / a.g : 0);
     st.lo = live ? max(a.window_left < 0 ? 0 : diag - a.window_left, 0) : 1;
-    st.hi = live ? diag : 0;
+    st.hi = live ? (a.causal ? diag : sg.u.n - 1) : 0;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll

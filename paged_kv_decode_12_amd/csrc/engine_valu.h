@@ -229,15 +229,15 @@ struct ValuEngine {
 
   // Q rows of a tile (rr = tile * RT + r -> token rr / g, head rr % g): the
   // lane's 16-byte piece of each row
-  static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg, int R,
+  static __device__ __forceinline__ void fetch_q(const DecodeArgs& a, const Segment& sg,
                                                  const Lane& ln, Q& q) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int rr = sg.tile * RT + r;
-      const bool live = rr < R;
+      const bool live = rr < sg.R;
       const int i = live ? rr / a.g : 0;
       const int hl = live ? rr - i * a.g : 0;
-      const uint16_t* qp = a.q + (int64_t)(sg.b * a.Lq + i) * a.q_sr +
+      const uint16_t* qp = a.q + (int64_t)(sg.row0 + i) * a.q_sr +
                            (int64_t)(sg.kvh * a.g + hl) * a.q_sh + ln.part * 8;
       // a padding row (past R) loads row 0 of the unit, which is live,
       // rather than selecting zeros: a select on the loaded value would make
@@ -247,22 +247,25 @@ struct ValuEngine {
   }
 
   // Reset for a new segment; returns the key range every row sees fully
-  // ([max_lo, min_hi]: groups inside it need no mask).
-  static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg, int R,
+  // ([max_lo, min_hi]: groups inside it need no mask).  Row i of the request
+  // sees [max(0, p_i - window_left), p_i] (causal) or [max(0, p_i -
+  // window_left), n - 1] (dense), p_i = n - lq + i.
+  static __device__ __forceinline__ void reset(const DecodeArgs& a, const Segment& sg,
                                                const Lane&, State& st, int& max_lo, int& min_hi) {
     max_lo = sg.u.key_lo;
     min_hi = sg.u.n - 1;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int rr = sg.tile * RT + r;
-      const bool live = rr < R;
-      const int diag = sg.u.n - a.Lq + (live ? rr / a.g : 0);
+      const bool live = rr < sg.R;
+      const int diag = sg.u.n - sg.lq + (live ? rr / a.g : 0);
       const int rlo = max(a.window_left < 0 ? 0 : diag - a.window_left, 0);
+      const int rhi = a.causal ? diag : sg.u.n - 1;
       st.lo[r] = live ? rlo : 1;     // dead rows see nothing
-      st.hi[r] = live ? diag : 0;
+      st.hi[r] = live ? rhi : 0;
       if (live) {
         max_lo = max(max_lo, rlo);
-        min_hi = min(min_hi, diag);
+        min_hi = min(min_hi, rhi);
       }
       st.s.m[r] = -INFINITY;
       st.s.l[r] = 0.f;

@@ -183,3 +183,212 @@ def test_merge_states_invalid_arguments(name, kw):
     st = pk._lib.pkvd_merge_states(*[r(d) for d in descs], None)
     assert st == 1, (name, st, pk._lib.pkvd_last_error())
     assert pk._lib.pkvd_last_error()
+
+
+# ----------------------------------------------------------------------------
+# the extended call (pkvd_decode_ex): packed rows, masks, output type, workspace
+# ----------------------------------------------------------------------------
+def ex_call(inp, workspace=None, workspace_bytes=0, **over):
+    """pkvd_decode_ex over fake, aligned addresses (only rejected calls)."""
+    d = dict(inp)
+    d.update(over)
+    base = 1 << 32
+    names = ["q", "k_cache", "v_cache", "block_tables", "seq_lens_kv", "qo_indptr", "sinks",
+             "out", "lse"]
+    descs = {}
+    for i, name in enumerate(names):
+        t = d.get(name)
+        if t is None:
+            descs[name] = None
+            continue
+        dd = pk._desc(t)
+        dd.data = base + (i << 24)
+        descs[name] = dd
+    P = ctypes.POINTER(pk._Tensor)
+    ptr = lambda x: ctypes.pointer(x) if x is not None else P()
+    x = pk._DecodeArgs()
+    for name in names:
+        setattr(x, name, ptr(descs[name]))
+    x.q_len = int(d.get("q_len", d.get("q_len_per_req", 1)))
+    x.mask = int(d.get("mask", 0))
+    x.window_left = int(d.get("window_left", -1))
+    x.scale = float(d.get("scale", 0.1))
+    x.out_scale = float(d.get("out_scale", 1.0))
+    x.workspace = workspace
+    x.workspace_bytes = workspace_bytes
+    return pk._lib.pkvd_decode_ex(ctypes.byref(x), None)
+
+
+def packed_inputs():
+    inp = workloads.make_case(B=3, Hq=4, Hkv=2, D=64, page_size=16, seq_lens=(5, 40, 9),
+                              q_lens=(2, 0, 3))
+    R, Hq, D = inp["q"].shape
+    inp["q"] = inp["q"].contiguous()
+    inp["out"] = torch.empty(R, Hq, D, dtype=torch.float32)
+    inp["lse"] = torch.empty(R, Hq, dtype=torch.float32)
+    return inp
+
+
+EX_BAD = [
+    ("mask_value", dict(mask=2)),
+    ("qo_dtype", lambda i: dict(qo_indptr=i["qo_indptr"].long())),
+    ("qo_len", lambda i: dict(qo_indptr=i["qo_indptr"][:3])),
+    ("out_dtype_f64", lambda i: dict(out=i["out"].double())),
+    ("out_shape", lambda i: dict(out=i["out"][:3].contiguous())),
+    ("lse_shape", lambda i: dict(lse=i["lse"][:, :2].contiguous())),
+    ("out_scale_inf", dict(out_scale=float("inf"))),
+    ("q_len_zero", dict(q_len=0)),
+    ("packed_4d_q", lambda i: dict(q=i["q"].reshape(1, 5, 4, 64), out=i["out"].reshape(1, 5, 4, 64),
+                                   lse=None)),
+]
+
+
+@pytest.mark.parametrize("name,mut", EX_BAD, ids=[b[0] for b in EX_BAD])
+def test_ex_invalid_arguments(name, mut):
+    inp = packed_inputs()
+    over = mut(inp) if callable(mut) else mut
+    st = ex_call(inp, **over)
+    assert st == 1, (name, st, pk._lib.pkvd_last_error())
+    assert pk._lib.pkvd_last_error()
+
+
+def test_ex_token_major_checks():
+    """A fixed seq_len_q > 1 query may be token-major (B, SQ, Hq, D); its B
+    must match the block table and its rows must step evenly."""
+    inp = workloads.make_case(B=2, Hq=4, Hkv=2, D=64, page_size=16, seq_lens=(5, 40),
+                              q_len_per_req=3)
+    q4 = inp["q"].contiguous().reshape(2, 3, 4, 64)
+    good = dict(inp, q=q4, out=torch.empty(2, 3, 4, 64, dtype=torch.bfloat16),
+                lse=torch.empty(2, 3, 4), q_len=3)
+    # a too-small per-call workspace is the first thing that fails (no HIP call)
+    assert ex_call(good, workspace=1 << 40, workspace_bytes=256) == 3
+    bad_b = dict(good, q=torch.zeros(3, 3, 4, 64, dtype=torch.bfloat16),
+                 out=torch.empty(3, 3, 4, 64, dtype=torch.bfloat16), lse=None)
+    assert ex_call(bad_b) == 1
+    strided = torch.zeros(2, 4, 4, 64, dtype=torch.bfloat16)[:, :3]
+    assert ex_call(dict(good, q=strided, lse=None)) == 1
+
+
+def test_ex_workspace_too_small_is_an_error():
+    """A caller workspace smaller than the plan needs is refused before any
+    HIP call (cudnn_batch_decode_with_kv_cache, Parameters / workspace_buffer)."""
+    inp = packed_inputs()
+    need = pk.plan_ex(inp["q"], inp["k_cache"], inp["block_tables"], 3,
+                      qo_indptr=inp["qo_indptr"])["workspace_bytes"]
+    st = ex_call(inp, q_len=3, workspace=1 << 40, workspace_bytes=need - 256)
+    assert st == 3, pk._lib.pkvd_last_error()
+    assert b"too small" in pk._lib.pkvd_last_error()
+    # and a misaligned one is an invalid argument
+    st = ex_call(inp, q_len=3, workspace=(1 << 40) + 16, workspace_bytes=need)
+    assert st == 1, pk._lib.pkvd_last_error()
+
+
+def test_plan_ex_packed_and_unit_mode():
+    """Packed plans size the row tiles by max_seq_len_q; short numerous units
+    (a window) are streamed whole, one unit per wave."""
+    inp = packed_inputs()
+    p = pk.plan_ex(inp["q"], inp["k_cache"], inp["block_tables"], 3, qo_indptr=inp["qo_indptr"])
+    assert p["path"] == "mfma" and p["row_tiles"] == 1       # g * max rows = 2 * 3 = 6 > 4
+    w = workloads.CONFIGS["sink_window"]
+    q = torch.empty(w.B, w.Hq, w.D, dtype=torch.float16)
+    k = torch.empty(1, w.Hkv, w.page_size, w.D, dtype=torch.float16)
+    bt = torch.empty(w.B, w.C, dtype=torch.int32)
+    p = pk.plan_ex(q, k, bt, 1, w.window_left)
+    assert p["unit_mode"] == 1 and p["merge_kernel"] == 0 and p["waves"] == w.B * w.Hkv
+
+
+# ----------------------------------------------------------------------------
+# host replay of the persistent schedule (the kernels' own arithmetic)
+# ----------------------------------------------------------------------------
+def _shape_tensors(w, dtype=torch.bfloat16):
+    q = torch.empty(w.B * w.q_len_per_req, w.Hq, w.D, dtype=dtype)
+    k = torch.empty(1, w.Hkv, w.page_size, w.D, dtype=dtype)
+    bt = torch.empty(w.B, w.C, dtype=torch.int32)
+    return q, k, bt
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_schedule_replay_of_the_workloads(name):
+    """On each workload's seeded lengths every 16-key block is streamed by
+    exactly one wave, and every cut unit's merge names exactly the waves that
+    hold its pieces.  The sink + window batch runs whole units (no cuts)."""
+    w = workloads.CONFIGS[name]
+    n = workloads.seq_lens_of(w)
+    q, k, bt = _shape_tensors(w)
+    st = pk.schedule_stats(q, k, bt, n, w.q_len_per_req, w.window_left)
+    print(name, st)
+    assert st["errors"] == 0, st
+    keys = [min(int(x), w.window_left + w.q_len_per_req) if w.window_left >= 0 else int(x)
+            for x in n.tolist()]
+    lo = [max(0, int(x) - w.q_len_per_req - w.window_left) if w.window_left >= 0 else 0
+          for x in n.tolist()]
+    blocks = sum((int(x) - 1) // 16 - l // 16 + 1 for x, l in zip(n.tolist(), lo))
+    rows = (w.Hq // w.Hkv) * w.q_len_per_req
+    tiles = -(-rows // (4 if rows <= 4 else 16))
+    assert st["blocks"] == blocks * w.Hkv * tiles
+    assert st["units"] == w.B * w.Hkv * tiles
+    if name == "sink_window":
+        assert st["cut_units"] == 0
+    assert sum(keys) > 0
+
+
+KNOBS = [{}, {"PKVD_WAVES": "7", "PKVD_MIN_WAVE_BLOCKS": "1"},
+         {"PKVD_WAVES": "64", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_SEG_COST": "5"},
+         {"PKVD_WAVES": "40", "PKVD_GROUPS": "5", "PKVD_SLOT_W": "140,100",
+          "PKVD_MIN_WAVE_BLOCKS": "1"},
+         {"PKVD_WAVES": "333", "PKVD_MIN_WAVE_BLOCKS": "1", "PKVD_SEG_COST": "17"},
+         {"PKVD_UNIT_MODE": "1"}, {"PKVD_UNIT_MODE": "1", "PKVD_WAVES": "5"},
+         {"PKVD_UNIT_MODE": "0", "PKVD_SEG_COST": "9"}]
+
+
+class _env:
+    def __init__(self, kv):
+        self.kv = kv
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update(self.kv)
+        pk.reload_tuning()
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        pk.reload_tuning()
+
+
+@pytest.mark.parametrize("knobs", KNOBS, ids=[",".join(f"{k}={v}" for k, v in d.items()) or "auto"
+                                              for d in KNOBS])
+def test_schedule_replay_random(knobs):
+    """Random batches (empty requests, packed rows of varying length, windows,
+    multi-token rows) under forced grids, seg costs, slot weights and the
+    whole-unit mode: blocks covered once, merges consistent."""
+    g = torch.Generator().manual_seed(77)
+    with _env(knobs):
+        for trial in range(40):
+            B = int(torch.randint(1, 40, (1,), generator=g))
+            Hkv = int(torch.randint(1, 4, (1,), generator=g))
+            grp = int(torch.randint(1, 9, (1,), generator=g))
+            ps = [1, 5, 16, 64][int(torch.randint(0, 4, (1,), generator=g))]
+            wl = [-1, 0, 7, 100][int(torch.randint(0, 4, (1,), generator=g))]
+            n = torch.randint(0, 700, (B,), generator=g, dtype=torch.int32)
+            packed = bool(torch.randint(0, 2, (1,), generator=g))
+            C = max(1, -(-int(n.max()) // ps))
+            k = torch.empty(1, Hkv, ps, 64, dtype=torch.bfloat16)
+            bt = torch.empty(B, C, dtype=torch.int32)
+            if packed:
+                ql = torch.randint(0, 5, (B,), generator=g, dtype=torch.int32)
+                qo = torch.zeros(B + 1, dtype=torch.int32)
+                qo[1:] = torch.cumsum(ql, 0)
+                rows = max(1, int(qo[-1]))
+                q = torch.empty(rows, grp * Hkv, 64, dtype=torch.bfloat16)
+                st = pk.schedule_stats(q, k, bt, n, max(1, int(ql.max())), wl, qo_indptr=qo)
+            else:
+                Lq = int(torch.randint(1, 4, (1,), generator=g))
+                q = torch.empty(B * Lq, grp * Hkv, 64, dtype=torch.bfloat16)
+                st = pk.schedule_stats(q, k, bt, n, Lq, wl)
+            assert st["errors"] == 0, (trial, st)
+            if knobs.get("PKVD_UNIT_MODE") == "1":
+                assert st["cut_units"] == 0, (trial, st)

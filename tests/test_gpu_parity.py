@@ -140,6 +140,9 @@ SCHEDULES = {
     "mk_segcost": {"PKVD_SEG_COST": "3", "PKVD_WAVES": "40", "PKVD_MIN_WAVE_BLOCKS": "1",
                    "PKVD_GROUPS": "5", "PKVD_SLOT_W": "130,100", "PKVD_MERGE_KERNEL": "1",
                    "PKVD_FORCE_PATH": "0"},
+    # whole units: slice bounds snap to unit starts (few waves, and the default grid)
+    "unit": {"PKVD_UNIT_MODE": "1"},
+    "unit_w5": {"PKVD_UNIT_MODE": "1", "PKVD_WAVES": "5", "PKVD_MIN_WAVE_BLOCKS": "1"},
 }
 
 
@@ -152,6 +155,7 @@ class schedule:
     def __enter__(self):
         self.old = {k: os.environ.get(k) for k in self.env}
         os.environ.update(self.env)
+        _pk().reload_tuning()
 
     def __exit__(self, *exc):
         for k, v in self.old.items():
@@ -159,6 +163,7 @@ class schedule:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+        _pk().reload_tuning()
 
 
 class env:
@@ -170,6 +175,7 @@ class env:
     def __enter__(self):
         self.old = {k: os.environ.get(k) for k in self.kv}
         os.environ.update(self.kv)
+        _pk().reload_tuning()
 
     def __exit__(self, *exc):
         for k, v in self.old.items():
@@ -177,6 +183,7 @@ class env:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+        _pk().reload_tuning()
 
 
 @pytest.mark.parametrize("name,path", [("llama3_8b", "1"), ("spec_verify", "0"),
@@ -186,26 +193,25 @@ def test_config_other_engine(name, path):
     log(f"[engine] config={name} PKVD_FORCE_PATH={path}")
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
-    os.environ["PKVD_FORCE_PATH"] = path
-    try:
+    with env(PKVD_FORCE_PATH=path):
         p = _pk().plan(d["q"], d["k_cache"], d["block_tables"], d["q_len_per_req"],
                        d["window_left"])
         log(f"[engine] plan={p}")
         assert p["path"] == {"0": "valu", "1": "mfma"}[path]
         out, lse = run_gpu(d, lse=True)
-    finally:
-        os.environ.pop("PKVD_FORCE_PATH", None)
     compare(f"{name}/path{path}", out, lse, ref_out, ref_lse)
 
 
 @pytest.mark.parametrize("name,mode", [("llama3_8b", "1"), ("long_ctx", "0"), ("spec_verify", "0"),
-                                       ("sink_window", "1")])
+                                       ("sink_window", "1"), ("sink_window", "0")])
 def test_config_other_merge(name, mode):
-    """Full-size configs with the merge mode the planner does not pick for them."""
+    """Full-size configs with the merge mode the planner does not pick for them
+    (the sink + window batch, streamed as whole units by default, is cut into
+    block slices here and merged both ways)."""
     log(f"[merge] config={name} PKVD_MERGE_KERNEL={mode}")
     inp, (ref_out, ref_lse, _) = config_inputs(name)
     d = to_dev(inp)
-    with env(PKVD_MERGE_KERNEL=mode):
+    with env(PKVD_MERGE_KERNEL=mode, PKVD_UNIT_MODE="0"):
         out, lse = run_gpu(d, lse=True)
         out2, lse2 = run_gpu(d, lse=True)
     compare(f"{name}/merge{mode}", out, lse, ref_out, ref_lse)

@@ -22,7 +22,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_config", "make_case"]
+__all__ = ["Workload", "CONFIGS", "make_config", "make_case", "seq_lens_of"]
 
 _DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
@@ -88,6 +88,15 @@ def _randn_chunked(shape: Sequence[int], gen: torch.Generator, std: float,
             x.mul_(std)
         out[s:e] = x.to(dtype)
     return out
+
+
+def seq_lens_of(w: Workload | str) -> torch.Tensor:
+    """The sequence lengths make_config draws for ``w`` (its first draw),
+    without drawing the rest of the batch."""
+    if isinstance(w, str):
+        w = CONFIGS[w]
+    gen = torch.Generator().manual_seed(w.seed)
+    return torch.randint(w.kv_lo, w.kv_hi + 1, (w.B,), generator=gen, dtype=torch.int32)
 
 
 def make_config(w: Workload | str, poison: bool = False,
