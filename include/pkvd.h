@@ -140,6 +140,26 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
                 pkvd_tensor* out, pkvd_tensor* lse, void* stream);
 
 /*
+ * pkvd_decode_static -- pkvd_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, layout, semantics and errors as
+ * pkvd_decode, but the workspace is a static device array of the library
+ * (32 MiB on each GPU the library runs on, held from load until the process
+ * ends) instead of a buffer the library or the caller allocates.  The call
+ * allocates and frees nothing (no hipMalloc, no library allocation) and
+ * never synchronises.  A call whose plan needs more than 32 MiB of workspace
+ * fails with PKVD_ERR_WORKSPACE before any HIP call.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams without events between them) race and must not be made; calls on
+ * one stream are ordered.  pkvd_decode's own workspace is separate.
+ */
+int pkvd_decode_static(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                       const pkvd_tensor* v_cache, const pkvd_tensor* block_tables,
+                       const pkvd_tensor* seq_lens_kv, float scale, int32_t q_len_per_req,
+                       int32_t window_left, const pkvd_tensor* sinks, pkvd_tensor* out,
+                       pkvd_tensor* lse, void* stream);
+
+/*
  * Arguments of pkvd_decode_ex: the pkvd_decode call plus packed query rows,
  * the mask type, the output scale and type, and a per-call workspace
  * (batch_decode_with_paged_kv_cache: summary; Parameters / q, paged_kv_cache,

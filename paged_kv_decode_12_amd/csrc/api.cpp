@@ -758,6 +758,37 @@ int pkvd_decode(const pkvd_tensor* q, const pkvd_tensor* k_cache, const pkvd_ten
 
 int pkvd_decode_ex(const pkvd_decode_args* args, void* stream) { return run_decode(args, stream); }
 
+int pkvd_decode_static(const pkvd_tensor* q, const pkvd_tensor* k_cache,
+                       const pkvd_tensor* v_cache, const pkvd_tensor* block_tables,
+                       const pkvd_tensor* seq_lens_kv, float scale, int32_t q_len_per_req,
+                       int32_t window_left, const pkvd_tensor* sinks, pkvd_tensor* out,
+                       pkvd_tensor* lse, void* stream) {
+  g_last_error.clear();
+  pkvd_decode_args x = fixed_args(q, k_cache, v_cache, block_tables, seq_lens_kv, scale,
+                                  q_len_per_req, window_left, sinks, out, lse);
+  if (out && q && out->dtype != q->dtype)
+    return fail(PKVD_ERR_INVALID_ARG, "out must have q's dtype");
+  // the size check comes before any HIP call
+  Shapes s;
+  int st = shapes_of(&x, &s);
+  if (st != PKVD_OK) return st;
+  Plan p;
+  st = plan_of(s, window_left, &p);
+  if (st != PKVD_OK) return st;
+  if (p.ws_bytes > pkvd::kStaticScratchBytes)
+    return fail(PKVD_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace, more than the %zu-byte static workspace "
+                "of pkvd_decode_static",
+                p.ws_bytes, pkvd::kStaticScratchBytes);
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipError_t e = pkvd::static_scratch(&ptr, &bytes);
+  if (e != hipSuccess) return fail(PKVD_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  x.workspace = ptr;
+  x.workspace_bytes = bytes;
+  return run_decode(&x, stream);
+}
+
 int pkvd_schedule_stats(const pkvd_decode_args* args, const int32_t* seq_lens,
                         const int32_t* qo_indptr, int64_t stats[8]) {
   using namespace pkvd::dev;

@@ -12,6 +12,8 @@ constexpr int kBlockKeys = 16;   // keys per block: the unit a wave loads and sc
 constexpr int kMaxSinkHeads = 4096;   // sink logits the decode kernel stages in LDS
 constexpr int kSimdsPerCu = 4;   // a decode workgroup holds WPE waves on each SIMD of a CU
 constexpr int kMaxBatch = 8192;        // requests per call (the schedule keeps a prefix in LDS)
+// Size of the static workspace of pkvd_decode_static (static_scratch.hip).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
 
 enum Path : int { kPathValu = 0, kPathMfma = 1 };
 enum OutType : int { kOutBf16 = 0, kOutF16 = 1, kOutF32 = 2 };
@@ -75,6 +77,10 @@ KernelPair kernels_d128_bf16(int path, int rows_per_tile, bool pow2);
 KernelPair kernels_d128_f16(int path, int rows_per_tile, bool pow2);
 KernelPair kernels_d64_bf16(int path, int rows_per_tile, bool pow2);
 KernelPair kernels_d64_f16(int path, int rows_per_tile, bool pow2);
+
+// The current device's address of the static workspace and its size
+// (static_scratch.hip).  Allocates nothing.
+hipError_t static_scratch(void** ptr, size_t* bytes);
 
 // Launcher (decode_launch.hip).  Returns the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int path, int rows_per_tile, bool bf16,

@@ -392,3 +392,29 @@ def test_schedule_replay_random(knobs):
             assert st["errors"] == 0, (trial, st)
             if knobs.get("PKVD_UNIT_MODE") == "1":
                 assert st["cut_units"] == 0, (trial, st)
+
+
+def test_static_entry_point_rejects_plans_beyond_its_workspace():
+    """pkvd_decode_static fails with PKVD_ERR_WORKSPACE, before any HIP call,
+    when the plan needs more than its 32 MiB static workspace."""
+    lib = pk._lib
+    P = ctypes.POINTER(pk._Tensor)
+    lib.pkvd_decode_static.restype = ctypes.c_int
+    lib.pkvd_decode_static.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int32,
+                                       ctypes.c_int32, P, P, P, ctypes.c_void_p]
+    B, Hq, Hkv, D, ps, C = 64, 64, 8, 128, 16, 64
+    q = torch.empty(B, Hq, D, dtype=torch.bfloat16)
+    k = torch.empty(4, Hkv, ps, D, dtype=torch.bfloat16)
+    bt = torch.empty(B, C, dtype=torch.int32)
+    n = torch.empty(B, dtype=torch.int32)
+    out = torch.empty_like(q)
+    with _env({"PKVD_WAVES": "4096"}):
+        assert pk.workspace_bytes(q, k, bt) > 32 << 20
+        descs = [pk._desc(t) for t in (q, k, k, bt, n, out)]
+        for i, d in enumerate(descs):
+            d.data = (1 << 32) + (i << 24)
+        r = [ctypes.byref(d) for d in descs]
+        st = lib.pkvd_decode_static(r[0], r[1], r[2], r[3], r[4], 0.1, 1, -1, None, r[5], None,
+                                    None)
+    assert st == 3, lib.pkvd_last_error()
+    assert b"static workspace" in lib.pkvd_last_error()
