@@ -150,6 +150,305 @@ def bench_merge_states(args):
                       "steps": args.steps, "max_abs_err_sampled": err}), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _ceiling_lib():
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_decode_12_amd", "libpkvd_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    if not hasattr(lib, "pkvd_ceiling_abi") or lib.pkvd_ceiling_abi() != 2:
+        raise SystemExit(f"{path} is stale (argument lists differ): rebuild it")
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.pkvd_ceiling_stream_read.restype = ctypes.c_int
+    c = ctypes.c_int
+    lib.pkvd_ceiling_stream_read.argtypes = [p, i64, c, c, p, p]
+    lib.pkvd_ceiling_paged_gather.restype = ctypes.c_int
+    lib.pkvd_ceiling_paged_gather.argtypes = [p, p, p, p, i64, c, c, c, c, c, p, p]
+    return lib
+
+
+def decode_blocks(inp):
+    """Byte offsets (K and V) of every 16-key block a decode call of these
+    inputs streams: per (request, kv head), the blocks covering the keys some
+    row of the request sees, in the decode's unit order."""
+    import numpy as np
+    k, v = inp["k_cache"], inp["v_cache"]
+    elt = k.element_size()
+    P, Hkv, ps, D = k.shape
+    if ps < 16 or ps & (ps - 1):
+        raise SystemExit("the paged-gather ceiling needs a power-of-two page_size >= 16")
+    bt = inp["block_tables"].numpy()
+    Lq, wl = inp["q_len_per_req"], inp["window_left"]
+    ko, vo = [], []
+    for b, n in enumerate(inp["seq_lens_kv"].tolist()):
+        lo = 0 if wl < 0 else max(0, n - Lq - wl)
+        if n <= lo:
+            continue
+        blocks = np.arange(lo // 16, (n - 1) // 16 + 1, dtype=np.int64)
+        pages = bt[b, (blocks * 16) // ps].astype(np.int64)
+        slot = (blocks * 16) % ps
+        for h in range(Hkv):
+            ko.append((pages * k.stride(0) + h * k.stride(1) + slot * D) * elt)
+            vo.append((pages * v.stride(0) + h * v.stride(1) + slot * D) * elt)
+    return np.concatenate(ko), np.concatenate(vo), 16 * D * elt
+
+
+def bench_ceiling(args):
+    """Memory-system references for a workload's bytes (ceiling.hip): a plain
+    streaming read of the decode's algorithmic byte count, and the decode's own
+    16-key block gather (every K/V block it streams, no arithmetic), with
+    loads into registers or staged through LDS.  Same grid as the decode
+    (its plan's waves); times from HIP events around `steps` back-to-back
+    launches."""
+    import numpy as np
+    import torch
+    import workloads
+    import paged_kv_decode_12_amd as pk
+    lib = _ceiling_lib()
+    w = workloads.CONFIGS[args.config]
+    inp = workloads.make_config(args.config)
+    nbytes = kv_bytes(inp)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    plan = pk.plan(inp["q"], inp["k_cache"], inp["block_tables"], w.q_len_per_req, w.window_left)
+    wpg = 4 * args.waves_per_simd
+    nw = 256 * wpg if args.waves_per_simd != 1 else int(plan["waves"])
+    sink = torch.empty(nw * 64, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.op == "stream_read":
+        total = (nbytes + 1023) // 1024 * 1024
+        buf = torch.ones(total // 4, dtype=torch.int32, device=dev)
+        call = lambda: lib.pkvd_ceiling_stream_read(buf.data_ptr(), total, nw, wpg,
+                                                    sink.data_ptr(), stream.cuda_stream)
+        read_bytes = total
+    else:
+        ko, vo, blk = decode_blocks(inp)
+        k, v = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+        kot = torch.from_numpy(ko).to(dev)
+        vot = torch.from_numpy(vo).to(dev)
+        call = lambda: lib.pkvd_ceiling_paged_gather(k.data_ptr(), v.data_ptr(), kot.data_ptr(),
+                                                     vot.data_ptr(), ko.size, blk, nw, wpg,
+                                                     args.pf, 1 if args.lds else 0,
+                                                     sink.data_ptr(), stream.cuda_stream)
+        read_bytes = 2 * ko.size * blk
+    for _ in range(args.warmup):
+        if call() != 0:
+            raise SystemExit("ceiling kernel launch failed")
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    kind = args.op + ("_lds" if args.op == "paged_gather" and args.lds else "")
+    print(json.dumps({"op": kind, "config": args.config, "waves": nw,
+                      "blocks_in_flight_per_wave": args.pf if args.op == "paged_gather" else None,
+                      "us_per_launch": round(us, 3),
+                      "bytes_read_per_launch": read_bytes,
+                      "GBps_read": round(read_bytes / (us * 1e-6) / 1e9, 1),
+                      "frac_of_peak": round(read_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "decode_kv_bytes": nbytes,
+                      "decode_us_at_this_rate": round(nbytes / (read_bytes / us), 2),
+                      "steps": args.steps}), flush=True)
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 csv -> profiles/ summaries
+# ----------------------------------------------------------------------------
+PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL {t} rocprofv3 {what} -d "
+               "$REPO/gpurun_out/prof/{tag} -o {tag} --output-format csv -- python3 $REPO/bench.py "
+               "{bargs}")
+
+
+def _csv_rows(pattern):
+    import csv
+    import glob
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise SystemExit(f"no rocprofv3 output matches {pattern}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def _per_dispatch(rows, counter, kfilter):
+    """`counter` per dispatch of kernels whose name contains kfilter, summed
+    over its instances (SEs, XCDs) -- or, for the GRBM_ cycle counters, their
+    maximum (rocprofv3's own reduction for them) -> per-dispatch list."""
+    per = {}
+    agg = max if counter.startswith("GRBM_") else (lambda a, b: a + b)
+    for r in rows:
+        if kfilter in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            k = r["Dispatch_Id"]
+            per[k] = agg(per[k], float(r["Counter_Value"])) if k in per else float(r["Counter_Value"])
+    return [per[k] for k in sorted(per, key=int)]
+
+
+SQ_SETS = {
+    "sq_a": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+             "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY",
+             "GRBM_GUI_ACTIVE"],
+    "sq_b": ["SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU",
+             "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+             "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"],
+}
+
+
+def summarize(args):
+    """Write a profiles/ summary from rocprofv3 csv output under --prof-dir
+    (the directory a rocprofv3 -d run wrote).  Kinds: trace (kernel-trace
+    statistics), fetch / write (FETCH_SIZE or WRITE_SIZE in KiB per dispatch,
+    combined into one traffic file once both exist), sq_a / sq_b (SQ counter
+    sets), calibration (a plain 1 GiB copy: the counter scale factors)."""
+    import statistics
+    kind, d, w = args.summarize, args.prof_dir, args.config
+    bargs = f"--config {w} --steps 10 --warmup 2 --cold-iters 0 --cpu-seconds 0 --no-check"
+    sha = kernel_source_hash()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    if kind == "calibration":
+        f = _per_dispatch(_csv_rows(d + "/fetch/**/*counter_collection.csv"), "FETCH_SIZE", "copyBuffer")
+        wr = _per_dispatch(_csv_rows(d + "/write/**/*counter_collection.csv"), "WRITE_SIZE", "copyBuffer")
+        nbytes = 1 << 30
+        L = ["# FETCH_SIZE / WRITE_SIZE calibration: a plain 1 GiB device-to-device copy",
+             "# (torch copy_ -> __amd_rocclr_copyBuffer), each dispatch reads and writes exactly 1 GiB",
+             "command_fetch: " + PROFILE_CMD.format(t=60, what="--pmc FETCH_SIZE", tag="calib/fetch",
+                                                    bargs="--copy-calibration"),
+             "command_write: " + PROFILE_CMD.format(t=60, what="--pmc WRITE_SIZE", tag="calib/write",
+                                                    bargs="--copy-calibration"),
+             f"dispatches: {len(f)}",
+             f"fetch_kib_per_dispatch: {statistics.mean(f):.2f}",
+             f"write_kib_per_dispatch: {statistics.mean(wr):.2f}",
+             f"bytes_per_dispatch: {nbytes}",
+             f"fetch_factor: {nbytes / (statistics.mean(f) * 1024):.4f}   (bytes = FETCH_SIZE KiB * 1024 * factor)",
+             f"write_factor: {nbytes / (statistics.mean(wr) * 1024):.4f}   (bytes = WRITE_SIZE KiB * 1024 * factor)"]
+        path = os.path.join(ROOT, "profiles", "copy_1GiB_counter_calibration.txt")
+    elif kind == "trace":
+        import workloads
+        kt = _csv_rows(d + "/**/*kernel_trace.csv")
+        dec = [r for r in kt if "decode_kernel" in r["Kernel_Name"]]
+        mer = [r for r in kt if "merge_kernel" in r["Kernel_Name"]]
+        dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        dd = [dur(r) for r in dec]
+        nbytes = kv_bytes(workloads.make_config(w))
+        r0 = dec[0]
+        tag = os.path.basename(d.rstrip("/"))
+        L = [f"# decode kernel, {w} workload: rocprofv3 kernel trace statistics",
+             "command: " + PROFILE_CMD.format(t=180, what="--kernel-trace --stats", tag=tag, bargs=bargs),
+             f"source_sha256: {sha}",
+             f"kernel: {r0['Kernel_Name']}",
+             f"grid: {r0.get('Grid_Size_X', r0.get('Grid_Size'))} work-items, workgroup "
+             f"{r0.get('Workgroup_Size_X', r0.get('Workgroup_Size'))}, LDS {r0.get('LDS_Block_Size')} B, "
+             f"VGPR {r0.get('VGPR_Count')}, AGPR {r0.get('Accum_VGPR_Count')}, SGPR {r0.get('SGPR_Count')}",
+             f"dispatches: {len(dd)}  median_us: {statistics.median(dd):.2f}  mean_us: "
+             f"{statistics.mean(dd):.2f}  min_us: {min(dd):.2f}  max_us: {max(dd):.2f}"]
+        tot = statistics.mean(dd)
+        if mer:
+            md = [dur(r) for r in mer]
+            L += [f"merge_kernel: {mer[0]['Kernel_Name'][:100]}",
+                  f"merge_dispatches: {len(md)}  median_us: {statistics.median(md):.2f}  mean_us: "
+                  f"{statistics.mean(md):.2f}",
+                  f"decode_plus_merge_mean_us: {tot + statistics.mean(md):.2f}"]
+            tot += statistics.mean(md)
+        L += [f"algorithmic_kv_bytes_per_launch: {nbytes}",
+              f"effective_GBps_at_mean: {nbytes / tot / 1e3:.1f}  ({nbytes / tot / 1e3 / 80:.1f}% of 8 TB/s)",
+              "", "# kernel_stats.csv (all kernels of the run)",
+              "name | calls | average_ns | min_ns | max_ns | percentage"]
+        for r in _csv_rows(d + "/**/*kernel_stats.csv"):
+            L.append(f"{r['Name'][:110]} | {r['Calls']} | {r['AverageNs']} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {r['Percentage']}")
+        path = os.path.join(ROOT, "profiles", f"decode_{w}_kernel_trace.txt")
+    elif kind in ("fetch", "write"):
+        import workloads
+        cal = {}
+        for line in open(os.path.join(ROOT, "profiles", "copy_1GiB_counter_calibration.txt")):
+            if line.startswith("fetch_factor:"):
+                cal["fetch"] = float(line.split()[1])
+            if line.startswith("write_factor:"):
+                cal["write"] = float(line.split()[1])
+        counter = kind.upper() + "_SIZE"
+        v = _per_dispatch(_csv_rows(d + "/**/*counter_collection.csv"), counter, "decode_kernel")
+        part = os.path.join(ROOT, "profiles", f".{w}_{kind}.part")
+        tag = os.path.basename(d.rstrip("/"))
+        with open(part, "w") as fh:
+            fh.write(json.dumps({"kib": statistics.mean(v), "min": min(v), "max": max(v), "n": len(v),
+                                 "factor": cal[kind], "sha": sha,
+                                 "cmd": PROFILE_CMD.format(t=90, what=f"--pmc {counter}", tag=tag,
+                                                           bargs=bargs)}))
+        other = os.path.join(ROOT, "profiles", f".{w}_{'write' if kind == 'fetch' else 'fetch'}.part")
+        if not os.path.exists(other):
+            print(f"stored {kind}; summarise the other counter to write the traffic file")
+            return
+        fp = json.load(open(part if kind == "fetch" else other))
+        wp = json.load(open(other if kind == "fetch" else part))
+        os.remove(part)
+        os.remove(other)
+        nbytes = kv_bytes(workloads.make_config(w))
+        fb, wb = int(fp["kib"] * 1024 * fp["factor"]), int(wp["kib"] * 1024 * wp["factor"])
+        L = [f"# decode kernel, {w} workload: HBM traffic per launch from rocprofv3 counters",
+             "# (one counter per run; scaled by the 1 GiB copy calibration in copy_1GiB_counter_calibration.txt)",
+             f"command_fetch: {fp['cmd']}", f"command_write: {wp['cmd']}",
+             f"source_sha256: {sha}", f"dispatches: {fp['n']}",
+             f"fetch_kib_per_dispatch: {fp['kib']:.2f} (min {fp['min']:.2f}, max {fp['max']:.2f})",
+             f"write_kib_per_dispatch: {wp['kib']:.2f} (min {wp['min']:.2f}, max {wp['max']:.2f})",
+             f"fetch_factor: {fp['factor']:.4f}", f"write_factor: {wp['factor']:.4f}",
+             f"fetch_bytes_per_launch: {fb}", f"write_bytes_per_launch: {wb}",
+             f"traffic_bytes_per_launch: {fb + wb}", f"algorithmic_kv_bytes_per_launch: {nbytes}",
+             f"fetch_over_algorithmic: {fb / nbytes:.4f}"]
+        path = os.path.join(ROOT, "profiles", f"decode_{w}_hbm_traffic.txt")
+    elif kind in SQ_SETS:
+        rows = _csv_rows(d + "/**/*counter_collection.csv")
+        names = SQ_SETS[kind]
+        vals = {n: statistics.mean(_per_dispatch(rows, n, "decode_kernel")) for n in names}
+        cus, simds = 256, 1024
+        gui = vals["GRBM_GUI_ACTIVE"]
+        tag = os.path.basename(d.rstrip("/"))
+        L = [f"# decode kernel, {w} workload: SQ counters per dispatch (mean over the run's dispatches, "
+             "summed over SEs and XCDs)",
+             "command: " + PROFILE_CMD.format(t=90, what="--pmc " + " ".join(names), tag=tag, bargs=bargs),
+             f"source_sha256: {sha}"]
+        L += [f"{n}: {vals[n]:.0f}" for n in names]
+        L.append("# derived (rocprofv3's own definitions; 256 CUs, 1024 SIMDs):")
+        if kind == "sq_a":
+            L += [f"MfmaUtil_pct: {100 * vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.2f}   "
+                  "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs))",
+                  f"VALUBusy_pct: {100 * vals['SQ_ACTIVE_INST_VALU'] / cus / gui:.2f}   "
+                  "(100 * SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE)",
+                  f"Occupancy_pct: {400 * vals['SQ_WAVE_CYCLES'] / gui / cus / 32:.2f}   "
+                  "(400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32)",
+                  f"waves_per_CU: {vals['SQ_WAVES'] / cus:.2f}",
+                  f"wait_inst_any_frac_of_wave_cycles: {vals['SQ_WAIT_INST_ANY'] / max(vals['SQ_WAVE_CYCLES'], 1):.3f}",
+                  f"valu_insts_per_wave: {vals['SQ_INSTS_VALU'] / max(vals['SQ_WAVES'], 1):.0f}",
+                  f"mfma_insts_per_wave: {vals['SQ_INSTS_MFMA'] / max(vals['SQ_WAVES'], 1):.0f}"]
+        else:
+            L += [f"LDSBankConflict_pct: {100 * vals['SQ_LDS_BANK_CONFLICT'] / gui / cus:.3f}   "
+                  "(100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs)",
+                  f"lds_insts: {vals['SQ_INSTS_LDS']:.0f}   vmem_rd_insts: {vals['SQ_INSTS_VMEM_RD']:.0f}",
+                  f"mfma_mops_bf16_f16 (x512 = flops): {vals['SQ_INSTS_VALU_MFMA_MOPS_BF16'] + vals['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}"]
+        path = os.path.join(ROOT, "profiles", f"decode_{w}_{kind}_counters.txt")
+    else:
+        raise SystemExit(f"unknown summary kind {kind}")
+    with open(path, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L[:12]))
+    print("wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,9 +459,21 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU-baseline leg (0 disables it)")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--op", choices=("decode", "merge_states"), default="decode",
+    ap.add_argument("--op", choices=("decode", "merge_states", "stream_read", "paged_gather"),
+                    default="decode",
                     help="merge_states: time the cascade merge on 16 states of the "
-                         "llama3_8b batch's rows instead of the decode")
+                         "llama3_8b batch's rows instead of the decode; stream_read / "
+                         "paged_gather: memory-system references for the workload's bytes")
+    ap.add_argument("--lds", action="store_true",
+                    help="paged_gather: stage the blocks through LDS instead of registers")
+    ap.add_argument("--pf", type=int, default=3,
+                    help="paged_gather: 16-key blocks in flight per wave (2, 3, 4, 6, 8)")
+    ap.add_argument("--waves-per-simd", type=int, default=1, choices=(1, 2),
+                    help="stream_read / paged_gather: 1 (the decode's grid) or 2 waves per SIMD")
+    ap.add_argument("--summarize", default=None,
+                    help="write a profiles/ summary from rocprofv3 csv output: trace, fetch, "
+                         "write, sq_a, sq_b or calibration (with --prof-dir)")
+    ap.add_argument("--prof-dir", default=None, help="the rocprofv3 -d directory to summarise")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -172,8 +483,14 @@ def main():
               "MI355X; multi-GPU sharding is a design note, not a built path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.summarize:
+        summarize(args)
+        return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op in ("stream_read", "paged_gather"):
+        bench_ceiling(args)
         return
     if args.op == "merge_states":
         bench_merge_states(args)
@@ -316,7 +633,7 @@ def main():
                 "kind": "oracle",
                 "sample": f"the whole {args.config} batch (all {inp['q'].shape[0] * w.Hq} "
                           f"row-heads), {runs} run(s), {per:.3f} s each, fp64 C + OpenMP",
-                "cpu": platform.processor() or platform.machine()}
+                "cpu": cpu_model()}
         if not args.no_check:
             got = out.float().cpu().numpy().reshape(-1, w.D)
             err = float(np.abs(got - ref[0]).max())

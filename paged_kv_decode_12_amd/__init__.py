@@ -58,12 +58,19 @@ class PkvdError(RuntimeError):
     """A HIP or workspace failure reported by the library."""
 
 
+_ABI_VERSION = "0.2.0"   # pkvd_version() of the argument lists this binding passes
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is missing: build it first (python paged_kv_decode_12_amd/build.py "
             "or __graft_entry__.build()); there is no fallback implementation")
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.pkvd_version.restype = ctypes.c_char_p
+    if lib.pkvd_version().decode() != _ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} reports version {lib.pkvd_version().decode()}, this "
+                          f"binding passes the arguments of {_ABI_VERSION}: rebuild the library")
     P = ctypes.POINTER(_Tensor)
     lib.pkvd_decode.restype = ctypes.c_int
     lib.pkvd_decode.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
