@@ -16,6 +16,11 @@ Parity status of each function:
                   golden cases; packed rows, dense rows and the output scale
                   against the brute force and hand-worked cases)
   merge_states    pinned (merge of disjoint key ranges equals the union)
+  prefill         pinned (tests/test_oracle.py: hand-worked cases, torch
+                  brute force over masks / GQA / packed rows, equality with
+                  the decode definition on one-page caches, closed forms,
+                  window key counts, variable windows equal to the causal
+                  window, packed rows equal to per-request fixed calls)
   decode, lse with sinks present: the keys-only reading of the LSE is a
                   reading, not fixed by the pages -> parity unpinned for that
                   combination.
@@ -66,6 +71,12 @@ def _load():
             p, i64, i64,                 # sinks, key range
             p, i64,                      # sel
             p, p, p, ctypes.c_int]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [
+            p, i64, i64, p, i64, i64, p, i64, i64,      # q, k, v (row, head strides)
+            ctypes.c_int, i64, i64, i64, i64, i64, i64,  # dtype, B, Hq, Hkv, D, Sq, Sk
+            p, p, ctypes.c_int, i64, p, p,              # qo, kvo, mask, window_left, starts, ends
+            ctypes.c_double, ctypes.c_double, p, i64, p, ctypes.c_int]
         lib.oracle_merge_states.restype = None
         lib.oracle_merge_states.argtypes = [p, p, i64, i64, p, p, p]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -161,6 +172,59 @@ def decode(inputs: dict, sel=None, key_range=None, nthreads: int = 0,
     if st != 0:
         raise ValueError(f"oracle_decode: {_ERRORS.get(st, st)}")
     return out, lse, lse_ws
+
+
+_PREFILL_MASKS = {"causal": 0, "dense": 1, "variable_window": 2}
+
+
+def prefill(inputs: dict, sel=None, nthreads: int = 0):
+    """Reference context attention (flashinfer.attention.prims_ts.batch_prefill)
+    for an inputs dict with keys q, k, v (fixed [B, S, H, D] or packed
+    [total, H, D] with qo_indptr and kv_indptr), mask_type, window_left,
+    window_starts / window_ends (variable_window), sm_scale, output_scale.
+    Returns out [count, D] float64 (rows x Hq in row-major order, or the
+    flat indices row * Hq + head listed in sel)."""
+    lib = _load()
+    q, k, v = inputs["q"], inputs["k"], inputs["v"]
+    qo, kvo = inputs.get("qo_indptr"), inputs.get("kv_indptr")
+    if qo is None:
+        B, Sq, Hq, D = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+        q, k, v = (t.reshape(t.shape[0] * t.shape[1], t.shape[2], t.shape[3]) for t in (q, k, v))
+    else:
+        B = qo.numel() - 1
+        Sq = Sk = 0
+        _, Hq, D = q.shape
+        Hkv = k.shape[1]
+    qb, code = _bits(q)
+    kb, kcode = _bits(k)
+    vb, vcode = _bits(v)
+    assert code == kcode == vcode
+    e = 2
+    qo_a = None if qo is None else np.ascontiguousarray(_i32(qo))
+    kvo_a = None if kvo is None else np.ascontiguousarray(_i32(kvo))
+    mask = _PREFILL_MASKS[inputs.get("mask_type", "dense")]
+    st_a = en_a = None
+    if mask == 2:
+        st_a = np.ascontiguousarray(_i32(inputs["window_starts"]))
+        en_a = np.ascontiguousarray(_i32(inputs["window_ends"]))
+    rows = q.shape[0]
+    sel_arr = None if sel is None else np.ascontiguousarray(np.asarray(sel, dtype=np.int64))
+    count = rows * Hq if sel is None else sel_arr.size
+    out = np.empty((count, D), dtype=np.float64)
+    scale = inputs.get("sm_scale")
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    ptr = lambda a: None if a is None else a.ctypes.data
+    st = lib.oracle_prefill(
+        ptr(qb), qb.strides[0] // e, qb.strides[1] // e,
+        ptr(kb), kb.strides[0] // e, kb.strides[1] // e,
+        ptr(vb), vb.strides[0] // e, vb.strides[1] // e,
+        code, B, Hq, Hkv, D, Sq, Sk, ptr(qo_a), ptr(kvo_a), mask,
+        int(inputs.get("window_left", -1)), ptr(st_a), ptr(en_a), scale,
+        float(inputs.get("output_scale", 1.0)), ptr(sel_arr), count, ptr(out), int(nthreads))
+    if st != 0:
+        raise ValueError(f"oracle_prefill: {_ERRORS.get(st, st)}")
+    return out
 
 
 def merge_states(o, lse, sink=None):

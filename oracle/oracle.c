@@ -305,3 +305,159 @@ void oracle_merge_states(const double* o, const double* lse_s, int64_t S, int64_
   for (int64_t d = 0; d < D; ++d) out[d] /= Z;
   *lse = top + log2(W);
 }
+
+/*
+ * oracle_prefill: context attention of flashinfer.attention.prims_ts.batch_prefill
+ * (summary and Parameters).  One output row per (query row r, query head h).
+ *   - summary / Parameters q, k, v, qo_indptr, kv_indptr: fixed tensors are
+ *     [B, S, H, D] (row r = b * Sq + i, key row b * Sk + j); with both
+ *     cumulative offset tensors the rows are packed: request b owns query rows
+ *     qo[b] .. qo[b + 1] - 1 and key/value rows kvo[b] .. kvo[b + 1] - 1.
+ *     The key/value head of query head h is h / (Hq / Hkv).
+ *   - summary: causal masking is bottom-right aligned: query token i of a
+ *     request with Sq queries and Sk keys sits at diagonal p_i = Sk - Sq + i
+ *     and sees keys j <= p_i.  mask_type dense: every key j < Sk.
+ *   - summary / Parameters window_left: -1 disables the left window; otherwise
+ *     keys before p_i - window_left are dropped (at most window_left + 1 keys
+ *     per causal row, also when Sq < Sk).
+ *   - Parameters variable_window_token_starts / _ends: with mask_type
+ *     variable_window, query token i of request b sees exactly the keys
+ *     starts[b, i] .. ends[b, i] (inclusive; int32 [B, Sq], fixed shapes only).
+ *   - Parameters sm_scale (softmax scale) and output_scale (a factor on the
+ *     output).
+ * The softmax is the plain two-pass form in double precision.  A row with no
+ * visible key gives out = 0.  mask: 0 causal, 1 dense, 2 variable window.
+ */
+typedef struct {
+  const uint16_t* q;  int64_t q_sr, q_sh;
+  const uint16_t* k;  int64_t k_sr, k_sh;
+  const uint16_t* v;  int64_t v_sr, v_sh;
+  int dtype;
+  int64_t B, Hq, Hkv, D, Sq, Sk;             /* Sq, Sk: fixed lengths */
+  const int32_t* qo;  const int32_t* kvo;    /* packed offsets or NULL */
+  int mask;
+  int64_t wl;
+  const int32_t* starts;  const int32_t* ends;   /* [B, Sq] for mask 2 */
+  double scale, out_scale;
+} prefill_t;
+
+static void prefill_row(const prefill_t* pb, int64_t r, int64_t h, double* buf, double* out) {
+  const int64_t D = pb->D;
+  int64_t b, i, sq, sk, q0, k0;
+  if (pb->qo) {
+    b = 0;
+    while (b + 1 < pb->B && pb->qo[b + 1] <= r) ++b;
+    q0 = pb->qo[b];
+    k0 = pb->kvo[b];
+    sq = pb->qo[b + 1] - q0;
+    sk = pb->kvo[b + 1] - k0;
+  } else {
+    b = r / pb->Sq;
+    q0 = b * pb->Sq;
+    k0 = b * pb->Sk;
+    sq = pb->Sq;
+    sk = pb->Sk;
+  }
+  i = r - q0;
+  const int64_t kvh = h / (pb->Hq / pb->Hkv);
+  const int64_t diag = sk - sq + i;
+  int64_t lo, hi;
+  if (pb->mask == 2) {
+    lo = pb->starts[b * pb->Sq + i];
+    hi = pb->ends[b * pb->Sq + i];
+  } else {
+    hi = pb->mask == 0 ? diag : sk - 1;
+    lo = pb->wl < 0 ? 0 : diag - pb->wl;
+  }
+  if (lo < 0) lo = 0;
+  if (hi > sk - 1) hi = sk - 1;
+  double* qd = buf;
+  double* s = buf + D;
+  const uint16_t* qrow = pb->q + r * pb->q_sr + h * pb->q_sh;
+  for (int64_t d = 0; d < D; ++d) qd[d] = decode(qrow[d], pb->dtype);
+  double m = -INFINITY;
+  int64_t cnt = 0;
+  for (int64_t j = lo; j <= hi; ++j) {
+    const uint16_t* krow = pb->k + (k0 + j) * pb->k_sr + kvh * pb->k_sh;
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += qd[d] * decode(krow[d], pb->dtype);
+    s[cnt] = pb->scale * dot;
+    if (s[cnt] > m) m = s[cnt];
+    ++cnt;
+  }
+  for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+  if (cnt == 0) return;
+  double S = 0.0;
+  cnt = 0;
+  for (int64_t j = lo; j <= hi; ++j) {
+    const uint16_t* vrow = pb->v + (k0 + j) * pb->v_sr + kvh * pb->v_sh;
+    const double w = exp(s[cnt++] - m);
+    S += w;
+    for (int64_t d = 0; d < D; ++d) out[d] += w * decode(vrow[d], pb->dtype);
+  }
+  for (int64_t d = 0; d < D; ++d) out[d] = pb->out_scale * (out[d] / S);
+}
+
+/*
+ * Rows are (total query rows) x Hq; sel: NULL for all in row-major order
+ * r * Hq + h, else nsel such indices.  out: [count, D].  Returns ORACLE_OK or
+ * ORACLE_BAD_ARG.
+ */
+int oracle_prefill(const uint16_t* q, int64_t q_sr, int64_t q_sh,
+                   const uint16_t* k, int64_t k_sr, int64_t k_sh,
+                   const uint16_t* v, int64_t v_sr, int64_t v_sh,
+                   int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                   int64_t Sq, int64_t Sk, const int32_t* qo, const int32_t* kvo,
+                   int mask, int64_t window_left, const int32_t* starts, const int32_t* ends,
+                   double scale, double out_scale, const int64_t* sel, int64_t nsel,
+                   double* out, int nthreads) {
+  if (!q || !k || !v || !out || B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return ORACLE_BAD_ARG;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return ORACLE_BAD_ARG;
+  if ((qo == NULL) != (kvo == NULL) || mask < 0 || mask > 2 || window_left < -1) return ORACLE_BAD_ARG;
+  if (mask == 2 && (qo || !starts || !ends)) return ORACLE_BAD_ARG;
+  int64_t rows, kmax;
+  if (qo) {
+    if (qo[0] != 0 || kvo[0] != 0) return ORACLE_BAD_ARG;
+    kmax = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      if (qo[b + 1] < qo[b] || kvo[b + 1] < kvo[b]) return ORACLE_BAD_ARG;
+      if (kvo[b + 1] - kvo[b] > kmax) kmax = kvo[b + 1] - kvo[b];
+    }
+    rows = qo[B];
+  } else {
+    if (Sq < 1 || Sk < 1) return ORACLE_BAD_ARG;
+    rows = B * Sq;
+    kmax = Sk;
+  }
+  prefill_t pb = {q, q_sr, q_sh, k, k_sr, k_sh, v, v_sr, v_sh, dtype, B, Hq, Hkv, D, Sq, Sk,
+                  qo, kvo, mask, window_left, starts, ends, scale, out_scale};
+  const int64_t count = sel ? nsel : rows * Hq;
+  int status = ORACLE_OK;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(D + kmax + 1));
+    if (!buf) {
+#pragma omp atomic write
+      status = ORACLE_NO_MEMORY;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = 0; t < count; ++t) {
+      if (!buf) continue;
+      const int64_t idx = sel ? sel[t] : t;
+      const int64_t r = idx / Hq, h = idx % Hq;
+      if (r < 0 || r >= rows) {
+#pragma omp atomic write
+        status = ORACLE_BAD_ARG;
+        continue;
+      }
+      prefill_row(&pb, r, h, buf, out + t * D);
+    }
+    free(buf);
+  }
+  return status;
+}

@@ -590,3 +590,183 @@ def test_token_major_query_is_the_row_layout():
     o2, l2, _ = run(tm)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# context attention (batch_prefill: summary and Parameters)
+# ----------------------------------------------------------------------------
+def prefill_reference(inp):
+    """Dense torch brute force: fp64 torch.softmax over explicit boolean masks
+    per (request, query head), packed or fixed rows."""
+    q, k, v = inp["q"].double(), inp["k"].double(), inp["v"].double()
+    mask = inp.get("mask_type", "dense")
+    wl = inp.get("window_left", -1)
+    scale = inp.get("sm_scale") or 1.0 / math.sqrt(q.shape[-1])
+    osc = inp.get("output_scale", 1.0)
+    if inp.get("qo_indptr") is None:
+        B, Sq, Hq, D = q.shape
+        Sk = k.shape[1]
+        qs = [q[b] for b in range(B)]
+        ks = [k[b] for b in range(B)]
+        vs = [v[b] for b in range(B)]
+    else:
+        qo = inp["qo_indptr"].tolist()
+        kvo = inp["kv_indptr"].tolist()
+        B = len(qo) - 1
+        Hq, D = q.shape[1], q.shape[2]
+        qs = [q[qo[b]:qo[b + 1]] for b in range(B)]
+        ks = [k[kvo[b]:kvo[b + 1]] for b in range(B)]
+        vs = [v[kvo[b]:kvo[b + 1]] for b in range(B)]
+    g = Hq // k.shape[-2]
+    outs = []
+    for b in range(B):
+        sq, sk = qs[b].shape[0], ks[b].shape[0]
+        o = torch.zeros(sq, Hq, D, dtype=torch.float64)
+        j = torch.arange(sk)
+        for i in range(sq):
+            diag = sk - sq + i
+            if mask == "variable_window":
+                m = (j >= int(inp["window_starts"][b, i])) & (j <= int(inp["window_ends"][b, i]))
+            else:
+                m = (j <= diag) if mask == "causal" else torch.ones(sk, dtype=torch.bool)
+                if wl >= 0:
+                    m &= j >= diag - wl
+            if not bool(m.any()):
+                continue
+            for h in range(Hq):
+                s = scale * (ks[b][:, h // g] @ qs[b][i, h])
+                s = torch.where(m, s, torch.tensor(-math.inf, dtype=torch.float64))
+                o[i, h] = osc * (torch.softmax(s, 0) @ vs[b][:, h // g])
+        outs.append(o.reshape(-1, D))
+    return torch.cat(outs).numpy()
+
+
+def _prefill_golden(case):
+    gold = json.load(open(os.path.join(GOLD, "hand_worked_prefill.json")))
+    c = gold["common"]
+    dt = torch.bfloat16
+    q = torch.tensor([[[[1.0, 0.0]]] * case["Sq"]]).to(dt)
+    inp = dict(q=q, k=torch.tensor(c["k"], dtype=torch.float32).to(dt),
+               v=torch.tensor(c["v"], dtype=torch.float32).to(dt), mask_type=case["mask_type"],
+               window_left=case["window_left"], output_scale=case["output_scale"], sm_scale=1.0)
+    if "starts" in case:
+        inp["window_starts"] = torch.tensor(case["starts"], dtype=torch.int32)
+        inp["window_ends"] = torch.tensor(case["ends"], dtype=torch.int32)
+    return inp
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLD, "hand_worked_prefill.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_prefill_hand_worked(case):
+    inp = _prefill_golden(case)
+    out = oracle.prefill(inp)
+    env = {"__builtins__": {}, "e": math.e}
+    want = np.array([[eval(x, env) for x in row] for row in case["out"]], dtype=np.float64)
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(prefill_reference(inp), want, rtol=0, atol=1e-14)
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(B=st.integers(1, 3), g=st.sampled_from([1, 2, 3]), Hkv=st.integers(1, 2),
+       D=st.sampled_from([1, 4, 8]), mask=st.sampled_from(["causal", "dense", "variable_window"]),
+       wl=st.sampled_from([-1, 0, 2, 5]), packed=st.booleans(),
+       osc=st.sampled_from([1.0, 0.5]), dtype=st.sampled_from(["bf16", "fp16"]),
+       seed=st.integers(0, 10_000), data=st.data())
+def test_prefill_brute_force(B, g, Hkv, D, mask, wl, packed, osc, dtype, seed, data):
+    """Masks, windows, GQA, packed rows and the output scale against the torch
+    brute force (variable windows only with fixed shapes, as documented)."""
+    if mask == "variable_window":
+        packed = False
+        wl = -1
+    if packed:
+        ql = data.draw(st.lists(st.integers(0, 6), min_size=B, max_size=B))
+        kl = data.draw(st.lists(st.integers(0, 9), min_size=B, max_size=B))
+        if sum(ql) == 0:
+            ql[0] = 1
+        inp = workloads.make_prefill_case(B=B, Hq=g * Hkv, Hkv=Hkv, D=D, q_lens=ql, kv_lens=kl,
+                                          mask_type=mask, window_left=wl, output_scale=osc,
+                                          dtype=dtype, seed=seed, pad_heads=1)
+    else:
+        Sq = data.draw(st.integers(1, 6))
+        Sk = data.draw(st.integers(1, 9))
+        win = None
+        if mask == "variable_window":
+            st_ = [[data.draw(st.integers(0, Sk - 1)) for _ in range(Sq)] for _ in range(B)]
+            en_ = [[data.draw(st.integers(s, Sk - 1)) for s in row] for row in st_]
+            win = (st_, en_)
+        inp = workloads.make_prefill_case(B=B, Sq=Sq, Sk=Sk, Hq=g * Hkv, Hkv=Hkv, D=D,
+                                          mask_type=mask, window_left=wl, output_scale=osc,
+                                          window=win, dtype=dtype, seed=seed, pad_heads=1)
+    np.testing.assert_allclose(oracle.prefill(inp), prefill_reference(inp), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_equals_decode_definition_on_one_page_caches():
+    """Causal context attention of Sq queries over Sk keys is the decode's
+    bottom-right causal multi-token definition (q_len_per_req = Sq) on a cache
+    holding each request's keys in one page: two independent definitions."""
+    B, Sq, Sk, Hq, Hkv, D = 3, 4, 11, 6, 2, 8
+    for wl in (-1, 3):
+        p = workloads.make_prefill_case(B=B, Sq=Sq, Sk=Sk, Hq=Hq, Hkv=Hkv, D=D, mask_type="causal",
+                                        window_left=wl, seed=8)
+        dec = dict(q=p["q"].reshape(B * Sq, Hq, D), k_cache=p["k"].transpose(1, 2).contiguous(),
+                   v_cache=p["v"].transpose(1, 2).contiguous(),
+                   block_tables=torch.arange(B, dtype=torch.int32).view(B, 1),
+                   seq_lens_kv=torch.full((B,), Sk, dtype=torch.int32), sinks=None,
+                   scale=p["sm_scale"], q_len_per_req=Sq, window_left=wl)
+        out_d, _, _ = oracle.decode(dec)
+        np.testing.assert_allclose(oracle.prefill(p), out_d, rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_zero_query_window_counts():
+    """q = 0: every visible key weighs the same, so the output is the mean of
+    the visible values; with a window a causal row keeps min(window_left + 1,
+    p_i + 1) keys (summary), also when Sq < Sk."""
+    B, Sq, Sk, D = 2, 3, 8, 4
+    for wl in (-1, 0, 2, 20):
+        p = workloads.make_prefill_case(B=B, Sq=Sq, Sk=Sk, Hq=2, Hkv=1, D=D, mask_type="causal",
+                                        window_left=wl, seed=9)
+        p["q"] = torch.zeros_like(p["q"])
+        out = oracle.prefill(p).reshape(B, Sq, 2, D)
+        v = p["v"].double()
+        for b in range(B):
+            for i in range(Sq):
+                diag = Sk - Sq + i
+                cnt = diag + 1 if wl < 0 else min(wl + 1, diag + 1)
+                np.testing.assert_allclose(out[b, i, 0], v[b, diag + 1 - cnt:diag + 1, 0].mean(0).numpy(),
+                                           atol=1e-14, rtol=0)
+
+
+def test_prefill_variable_window_equal_to_causal_window():
+    """variable_window bounds set to [p_i - window_left, p_i] give the causal
+    window's result."""
+    B, Sq, Sk, wl = 2, 5, 9, 2
+    p = workloads.make_prefill_case(B=B, Sq=Sq, Sk=Sk, Hq=4, Hkv=2, D=8, mask_type="causal",
+                                    window_left=wl, seed=10)
+    starts = [[max(0, Sk - Sq + i - wl) for i in range(Sq)] for _ in range(B)]
+    ends = [[Sk - Sq + i for i in range(Sq)] for _ in range(B)]
+    vw = dict(p, mask_type="variable_window", window_left=-1,
+              window_starts=torch.tensor(starts, dtype=torch.int32),
+              window_ends=torch.tensor(ends, dtype=torch.int32))
+    np.testing.assert_array_equal(oracle.prefill(p), oracle.prefill(vw))
+
+
+def test_prefill_packed_equals_per_request_fixed():
+    """Packed rows equal fixed calls on each request alone."""
+    ql, kl = (3, 1, 4), (5, 1, 9)
+    for mask in ("causal", "dense"):
+        p = workloads.make_prefill_case(B=3, Hq=4, Hkv=2, D=8, q_lens=ql, kv_lens=kl,
+                                        mask_type=mask, window_left=2, seed=12)
+        out = oracle.prefill(p)
+        qo, kvo = p["qo_indptr"].tolist(), p["kv_indptr"].tolist()
+        for b in range(3):
+            one = dict(p, q=p["q"][qo[b]:qo[b + 1]].unsqueeze(0),
+                       k=p["k"][kvo[b]:kvo[b + 1]].unsqueeze(0),
+                       v=p["v"][kvo[b]:kvo[b + 1]].unsqueeze(0), qo_indptr=None, kv_indptr=None)
+            np.testing.assert_array_equal(out[qo[b] * 4:qo[b + 1] * 4], oracle.prefill(one))
+
+
+def test_prefill_gqa_equals_mha():
+    p = workloads.make_prefill_case(B=2, Sq=4, Sk=7, Hq=6, Hkv=2, D=8, mask_type="causal", seed=13)
+    mha = dict(p, k=p["k"].repeat_interleave(3, dim=2).contiguous(),
+               v=p["v"].repeat_interleave(3, dim=2).contiguous())
+    np.testing.assert_array_equal(oracle.prefill(p), oracle.prefill(mha))

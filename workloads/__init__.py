@@ -22,7 +22,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_config", "make_case", "seq_lens_of"]
+__all__ = ["Workload", "CONFIGS", "make_config", "make_case", "seq_lens_of", "make_prefill_case",
+           "PREFILL_CONFIGS", "make_prefill_config"]
 
 _DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
@@ -229,3 +230,74 @@ def make_case(B: int = 2, Hq: int = 4, Hkv: int = 2, D: int = 64, page_size: int
                 q_len_per_req=q_len_per_req, window_left=window_left, return_lse=True,
                 qo_indptr=qo_indptr, mask_type=mask_type, out_scale=out_scale)
 
+
+
+def make_prefill_case(B: int = 2, Sq: int = 5, Sk: int = 9, Hq: int = 4, Hkv: int = 2,
+                      D: int = 128, dtype: str = "bf16", value_std: float = 1.0,
+                      q_lens: Optional[Sequence[int]] = None,
+                      kv_lens: Optional[Sequence[int]] = None, mask_type: str = "causal",
+                      window_left: int = -1, output_scale: float = 1.0,
+                      window: Optional[Sequence[Sequence[int]]] = None, seed: int = 0,
+                      pad_heads: int = 0) -> dict:
+    """Inputs of one context-attention (prefill) call (batch_prefill's layout).
+
+    Fixed: q [B, Sq, Hq, D], k and v [B, Sk, Hkv, D].  Packed (q_lens and
+    kv_lens given): q [sum q_lens, Hq, D], k and v [sum kv_lens, Hkv, D] with
+    qo_indptr / kv_indptr (cumulative, B + 1 entries).  ``window`` =
+    (starts, ends) as [B][Sq] nested lists gives the variable_window bounds.
+    ``pad_heads`` makes q, k and v head slices of wider tensors (free strides).
+    Draw order: q, k, v.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    dt = _DTYPES[dtype]
+
+    def draw(shape):
+        full = list(shape)
+        full[-2] += pad_heads
+        x = (torch.randn(tuple(full), generator=gen) * value_std).to(dt)
+        return x[..., pad_heads:, :] if pad_heads else x
+
+    d = dict(mask_type=mask_type, window_left=window_left, output_scale=output_scale,
+             sm_scale=1.0 / math.sqrt(D))
+    if q_lens is not None:
+        assert kv_lens is not None and len(q_lens) == len(kv_lens) == B
+        qo = torch.zeros(B + 1, dtype=torch.int32)
+        kvo = torch.zeros(B + 1, dtype=torch.int32)
+        qo[1:] = torch.cumsum(torch.tensor(list(q_lens)), 0).to(torch.int32)
+        kvo[1:] = torch.cumsum(torch.tensor(list(kv_lens)), 0).to(torch.int32)
+        d.update(q=draw((int(qo[-1]), Hq, D)), k=draw((int(kvo[-1]), Hkv, D)),
+                 v=draw((int(kvo[-1]), Hkv, D)), qo_indptr=qo, kv_indptr=kvo,
+                 max_seq_len_q=max(1, max(q_lens)))
+    else:
+        d.update(q=draw((B, Sq, Hq, D)), k=draw((B, Sk, Hkv, D)), v=draw((B, Sk, Hkv, D)))
+    if window is not None:
+        d["window_starts"] = torch.tensor(window[0], dtype=torch.int32).reshape(B, Sq)
+        d["window_ends"] = torch.tensor(window[1], dtype=torch.int32).reshape(B, Sq)
+    return d
+
+
+# Context-attention (prefill) workloads measured and parity-tested beside the
+# decode: a fixed causal batch at head_dim 128 and 256, a packed ragged batch
+# and a windowed one.  Seeds 2001..2004.
+PREFILL_CONFIGS = {
+    "prefill_causal_d128": dict(B=4, Sq=4096, Sk=4096, Hq=32, Hkv=8, D=128, mask_type="causal",
+                                seed=2001),
+    "prefill_causal_d256": dict(B=4, Sq=4096, Sk=4096, Hq=16, Hkv=4, D=256, mask_type="causal",
+                                seed=2002),
+    "prefill_packed_d128": dict(B=8, Hq=32, Hkv=8, D=128, mask_type="causal", seed=2003,
+                                lens=(512, 4096)),
+    "prefill_window_d128": dict(B=4, Sq=4096, Sk=4096, Hq=32, Hkv=8, D=128, mask_type="causal",
+                                window_left=1023, seed=2004),
+}
+
+
+def make_prefill_config(name: str) -> dict:
+    """Draw one prefill workload of PREFILL_CONFIGS (packed lengths uniform in
+    the stated range, equal query and key lengths per request)."""
+    c = dict(PREFILL_CONFIGS[name])
+    lens = c.pop("lens", None)
+    if lens is not None:
+        g = torch.Generator().manual_seed(c["seed"] + 100000)
+        n = torch.randint(lens[0], lens[1] + 1, (c["B"],), generator=g).tolist()
+        c.update(q_lens=n, kv_lens=n)
+    return make_prefill_case(**c)
