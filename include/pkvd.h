@@ -72,8 +72,9 @@ typedef enum {
 /* Mask of the query rows of a request (batch_decode_with_paged_kv_cache,
  * Parameters / mask_type). */
 typedef enum {
-  PKVD_MASK_CAUSAL = 0, /* row i sees keys up to its diagonal n - Lq_b + i */
-  PKVD_MASK_DENSE = 1   /* every row sees keys up to n - 1 */
+  PKVD_MASK_CAUSAL = 0,          /* row i sees keys up to its diagonal n - Lq_b + i */
+  PKVD_MASK_DENSE = 1,           /* every row sees keys up to n - 1 */
+  PKVD_MASK_VARIABLE_WINDOW = 2  /* pkvd_prefill only: per-query [start, end] bounds */
 } pkvd_mask;
 
 /*
@@ -309,6 +310,61 @@ int pkvd_decode_plan(const pkvd_tensor* q, const pkvd_tensor* k_cache,
  * call, otherwise.
  */
 void pkvd_reload_tuning(void);
+
+/*
+ * pkvd_prefill -- context attention: every query row of a request attends to
+ * that request's own keys, the operation of
+ * flashinfer.attention.prims_ts.batch_prefill (summary, Parameters).  For
+ * request b with Sq_b queries and Sk_b keys, query token i, query head h:
+ *   diagonal p = Sk_b - Sq_b + i (bottom-right aligned), visible keys j with
+ *     max(0, p - window_left) <= j <= p        (PKVD_MASK_CAUSAL)
+ *     max(0, p - window_left) <= j <= Sk_b - 1 (PKVD_MASK_DENSE)
+ *     starts[b, i] <= j <= ends[b, i]          (PKVD_MASK_VARIABLE_WINDOW)
+ *   (no lower bound from the window when window_left == -1);
+ *   out[row, h, :] = output_scale * softmax_j(sm_scale * q . k_j) . v_j with
+ *   kv head h / (Hq / Hkv); a row with no visible key gives 0.
+ *
+ *   q        bf16 or fp16: fixed (B, Sq, Hq, D) or packed (total_q, Hq, D);
+ *            head_dim innermost and dense, rows 16-byte aligned, the other
+ *            strides free (a fixed tensor must step its S rows at one stride).
+ *   k, v     q's dtype: fixed (B, Sk, Hkv, D) or packed (total_kv, Hkv, D),
+ *            the same layout rules; Hq % Hkv == 0.
+ *   qo_indptr, kv_indptr  NULL (fixed) or both int32 (B + 1,) contiguous
+ *            device tensors of cumulative offsets: request b owns query rows
+ *            qo_indptr[b] .. qo_indptr[b + 1] - 1 and key/value rows
+ *            kv_indptr[b] .. kv_indptr[b + 1] - 1 (device data, not checked:
+ *            offsets are clamped into the tensors, query counts to
+ *            max_seq_len_q).
+ *   max_seq_len_q  packed: the largest query count of any request (sizes the
+ *            grid); fixed: ignored.
+ *   mask     PKVD_MASK_CAUSAL, PKVD_MASK_DENSE or PKVD_MASK_VARIABLE_WINDOW
+ *            (fixed shapes only, window_left must be -1).
+ *   window_left  -1 or >= 0.
+ *   window_starts, window_ends  variable window: int32 (B, Sq) contiguous
+ *            device tensors, 0 <= starts <= ends < Sk (clamped on the device).
+ *   sm_scale, output_scale  finite.
+ *   out      caller-owned, q's shape, contiguous, 16-byte aligned; bf16,
+ *            fp16 or fp32 (out_dtype).
+ * Supported: D in {128, 256}.  Work is only enqueued on `stream`; nothing is
+ * allocated and nothing is read back.  Errors as for pkvd_decode.
+ */
+typedef struct {
+  const pkvd_tensor* q;
+  const pkvd_tensor* k;
+  const pkvd_tensor* v;
+  const pkvd_tensor* qo_indptr;
+  const pkvd_tensor* kv_indptr;
+  int32_t max_seq_len_q;
+  int32_t mask;
+  int32_t window_left;
+  const pkvd_tensor* window_starts;
+  const pkvd_tensor* window_ends;
+  float sm_scale;
+  float output_scale;
+  pkvd_tensor* out;
+} pkvd_prefill_args;
+
+int pkvd_prefill(const pkvd_prefill_args* args, void* stream);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char* pkvd_last_error(void);

@@ -22,7 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["decode", "batch_decode_with_paged_kv_cache", "bind_decode", "merge_states", "plan",
+__all__ = ["decode", "batch_decode_with_paged_kv_cache", "batch_prefill", "bind_decode",
+           "merge_states", "plan",
            "plan_ex", "schedule_stats", "workspace_bytes", "reserve_workspace", "set_workspace",
            "reload_tuning",
            "library_path", "PkvdError"]
@@ -51,7 +52,17 @@ class _DecodeArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
-_MASKS = {"causal": 0, "dense": 1}
+_MASKS = {"causal": 0, "dense": 1, "variable_window": 2}
+
+
+class _PrefillArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.POINTER(_Tensor)), ("k", ctypes.POINTER(_Tensor)),
+                ("v", ctypes.POINTER(_Tensor)), ("qo_indptr", ctypes.POINTER(_Tensor)),
+                ("kv_indptr", ctypes.POINTER(_Tensor)), ("max_seq_len_q", ctypes.c_int32),
+                ("mask", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_starts", ctypes.POINTER(_Tensor)),
+                ("window_ends", ctypes.POINTER(_Tensor)), ("sm_scale", ctypes.c_float),
+                ("output_scale", ctypes.c_float), ("out", ctypes.POINTER(_Tensor))]
 
 
 class PkvdError(RuntimeError):
@@ -99,6 +110,8 @@ def _load():
     lib.pkvd_set_workspace.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     lib.pkvd_reload_tuning.restype = None
     lib.pkvd_reload_tuning.argtypes = []
+    lib.pkvd_prefill.restype = ctypes.c_int
+    lib.pkvd_prefill.argtypes = [ctypes.POINTER(_PrefillArgs), ctypes.c_void_p]
     lib.pkvd_schedule_stats.restype = ctypes.c_int
     lib.pkvd_schedule_stats.argtypes = [A, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_int64 * 8)]
@@ -382,6 +395,57 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, sinks: Optional[torch.Tensor]
                                     ctypes.c_void_p(stream))
     _check(st)
     return (v_out, s_out) if s_out is not None else v_out
+
+
+def batch_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                  qo_indptr: Optional[torch.Tensor] = None,
+                  kv_indptr: Optional[torch.Tensor] = None, mask_type: str = "dense",
+                  window_left: int = -1,
+                  variable_window_token_starts: Optional[torch.Tensor] = None,
+                  variable_window_token_ends: Optional[torch.Tensor] = None,
+                  sm_scale: Optional[float] = None, output_scale: float = 1.0, out_dtype=None,
+                  out: Optional[torch.Tensor] = None, max_seq_len_q: Optional[int] = None,
+                  stream=None) -> torch.Tensor:
+    """Context attention over fixed [B, S, H, D] or packed [total, H, D] q, k, v
+    (the argument set of flashinfer.attention.prims_ts.batch_prefill; pkvd_prefill).
+
+    mask_type "dense", "causal" (bottom-right) or "variable_window" (fixed
+    shapes; inclusive int32 [B, Sq] bounds).  With packed rows the largest
+    query count sizes the grid: pass max_seq_len_q, or it is derived from
+    qo_indptr here (a device-to-host read).  Returns out (q's shape, out_dtype
+    or out's dtype or q's).  Enqueued on torch's current stream; never
+    synchronises otherwise.
+    """
+    dev = q.device
+    _same_device(dev, (("q", q), ("k", k), ("v", v), ("qo_indptr", qo_indptr),
+                       ("kv_indptr", kv_indptr), ("out", out),
+                       ("variable_window_token_starts", variable_window_token_starts),
+                       ("variable_window_token_ends", variable_window_token_ends)))
+    if (qo_indptr is None) != (kv_indptr is None):
+        raise ValueError("qo_indptr and kv_indptr are given together")
+    if qo_indptr is not None and max_seq_len_q is None:
+        qo = qo_indptr.cpu()
+        max_seq_len_q = max(1, int((qo[1:] - qo[:-1]).max())) if qo.numel() > 1 else 1
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    descs = [_desc(t) for t in (q, k, v, qo_indptr, kv_indptr, variable_window_token_starts,
+                                variable_window_token_ends, out)]
+    P = ctypes.POINTER(_Tensor)
+    ptr = lambda d: ctypes.pointer(d) if d is not None else P()
+    x = _PrefillArgs()
+    (x.q, x.k, x.v, x.qo_indptr, x.kv_indptr, x.window_starts, x.window_ends, x.out) = \
+        [ptr(d) for d in descs]
+    x.max_seq_len_q = int(max_seq_len_q or 0)
+    x.mask = _MASKS[mask_type]
+    x.window_left = int(window_left)
+    x.sm_scale = float(sm_scale)
+    x.output_scale = float(output_scale)
+    with torch.cuda.device(dev):
+        st = _lib.pkvd_prefill(ctypes.byref(x), ctypes.c_void_p(_stream_of(stream, dev)))
+    _check(st)
+    return out
 
 
 def plan(q, k_cache, block_tables, q_len_per_req: int = 1, window_left: int = -1) -> dict:

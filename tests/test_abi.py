@@ -418,3 +418,106 @@ def test_static_entry_point_rejects_plans_beyond_its_workspace():
                                     None)
     assert st == 3, lib.pkvd_last_error()
     assert b"static workspace" in lib.pkvd_last_error()
+
+
+# ----------------------------------------------------------------------------
+# context attention (pkvd_prefill): argument checks before any launch
+# ----------------------------------------------------------------------------
+def prefill_call(inp, **over):
+    """pkvd_prefill over fake, aligned addresses (only rejected calls)."""
+    d = dict(inp)
+    d.update(over)
+    base = 1 << 32
+    names = ["q", "k", "v", "qo_indptr", "kv_indptr", "window_starts", "window_ends", "out"]
+    P = ctypes.POINTER(pk._Tensor)
+    x = pk._PrefillArgs()
+    keep = []
+    for i, name in enumerate(names):
+        t = d.get(name)
+        if t is None:
+            setattr(x, name, P())
+            continue
+        dd = pk._desc(t)
+        dd.data = base + (i << 24)
+        keep.append(dd)
+        setattr(x, name, ctypes.pointer(dd))
+    x.max_seq_len_q = int(d.get("max_seq_len_q", 0) or 0)
+    x.mask = int(d.get("mask", 0))
+    x.window_left = int(d.get("window_left", -1))
+    x.sm_scale = float(d.get("sm_scale", 0.1))
+    x.output_scale = float(d.get("output_scale", 1.0))
+    return pk._lib.pkvd_prefill(ctypes.byref(x), None)
+
+
+def prefill_fixed():
+    inp = workloads.make_prefill_case(B=2, Sq=5, Sk=9, Hq=4, Hkv=2, D=128)
+    inp["out"] = torch.empty(inp["q"].shape, dtype=torch.float32)
+    return inp
+
+
+def prefill_packed():
+    inp = workloads.make_prefill_case(B=2, Hq=4, Hkv=2, D=128, q_lens=(3, 2), kv_lens=(4, 6))
+    inp["out"] = torch.empty(inp["q"].shape, dtype=torch.bfloat16)
+    return inp
+
+
+PREFILL_BAD = [
+    ("q_dtype", prefill_fixed, lambda i: dict(q=i["q"].float())),
+    ("kv_dtype", prefill_fixed, lambda i: dict(k=i["k"].half())),
+    ("kv_shape_mismatch", prefill_fixed, lambda i: dict(v=i["v"][:, :8].contiguous())),
+    ("batch_mismatch", prefill_fixed, lambda i: dict(k=i["k"][:1], v=i["v"][:1])),
+    ("heads_not_multiple", prefill_fixed,
+     lambda i: dict(q=torch.zeros(2, 5, 3, 128, dtype=torch.bfloat16),
+                    out=torch.zeros(2, 5, 3, 128))),
+    ("q_3d_fixed", prefill_fixed, lambda i: dict(q=i["q"][0], out=i["out"][0])),
+    ("head_dim_strided", prefill_fixed,
+     lambda i: dict(q=i["q"].transpose(2, 3).contiguous().transpose(2, 3))),
+    ("rows_not_one_stride", prefill_fixed, lambda i: dict(k=torch.zeros(2, 9, 3, 128,
+                                                                        dtype=torch.bfloat16)
+                                                          .transpose(1, 0).contiguous()
+                                                          .transpose(1, 0)[:, :, :2],
+                                                          v=i["v"])),
+    ("mask_value", prefill_fixed, dict(mask=3)),
+    ("window_below_minus_one", prefill_fixed, dict(window_left=-2)),
+    ("varwin_missing_bounds", prefill_fixed, dict(mask=2)),
+    ("varwin_with_window", prefill_fixed,
+     lambda i: dict(mask=2, window_left=3, window_starts=torch.zeros(2, 5, dtype=torch.int32),
+                    window_ends=torch.zeros(2, 5, dtype=torch.int32))),
+    ("varwin_bounds_shape", prefill_fixed,
+     lambda i: dict(mask=2, window_starts=torch.zeros(2, 4, dtype=torch.int32),
+                    window_ends=torch.zeros(2, 4, dtype=torch.int32))),
+    ("varwin_packed", prefill_packed,
+     lambda i: dict(mask=2, window_starts=torch.zeros(2, 3, dtype=torch.int32),
+                    window_ends=torch.zeros(2, 3, dtype=torch.int32), max_seq_len_q=3)),
+    ("scale_nan", prefill_fixed, dict(sm_scale=float("nan"))),
+    ("output_scale_inf", prefill_fixed, dict(output_scale=float("inf"))),
+    ("out_shape", prefill_fixed, lambda i: dict(out=i["out"][:, :4].contiguous())),
+    ("out_dtype", prefill_fixed, lambda i: dict(out=i["out"].double())),
+    ("missing_out", prefill_fixed, dict(out=None)),
+    ("only_qo_indptr", prefill_packed, lambda i: dict(kv_indptr=None, max_seq_len_q=3)),
+    ("indptr_dtype", prefill_packed, lambda i: dict(qo_indptr=i["qo_indptr"].long(),
+                                                     max_seq_len_q=3)),
+    ("indptr_lengths_differ", prefill_packed, lambda i: dict(kv_indptr=i["kv_indptr"][:2],
+                                                              max_seq_len_q=3)),
+    ("packed_without_max_len", prefill_packed, dict(max_seq_len_q=0)),
+    ("packed_4d_q", prefill_packed, lambda i: dict(q=i["q"].reshape(1, 5, 4, 128),
+                                                   out=i["out"].reshape(1, 5, 4, 128),
+                                                   max_seq_len_q=3)),
+]
+
+
+@pytest.mark.parametrize("name,make,mut", PREFILL_BAD, ids=[b[0] for b in PREFILL_BAD])
+def test_prefill_invalid_arguments(name, make, mut):
+    inp = make()
+    over = mut(inp) if callable(mut) else mut
+    st = prefill_call(inp, **over)
+    assert st == 1, (name, st, pk._lib.pkvd_last_error())
+    assert pk._lib.pkvd_last_error()
+
+
+@pytest.mark.parametrize("D", [64, 96])
+def test_prefill_unsupported_head_dim(D):
+    inp = workloads.make_prefill_case(B=1, Sq=2, Sk=3, Hq=2, Hkv=1, D=D)
+    inp["out"] = torch.empty(inp["q"].shape, dtype=torch.bfloat16)
+    assert prefill_call(inp) == 2
+    assert pk._lib.pkvd_last_error()

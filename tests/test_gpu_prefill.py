@@ -1,0 +1,113 @@
+"""GPU parity of context attention (pkvd_prefill) against the fp64 oracle:
+fixed and packed rows, causal / dense / windowed / variable-window masks,
+head_dim 128 and 256, GQA, bf16 / fp16 inputs, bf16 / fp16 / fp32 outputs and
+the output scale (flashinfer.attention.prims_ts.batch_prefill, summary and
+Parameters).
+
+Tolerances as for the decode: max |out - ref| <= 2e-2 and <= 1e-2 relative
+to the largest reference output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+OUT_ATOL = 2e-2
+REL = 1e-2
+ODT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def run(inp, out_dtype=None):
+    import paged_kv_decode_12_amd as pk
+    dev = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    out = pk.batch_prefill(dev["q"], dev["k"], dev["v"], qo_indptr=dev.get("qo_indptr"),
+                           kv_indptr=dev.get("kv_indptr"), mask_type=dev["mask_type"],
+                           window_left=dev["window_left"],
+                           variable_window_token_starts=dev.get("window_starts"),
+                           variable_window_token_ends=dev.get("window_ends"),
+                           sm_scale=dev["sm_scale"], output_scale=dev["output_scale"],
+                           out_dtype=out_dtype, max_seq_len_q=dev.get("max_seq_len_q"))
+    torch.cuda.synchronize()
+    assert out.shape == inp["q"].shape
+    return out.float().cpu().numpy().reshape(-1, out.shape[-1])
+
+
+def compare(name, got, ref):
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    err = np.abs(got - ref)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    msg = f"{name}: max|err|={err.max():.3e} max|ref|={scale:.3e} rel={err.max() / scale:.3e}"
+    log(msg)
+    assert err.max() <= OUT_ATOL, msg
+    assert err.max() / scale <= REL, msg
+
+
+CASES = []
+for D in (128, 256):
+    for mask, wl in (("causal", -1), ("dense", -1), ("causal", 37), ("dense", 5)):
+        CASES.append(dict(D=D, B=2, Sq=150, Sk=150, Hq=4, Hkv=2, mask_type=mask, window_left=wl))
+    CASES.append(dict(D=D, B=2, Sq=70, Sk=333, Hq=4, Hkv=1, mask_type="causal", window_left=-1))
+    CASES.append(dict(D=D, B=1, Sq=200, Sk=90, Hq=2, Hkv=2, mask_type="causal", window_left=-1))
+    CASES.append(dict(D=D, B=3, Hq=6, Hkv=3, q_lens=(1, 0, 130), kv_lens=(40, 7, 260),
+                      mask_type="causal", window_left=-1))
+    CASES.append(dict(D=D, B=3, Hq=4, Hkv=4, q_lens=(65, 17, 3), kv_lens=(65, 0, 300),
+                      mask_type="dense", window_left=20))
+CASES.append(dict(D=128, B=1, Sq=1, Sk=1, Hq=1, Hkv=1, mask_type="causal", window_left=-1))
+CASES.append(dict(D=128, B=2, Sq=64, Sk=64, Hq=8, Hkv=2, mask_type="causal", window_left=0,
+                  dtype="fp16", value_std=0.5))
+CASES.append(dict(D=256, B=2, Sq=33, Sk=129, Hq=2, Hkv=1, mask_type="dense", window_left=-1,
+                  dtype="fp16", pad_heads=2))
+
+
+def _id(c):
+    return ",".join(f"{k}={v}" for k, v in c.items())
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
+def test_prefill_cases(case):
+    inp = workloads.make_prefill_case(seed=31, output_scale=0.8, **case)
+    ref = oracle.prefill(inp)
+    for odt in (None, "fp32"):
+        log(f"[prefill] {_id(case)} out={odt}")
+        got = run(inp, None if odt is None else ODT[odt])
+        compare(f"{_id(case)}/{odt}", got, ref)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_variable_window(D):
+    """Per-query inclusive [start, end] bounds (fixed shapes), random bounds and
+    bounds equal to the causal window."""
+    g = torch.Generator().manual_seed(D)
+    B, Sq, Sk = 2, 100, 180
+    starts = torch.randint(0, Sk, (B, Sq), generator=g)
+    ends = torch.minimum(starts + torch.randint(0, 90, (B, Sq), generator=g),
+                         torch.tensor(Sk - 1))
+    inp = workloads.make_prefill_case(B=B, Sq=Sq, Sk=Sk, Hq=4, Hkv=2, D=D,
+                                      mask_type="variable_window",
+                                      window=(starts.tolist(), ends.tolist()), seed=41)
+    compare(f"varwin/D{D}", run(inp), oracle.prefill(inp))
+
+
+@pytest.mark.parametrize("name", list(workloads.PREFILL_CONFIGS))
+def test_prefill_configs_sampled(name):
+    """The measured prefill workloads at full size: sampled (row, head) pairs
+    (first and last rows of requests included) against the oracle."""
+    inp = workloads.make_prefill_config(name)
+    rows, Hq = inp["q"].shape[0] * (inp["q"].shape[1] if inp["q"].dim() == 4 else 1), \
+        inp["q"].shape[-2]
+    g = torch.Generator().manual_seed(7)
+    sel = set(torch.randint(0, rows * Hq, (400,), generator=g).tolist())
+    sel |= {0, Hq - 1, rows * Hq - 1, (rows - 1) * Hq}
+    sel = sorted(sel)
+    ref = oracle.prefill(inp, sel=sel)
+    log(f"[prefill_cfg] {name} rows={rows}")
+    got = run(inp)
+    compare(name, got[sel], ref)
