@@ -55,8 +55,16 @@ def kv_bytes(inp) -> int:
     return 2 * D * elt * Hkv * keys
 
 
-def kernel_source_hash() -> str:
-    """SHA-256 over the library's sources and build flags (what the counters measured)."""
+# sources each kernel family is built from (its counters stay valid while these do not change)
+PREFILL_ONLY = ("prefill_kernel.hip", "prefill_args.h", "prefill_api.cpp")
+PREFILL_SHARED = ("engine_mfma.h", "decode_common.h", "decode_args.h", "schedule.h", "api_util.h",
+                  "pkvd.h")
+
+
+def kernel_source_hash(op: str = "decode") -> str:
+    """SHA-256 over the sources and build flags one kernel family is built
+    from (what its counters measured): op "decode" (decode and merge kernels)
+    or "prefill"."""
     import importlib.util
     spec = importlib.util.spec_from_file_location(
         "_pkvd_build", os.path.join(ROOT, "paged_kv_decode_12_amd", "build.py"))
@@ -64,8 +72,13 @@ def kernel_source_hash() -> str:
     spec.loader.exec_module(b)
     h = hashlib.sha256()
     for path in b.SOURCES + b.HEADERS:
+        name = os.path.basename(path)
+        if op == "prefill" and name not in PREFILL_ONLY + PREFILL_SHARED:
+            continue
+        if op == "decode" and name in PREFILL_ONLY:
+            continue
         with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+            h.update(name.encode() + b"\0" + f.read())
     h.update(" ".join(b.FLAGS[:-2]).encode())      # flags minus the machine-specific -I paths
     return h.hexdigest()
 
@@ -148,6 +161,101 @@ def bench_merge_states(args):
                       "config": {"S": S, "rows": R, "heads": H, "D": D, "dtype": "bf16",
                                  "sinks": True},
                       "steps": args.steps, "max_abs_err_sampled": err}), flush=True)
+
+
+def prefill_flops(inp) -> int:
+    """Algorithmic flops of one context-attention call: 4 * D per visible
+    (query row, query head, key) triple (2 D for q . k, 2 D for p . v)."""
+    import numpy as np
+    q, k = inp["q"], inp["k"]
+    D, Hq = q.shape[-1], q.shape[-2]
+    mask, wl = inp["mask_type"], inp["window_left"]
+    if inp.get("qo_indptr") is not None:
+        qo, kvo = inp["qo_indptr"].tolist(), inp["kv_indptr"].tolist()
+        lens = [(qo[b + 1] - qo[b], kvo[b + 1] - kvo[b]) for b in range(len(qo) - 1)]
+    else:
+        lens = [(q.shape[1], k.shape[1])] * q.shape[0]
+    pairs = 0
+    for b, (sq, sk) in enumerate(lens):
+        i = np.arange(sq, dtype=np.int64)
+        if mask == "variable_window":
+            lo = np.maximum(inp["window_starts"][b].numpy().astype(np.int64), 0)
+            hi = np.minimum(inp["window_ends"][b].numpy().astype(np.int64), sk - 1)
+        else:
+            p = sk - sq + i
+            hi = np.minimum(p if mask == "causal" else np.full_like(i, sk - 1), sk - 1)
+            lo = np.zeros_like(i) if wl < 0 else np.maximum(p - wl, 0)
+        pairs += int(np.maximum(hi - lo + 1, 0).sum())
+    return 4 * D * Hq * pairs
+
+
+def bench_prefill(args):
+    """Context attention (pkvd_prefill) on one of the prefill workloads:
+    TFLOP/s of algorithmic flops (4 D per visible query-key pair and head)
+    against the dense bf16/fp16 MFMA peak, HIP events around `steps`
+    back-to-back calls on the launch stream; sampled rows checked against the
+    oracle, which is also timed on those rows as the CPU baseline."""
+    import numpy as np
+    import torch
+    import workloads
+    import paged_kv_decode_12_amd as pk
+    name = args.config if args.config in workloads.PREFILL_CONFIGS else "prefill_causal_d128"
+    inp = workloads.make_prefill_config(name)
+    flops = prefill_flops(inp)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    out = torch.empty_like(d["q"])
+    step = lambda: pk.batch_prefill(d["q"], d["k"], d["v"], qo_indptr=d.get("qo_indptr"),
+                                    kv_indptr=d.get("kv_indptr"), mask_type=d["mask_type"],
+                                    window_left=d["window_left"], sm_scale=d["sm_scale"],
+                                    output_scale=d["output_scale"], out=out,
+                                    max_seq_len_q=d.get("max_seq_len_q"))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    tflops = flops / (us * 1e-6) / 1e12
+    peak = 2500.0
+    res = {"op": "prefill", "metric": "context-attention TFLOP/s (4 D flops per visible "
+                                      "query-key pair and head)",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_call": round(us, 3),
+           "steps": args.steps, "warmup": args.warmup,
+           "dtype": "bf16" if inp["q"].dtype == torch.bfloat16 else "fp16",
+           "config": {"workload": name, **{k: v for k, v in workloads.PREFILL_CONFIGS[name].items()
+                                          if k != "seed"}},
+           "flops_per_call": flops,
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None}}
+    if not args.no_check or args.cpu_seconds > 0:
+        import oracle
+        rows = out.shape[0] * (out.shape[1] if out.dim() == 4 else 1)
+        Hq = out.shape[-2]
+        g = torch.Generator().manual_seed(7)
+        sel = sorted(set(torch.randint(0, rows * Hq, (64,), generator=g).tolist()) |
+                     {rows * Hq - 1})
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        t = time.perf_counter()
+        ref = oracle.prefill(inp, sel=sel, nthreads=threads)
+        t_cpu = time.perf_counter() - t
+        got = out.float().cpu().numpy().reshape(-1, out.shape[-1])[sel]
+        res["check"] = {"max_abs_err_out_sampled": float(np.abs(got - ref).max()),
+                        "rows_sampled": len(sel)}
+        sflops = flops / (rows * Hq) * len(sel)   # the sample's share (rows differ in length)
+        res["cpu_baseline"] = {"value": round(sflops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{len(sel)} sampled (row, head) pairs of {name}, "
+                                         f"{t_cpu:.2f} s, fp64 C + OpenMP (flops prorated by "
+                                         "the mean visible keys per row)",
+                               "cpu": cpu_model()}
+    print(json.dumps(res), flush=True)
 
 
 def cpu_model() -> str:
@@ -300,6 +408,8 @@ def _per_dispatch(rows, counter, kfilter):
     return [per[k] for k in sorted(per, key=int)]
 
 
+DERIVED = ["MfmaUtil", "VALUBusy", "OccupancyPercent", "LDSBankConflict"]
+
 SQ_SETS = {
     "sq_a": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
              "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY",
@@ -318,8 +428,12 @@ def summarize(args):
     sets), calibration (a plain 1 GiB copy: the counter scale factors)."""
     import statistics
     kind, d, w = args.summarize, args.prof_dir, args.config
-    bargs = f"--config {w} --steps 10 --warmup 2 --cold-iters 0 --cpu-seconds 0 --no-check"
-    sha = kernel_source_hash()
+    pre = args.op == "prefill"
+    fam = "prefill" if pre else "decode"          # file prefix and kernel family
+    kfilter = "prefill_kernel" if pre else "decode_kernel"
+    bargs = (f"--op prefill --config {w} --steps 5 --warmup 1 --cpu-seconds 0 --no-check" if pre
+             else f"--config {w} --steps 10 --warmup 2 --cold-iters 0 --cpu-seconds 0 --no-check")
+    sha = kernel_source_hash(fam)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     if kind == "calibration":
         f = _per_dispatch(_csv_rows(d + "/fetch/**/*counter_collection.csv"), "FETCH_SIZE", "copyBuffer")
@@ -341,14 +455,15 @@ def summarize(args):
     elif kind == "trace":
         import workloads
         kt = _csv_rows(d + "/**/*kernel_trace.csv")
-        dec = [r for r in kt if "decode_kernel" in r["Kernel_Name"]]
+        dec = [r for r in kt if kfilter in r["Kernel_Name"]]
         mer = [r for r in kt if "merge_kernel" in r["Kernel_Name"]]
         dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         dd = [dur(r) for r in dec]
-        nbytes = kv_bytes(workloads.make_config(w))
+        nbytes = (prefill_flops(workloads.make_prefill_config(w)) if pre
+                  else kv_bytes(workloads.make_config(w)))
         r0 = dec[0]
         tag = os.path.basename(d.rstrip("/"))
-        L = [f"# decode kernel, {w} workload: rocprofv3 kernel trace statistics",
+        L = [f"# {fam} kernel, {w} workload: rocprofv3 kernel trace statistics",
              "command: " + PROFILE_CMD.format(t=180, what="--kernel-trace --stats", tag=tag, bargs=bargs),
              f"source_sha256: {sha}",
              f"kernel: {r0['Kernel_Name']}",
@@ -365,14 +480,21 @@ def summarize(args):
                   f"{statistics.mean(md):.2f}",
                   f"decode_plus_merge_mean_us: {tot + statistics.mean(md):.2f}"]
             tot += statistics.mean(md)
-        L += [f"algorithmic_kv_bytes_per_launch: {nbytes}",
-              f"effective_GBps_at_mean: {nbytes / tot / 1e3:.1f}  ({nbytes / tot / 1e3 / 80:.1f}% of 8 TB/s)",
+        if pre:
+            L += [f"algorithmic_flops_per_launch: {nbytes}",
+                  f"TFLOPs_at_mean: {nbytes / tot / 1e6:.1f}  ({nbytes / tot / 1e6 / 25:.1f}% of "
+                  "2.5 PFLOP/s dense bf16/fp16 MFMA)"]
+        else:
+            L += [f"algorithmic_kv_bytes_per_launch: {nbytes}",
+                  f"effective_GBps_at_mean: {nbytes / tot / 1e3:.1f}  ({nbytes / tot / 1e3 / 80:.1f}% "
+                  "of 8 TB/s)"]
+        L += [
               "", "# kernel_stats.csv (all kernels of the run)",
               "name | calls | average_ns | min_ns | max_ns | percentage"]
         for r in _csv_rows(d + "/**/*kernel_stats.csv"):
             L.append(f"{r['Name'][:110]} | {r['Calls']} | {r['AverageNs']} | {r['MinNs']} | "
                      f"{r['MaxNs']} | {r['Percentage']}")
-        path = os.path.join(ROOT, "profiles", f"decode_{w}_kernel_trace.txt")
+        path = os.path.join(ROOT, "profiles", f"{fam}_{w}_kernel_trace.txt")
     elif kind in ("fetch", "write"):
         import workloads
         cal = {}
@@ -382,15 +504,16 @@ def summarize(args):
             if line.startswith("write_factor:"):
                 cal["write"] = float(line.split()[1])
         counter = kind.upper() + "_SIZE"
-        v = _per_dispatch(_csv_rows(d + "/**/*counter_collection.csv"), counter, "decode_kernel")
-        part = os.path.join(ROOT, "profiles", f".{w}_{kind}.part")
+        v = _per_dispatch(_csv_rows(d + "/**/*counter_collection.csv"), counter, kfilter)
+        part = os.path.join(ROOT, "profiles", f".{fam}_{w}_{kind}.part")
         tag = os.path.basename(d.rstrip("/"))
         with open(part, "w") as fh:
             fh.write(json.dumps({"kib": statistics.mean(v), "min": min(v), "max": max(v), "n": len(v),
                                  "factor": cal[kind], "sha": sha,
                                  "cmd": PROFILE_CMD.format(t=90, what=f"--pmc {counter}", tag=tag,
                                                            bargs=bargs)}))
-        other = os.path.join(ROOT, "profiles", f".{w}_{'write' if kind == 'fetch' else 'fetch'}.part")
+        other = os.path.join(ROOT, "profiles",
+                             f".{fam}_{w}_{'write' if kind == 'fetch' else 'fetch'}.part")
         if not os.path.exists(other):
             print(f"stored {kind}; summarise the other counter to write the traffic file")
             return
@@ -398,9 +521,13 @@ def summarize(args):
         wp = json.load(open(other if kind == "fetch" else part))
         os.remove(part)
         os.remove(other)
-        nbytes = kv_bytes(workloads.make_config(w))
+        if pre:   # q, k, v read once and out written once
+            pin = workloads.make_prefill_config(w)
+            nbytes = sum(pin[t].numel() * pin[t].element_size() for t in ("q", "k", "v", "q"))
+        else:
+            nbytes = kv_bytes(workloads.make_config(w))
         fb, wb = int(fp["kib"] * 1024 * fp["factor"]), int(wp["kib"] * 1024 * wp["factor"])
-        L = [f"# decode kernel, {w} workload: HBM traffic per launch from rocprofv3 counters",
+        L = [f"# {fam} kernel, {w} workload: HBM traffic per launch from rocprofv3 counters",
              "# (one counter per run; scaled by the 1 GiB copy calibration in copy_1GiB_counter_calibration.txt)",
              f"command_fetch: {fp['cmd']}", f"command_write: {wp['cmd']}",
              f"source_sha256: {sha}", f"dispatches: {fp['n']}",
@@ -408,22 +535,44 @@ def summarize(args):
              f"write_kib_per_dispatch: {wp['kib']:.2f} (min {wp['min']:.2f}, max {wp['max']:.2f})",
              f"fetch_factor: {fp['factor']:.4f}", f"write_factor: {wp['factor']:.4f}",
              f"fetch_bytes_per_launch: {fb}", f"write_bytes_per_launch: {wb}",
-             f"traffic_bytes_per_launch: {fb + wb}", f"algorithmic_kv_bytes_per_launch: {nbytes}",
-             f"fetch_over_algorithmic: {fb / nbytes:.4f}"]
-        path = os.path.join(ROOT, "profiles", f"decode_{w}_hbm_traffic.txt")
+             f"traffic_bytes_per_launch: {fb + wb}",
+             (f"algorithmic_bytes_per_launch (q, k, v read once, out written once): {nbytes}" if pre
+              else f"algorithmic_kv_bytes_per_launch: {nbytes}"),
+             f"{'traffic' if pre else 'fetch'}_over_algorithmic: {(fb + wb if pre else fb) / nbytes:.4f}"]
+        path = os.path.join(ROOT, "profiles", f"{fam}_{w}_hbm_traffic.txt")
+    elif kind == "derived":
+        rows = _csv_rows(d + "/**/*counter_collection.csv")
+        vals = {n: statistics.mean(_per_dispatch(rows, n, kfilter)) for n in DERIVED}
+        tag = os.path.basename(d.rstrip("/"))
+        L = [f"# {fam} kernel, {w} workload: rocprofv3's derived metrics per dispatch (its own "
+             "expressions, evaluated by rocprofv3; mean over the run's dispatches)",
+             "command: " + PROFILE_CMD.format(t=90, what="--pmc " + " ".join(DERIVED), tag=tag,
+                                              bargs=bargs),
+             f"source_sha256: {sha}"]
+        L += [f"{n}: {vals[n]:.3f}" for n in DERIVED]
+        L += ["# MfmaUtil % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE max over XCDs * SIMDs)",
+              "# VALUBusy % = SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE (max over XCDs)",
+              "# OccupancyPercent = 400 SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32 (waves of 32 slots)",
+              "# LDSBankConflict % = SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs"]
+        path = os.path.join(ROOT, "profiles", f"{fam}_{w}_derived_counters.txt")
     elif kind in SQ_SETS:
         rows = _csv_rows(d + "/**/*counter_collection.csv")
         names = SQ_SETS[kind]
-        vals = {n: statistics.mean(_per_dispatch(rows, n, "decode_kernel")) for n in names}
-        cus, simds = 256, 1024
-        gui = vals["GRBM_GUI_ACTIVE"]
+        vals = {n: statistics.mean(_per_dispatch(rows, n, kfilter)) for n in names}
+        cus, simds, xcds = 256, 1024, 8
+        # rocprofv3's csv gives GRBM_GUI_ACTIVE summed over the 8 XCDs (8x the
+        # dispatch's cycles); its own derived metrics take the maximum over
+        # XCDs, which the sum / 8 stands for here
+        gui = vals["GRBM_GUI_ACTIVE"] / xcds
         tag = os.path.basename(d.rstrip("/"))
-        L = [f"# decode kernel, {w} workload: SQ counters per dispatch (mean over the run's dispatches, "
+        L = [f"# {fam} kernel, {w} workload: SQ counters per dispatch (mean over the run's dispatches, "
              "summed over SEs and XCDs)",
              "command: " + PROFILE_CMD.format(t=90, what="--pmc " + " ".join(names), tag=tag, bargs=bargs),
              f"source_sha256: {sha}"]
         L += [f"{n}: {vals[n]:.0f}" for n in names]
-        L.append("# derived (rocprofv3's own definitions; 256 CUs, 1024 SIMDs):")
+        L.append("# derived (rocprofv3's own definitions; 256 CUs, 1024 SIMDs, GRBM_GUI_ACTIVE / 8 "
+                 "per XCD; cycle counters named *_CYCLES / SQ_WAIT_* / SQ_ACTIVE_* as the csv gives "
+                 "them):")
         if kind == "sq_a":
             L += [f"MfmaUtil_pct: {100 * vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.2f}   "
                   "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs))",
@@ -440,7 +589,7 @@ def summarize(args):
                   "(100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs)",
                   f"lds_insts: {vals['SQ_INSTS_LDS']:.0f}   vmem_rd_insts: {vals['SQ_INSTS_VMEM_RD']:.0f}",
                   f"mfma_mops_bf16_f16 (x512 = flops): {vals['SQ_INSTS_VALU_MFMA_MOPS_BF16'] + vals['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}"]
-        path = os.path.join(ROOT, "profiles", f"decode_{w}_{kind}_counters.txt")
+        path = os.path.join(ROOT, "profiles", f"{fam}_{w}_{kind}_counters.txt")
     else:
         raise SystemExit(f"unknown summary kind {kind}")
     with open(path, "w") as fh:
@@ -459,11 +608,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU-baseline leg (0 disables it)")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--op", choices=("decode", "merge_states", "stream_read", "paged_gather"),
+    ap.add_argument("--op", choices=("decode", "merge_states", "stream_read", "paged_gather",
+                                     "prefill"),
                     default="decode",
                     help="merge_states: time the cascade merge on 16 states of the "
                          "llama3_8b batch's rows instead of the decode; stream_read / "
-                         "paged_gather: memory-system references for the workload's bytes")
+                         "paged_gather: memory-system references for the workload's bytes; "
+                         "prefill: context attention on --config prefill_* (TFLOP/s)")
     ap.add_argument("--lds", action="store_true",
                     help="paged_gather: stage the blocks through LDS instead of registers")
     ap.add_argument("--pf", type=int, default=3,
@@ -472,7 +623,8 @@ def main():
                     help="stream_read / paged_gather: 1 (the decode's grid) or 2 waves per SIMD")
     ap.add_argument("--summarize", default=None,
                     help="write a profiles/ summary from rocprofv3 csv output: trace, fetch, "
-                         "write, sq_a, sq_b or calibration (with --prof-dir)")
+                         "write, sq_a, sq_b, derived or calibration (with --prof-dir; "
+                         "--op prefill for the prefill kernel)")
     ap.add_argument("--prof-dir", default=None, help="the rocprofv3 -d directory to summarise")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
@@ -494,6 +646,9 @@ def main():
         return
     if args.op == "merge_states":
         bench_merge_states(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import numpy as np
