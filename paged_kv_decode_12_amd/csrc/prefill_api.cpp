@@ -115,10 +115,13 @@ extern "C" int pkvd_prefill(const pkvd_prefill_args* x, void* stream) {
   if (out->dtype != PKVD_BF16 && out->dtype != PKVD_F16 && out->dtype != PKVD_F32)
     return fail(PKVD_ERR_INVALID_ARG, "out must be bf16, fp16 or fp32");
   if (!aligned16(out->data)) return fail(PKVD_ERR_INVALID_ARG, "out must be 16-byte aligned");
-  const int bm = pkvd::prefill_block_rows((int)D);
-  const int64_t m_tiles = (Sq + bm - 1) / bm;
+  int hpw = 0, tt = 0;
+  if (!pkvd::prefill_geometry((int)D, (int)(Hq / Hkv), &hpw, &tt))
+    return fail(PKVD_ERR_UNSUPPORTED, "head_dim=%lld not built for prefill", (long long)D);
+  const int64_t m_tiles = (Sq + tt - 1) / tt;
+  const int64_t groups = B * Hkv * ((Hq / Hkv) / hpw);
   if (rq > INT32_MAX || rk > INT32_MAX || rq * Hq * D > (1LL << 40) || Sq > INT32_MAX ||
-      Sk > INT32_MAX || B * Hq * m_tiles > INT32_MAX - 8 || B * Sq > INT32_MAX)
+      Sk > INT32_MAX || groups * m_tiles > INT32_MAX - 8 || B * Sq > INT32_MAX)
     return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
   pkvd::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
@@ -150,8 +153,11 @@ extern "C" int pkvd_prefill(const pkvd_prefill_args* x, void* stream) {
   a.window_left = x->window_left;
   a.scale_log2 = (float)((double)x->sm_scale * 1.4426950408889634);
   a.out_scale = x->output_scale;
+  a.hpw = hpw;
+  a.tt = tt;
+  a.groups = (int32_t)groups;
   a.m_tiles = (int32_t)m_tiles;
-  a.items = (int32_t)(B * Hq * m_tiles);
+  a.items = (int32_t)(groups * m_tiles);
   hipError_t e = pkvd::launch_prefill(a, q->dtype == PKVD_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return PKVD_OK;

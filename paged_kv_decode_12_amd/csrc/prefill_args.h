@@ -1,6 +1,6 @@
 // prefill_args.h -- launch arguments of the context-attention (prefill)
-// kernel, shared by the host (api.cpp) and the kernel (prefill_kernel.hip).
-// Internal; not part of the C ABI.
+// kernel, shared by the host (prefill_api.cpp) and the kernel
+// (prefill_kernel.hip).  Internal; not part of the C ABI.
 #pragma once
 
 #include <stdint.h>
@@ -34,12 +34,20 @@ struct PrefillArgs {
   int32_t window_left;         // -1: none
   float scale_log2;            // sm_scale * log2(e)
   float out_scale;             // factor on the output
-  int32_t m_tiles;             // query tiles per (request, head)
-  int32_t items;               // B * Hq * m_tiles
+  // grid: a workgroup takes hpw query heads of one kv head (a head group)
+  // times tt query tokens; items run over (token tile, request, kv head,
+  // head group), token tiles from the last to the first
+  int32_t hpw;                 // query heads per workgroup (divides g)
+  int32_t tt;                  // query tokens per workgroup
+  int32_t groups;              // B * Hkv * (g / hpw)
+  int32_t m_tiles;             // token tiles: ceil(Sq / tt)
+  int32_t items;               // m_tiles * groups
 };
 
-// Query rows per workgroup for a head_dim (the tile the grid counts).
-int prefill_block_rows(int head_dim);
+// Query heads and tokens per workgroup for a head_dim and GQA group size g:
+// *hpw = the largest power of two dividing g (at most the workgroup's 16-row
+// tiles), *tt = its rows / *hpw.  Returns false for an unsupported head_dim.
+bool prefill_geometry(int head_dim, int g, int* hpw, int* tt);
 // Launch (prefill_kernel.hip).  Returns the hipError_t of the launch.
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, hipStream_t stream);
 

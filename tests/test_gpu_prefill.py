@@ -111,3 +111,15 @@ def test_prefill_configs_sampled(name):
     log(f"[prefill_cfg] {name} rows={rows}")
     got = run(inp)
     compare(name, got[sel], ref)
+
+
+@pytest.mark.parametrize("dtype,sm_scale", [("bf16", 30.0), ("fp16", 3.0)])
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_large_logits(D, dtype, sm_scale):
+    """Scores spread over hundreds of base-2 units: later keys exceed a row's
+    first maximum by far more than the fast pass allows (2^64 for bf16, 2^15
+    for fp16 probabilities), so the kernel must take its rescaling pass."""
+    inp = workloads.make_prefill_case(B=2, Sq=140, Sk=300, Hq=4, Hkv=2, D=D, dtype=dtype,
+                                      mask_type="causal", seed=77)
+    inp["sm_scale"] = sm_scale
+    compare(f"large_logits/D{D}/{dtype}", run(inp), oracle.prefill(inp))
