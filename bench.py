@@ -417,6 +417,10 @@ SQ_SETS = {
     "sq_b": ["SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU",
              "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
              "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"],
+    # where issue time goes: waiting (any / for an instruction / for LDS) vs active by type
+    "sq_c": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+             "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA",
+             "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"],
 }
 
 
@@ -584,6 +588,16 @@ def summarize(args):
                   f"wait_inst_any_frac_of_wave_cycles: {vals['SQ_WAIT_INST_ANY'] / max(vals['SQ_WAVE_CYCLES'], 1):.3f}",
                   f"valu_insts_per_wave: {vals['SQ_INSTS_VALU'] / max(vals['SQ_WAVES'], 1):.0f}",
                   f"mfma_insts_per_wave: {vals['SQ_INSTS_MFMA'] / max(vals['SQ_WAVES'], 1):.0f}"]
+        elif kind == "sq_c":
+            wc = max(vals["SQ_WAVE_CYCLES"], 1)
+            L += [f"wait_any_frac_of_wave_cycles: {vals['SQ_WAIT_ANY'] / wc:.3f}",
+                  f"wait_inst_any_frac_of_wave_cycles: {vals['SQ_WAIT_INST_ANY'] / wc:.3f}",
+                  f"wait_inst_lds_frac_of_wave_cycles: {vals['SQ_WAIT_INST_LDS'] / wc:.3f}",
+                  f"active_lds_frac_of_wave_cycles: {vals['SQ_ACTIVE_INST_LDS'] / wc:.3f}",
+                  f"active_misc_frac_of_wave_cycles: {vals['SQ_ACTIVE_INST_MISC'] / wc:.3f}",
+                  f"active_scalar_frac_of_wave_cycles: {vals['SQ_ACTIVE_INST_SCA'] / wc:.3f}",
+                  f"LDS_busy_pct: {100 * vals['SQ_LDS_IDX_ACTIVE'] / gui / cus:.2f}   "
+                  "(SQ_LDS_IDX_ACTIVE / GRBM_GUI_ACTIVE / CUs)"]
         else:
             L += [f"LDSBankConflict_pct: {100 * vals['SQ_LDS_BANK_CONFLICT'] / gui / cus:.3f}   "
                   "(100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs)",
@@ -623,7 +637,7 @@ def main():
                     help="stream_read / paged_gather: 1 (the decode's grid) or 2 waves per SIMD")
     ap.add_argument("--summarize", default=None,
                     help="write a profiles/ summary from rocprofv3 csv output: trace, fetch, "
-                         "write, sq_a, sq_b, derived or calibration (with --prof-dir; "
+                         "write, sq_a, sq_b, sq_c, derived or calibration (with --prof-dir; "
                          "--op prefill for the prefill kernel)")
     ap.add_argument("--prof-dir", default=None, help="the rocprofv3 -d directory to summarise")
     ap.add_argument("--copy-calibration", action="store_true",

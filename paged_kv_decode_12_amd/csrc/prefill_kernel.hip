@@ -37,6 +37,8 @@
 //    row-major V tile: lane j of each 16-lane group points at 4 dims of one
 //    key row and receives one dim of 4 key rows.
 // Output tile u leaves lane l with rows 4q + i, dim 16u + j of O.
+#include <float.h>
+
 #include <type_traits>
 
 #include "engine_mfma.h"
@@ -89,20 +91,37 @@ __device__ __forceinline__ int wave_maxi(int x) {
 }
 
 // Direct 16-byte global-to-LDS load: each lane's 16 bytes from `g` land at
-// LDS byte address lds_base + 16 * lane (lds_base wave-uniform, in M0).
+// LDS byte address lds_base + OFF + 16 * lane (lds_base wave-uniform, in an
+// SGPR; the sum goes to M0).
 // Written out rather than through the builtin because the compiler, which
 // cannot always tell which LDS variable such a load fills, would wait for
 // all of them (vmcnt 0) before reading any stage of the ring; the kernel
 // waits for each stage itself (wait_vmcnt, then a barrier).  The load has
 // no register result, so no destination register can be reused while it is
-// in flight; its address registers are read at issue.
-__device__ __forceinline__ void dma16(const uint16_t* g, const uint16_t* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(PKVD_LDS const uint16_t*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(m0)
-               : "memory", "m0");
+// in flight; its address registers and M0 are read at issue, and M0 is
+// restored before the block ends.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_base) {
+  uint32_t saved;   // M0 is the compiler's register: restored before the block ends
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base), "n"(OFF)
+      : "memory", "scc");
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1.
+template <int N, class Fn, int I = 0>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, Fn, I + 1>(static_cast<Fn&&>(f));
+  }
+}
+
+// LDS byte address of an LDS variable (wave-uniform).
+__device__ __forceinline__ uint32_t lds_address(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(PKVD_LDS const uint16_t*)p);
 }
 
 // s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding:
@@ -125,8 +144,20 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs a) {
+template <int D>
+struct PrefillGeom {
+  static constexpr int TW = PrefillTile<D>::TW, BN = PrefillTile<D>::BN;
+  static constexpr int TILE = BN * D;   // elements of one K or V tile
+};
+
+// The workgroup's whole computation, in the FAST mode (SAFE = false:
+// returns true when the pass overflowed and wrote nothing) or the SAFE
+// mode (SAFE = true: the rescaling passes, one tile and half of the
+// output dims at a time).  st0 .. st2: the LDS ring's stages (a K tile,
+// then a V tile); s_range, s_flag: LDS scratch of the workgroup.
+template <int D, bool BF16, bool SAFE>
+__device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0, uint16_t* st1,
+                                             uint16_t* st2, int* s_range, int* s_flag) {
   using Mf = Mfma<BF16>;
   using F = Fmt<BF16>;
   constexpr int TW = PrefillTile<D>::TW, BN = PrefillTile<D>::BN;
@@ -139,14 +170,10 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
   constexpr int LPT = TILE / 8 / 64 / kPW;   // wave-wide loads per wave, tile and tensor
   static_assert(LPT >= 1 && TILE / 8 == LPT * 64 * kPW, "tile loads must divide over the waves");
   static_assert(2 * LPT < 16, "outstanding loads must fit the vmcnt field");
-  // the ring's stages: a K tile, then a V tile
-  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
-  __shared__ int s_range[2];
-  __shared__ int s_flag;   // a FAST pass overflowed (see attend)
   static_assert(kStages == 3, "three ring stages");
 
   const int item = (int)blockIdx.x;
-  if (item >= a.items) return;
+  if (item >= a.items) return false;
   const int mt = a.m_tiles - 1 - item / a.groups;
   const int grp = item - (item / a.groups) * a.groups;
   const int nbk = a.B * a.Hkv;
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
     sk = a.Sk;
   }
   const int t_begin = mt * a.tt;   // first query token of the workgroup
-  if (t_begin >= sq) return;       // uniform over the workgroup
+  if (t_begin >= sq) return false;   // uniform over the workgroup
 
   // keys query token i sees: [lo, hi] (empty when hi < lo)
   auto bounds = [&](int i, int& lo, int& hi) {
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
   if (tid == 0) {
     s_range[0] = INT32_MAX;
     s_range[1] = INT32_MIN;
-    s_flag = 0;
+    *s_flag = 0;
   }
   __syncthreads();
   if (tid < a.tt && t_begin + tid < sq) {
@@ -211,28 +238,60 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
   const int kbase = klo <= khi ? (klo / 16) * 16 : 0;
   const int ntiles = klo <= khi ? (khi - kbase) / BN + 1 : 0;
 
-  // direct loads of tile i into stage s: wave-wide load u of the wave fills
-  // key rows (u * kPW + wave) * RPI .. + RPI - 1 (1 KB of LDS, lane-major);
-  // keys past the request's last are read as its last key (masked below)
-  auto issue = [&](int i, uint16_t* sK, uint16_t* sV) {
-    const int kb = kbase + i * BN;
+  // LDS byte addresses of this wave's first load in each stage of the ring
+  // (the direct loads' M0 adds a constant per load)
+  const uint32_t lds_st[kStages] = {(uint32_t)uniform(lds_address(st0) + wave * 1024),
+                                    (uint32_t)uniform(lds_address(st1) + wave * 1024),
+                                    (uint32_t)uniform(lds_address(st2) + wave * 1024)};
+  // Direct loads of a tile: wave-wide load u of the wave fills key rows
+  // (u * kPW + wave) * RPI .. + RPI - 1 of the tile (1 KB of LDS,
+  // lane-major); lane l loads chunk swz(row, l % CPR) of its row.  The
+  // lane's element offsets (row, kv head, chunk) are fixed per call; a tile
+  // adds its first key's row.
+  // (the host keeps a tile's span of rows and the heads within int32)
+  const uint16_t* kbase_p = a.k + (int64_t)k0 * a.k_sr + (int64_t)kvh * a.k_sh;
+  const uint16_t* vbase_p = a.v + (int64_t)k0 * a.v_sr + (int64_t)kvh * a.v_sh;
+  int koff[LPT], voff[LPT], lrow[LPT];
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int inst = u * kPW + wave;
-      const int r = inst * RPI + lane / CPR;
-      const int c = swz(r, lane % CPR);
-      const int key = min(kb + r, sk - 1);
-      const uint16_t* gk = a.k + (int64_t)(k0 + key) * a.k_sr + (int64_t)kvh * a.k_sh + c * 8;
-      const uint16_t* gv = a.v + (int64_t)(k0 + key) * a.v_sr + (int64_t)kvh * a.v_sh + c * 8;
-      dma16(gk, sK + inst * 512);
-      dma16(gv, sV + inst * 512);
+  for (int u = 0; u < LPT; ++u) {
+    const int r = (u * kPW + wave) * RPI + lane / CPR;
+    const int c = swz(r, lane % CPR);
+    lrow[u] = r;
+    koff[u] = r * (int)a.k_sr + c * 8;
+    voff[u] = r * (int)a.v_sr + c * 8;
+  }
+  // keys past the request's last are read as its last key (masked below)
+  auto issue = [&](int i, uint32_t st) {
+    const int kb = kbase + i * BN;
+    if (kb + BN <= sk) {   // uniform: a whole tile of keys
+      const uint16_t* kt = kbase_p + (int64_t)kb * a.k_sr;
+      const uint16_t* vt = vbase_p + (int64_t)kb * a.v_sr;
+      static_for<LPT>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        dma16<u * kPW * 1024u>(kt + koff[u], st);
+        dma16<u * kPW * 1024u + 2u * TILE>(vt + voff[u], st);
+      });
+    } else {
+      static_for<LPT>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        // row min(kb + r, sk - 1) of the request: koff holds r's part
+        const int64_t d = (int64_t)(min(kb + lrow[u], sk - 1) - lrow[u]);
+        dma16<u * kPW * 1024u>(kbase_p + d * a.k_sr + koff[u], st);
+        dma16<u * kPW * 1024u + 2u * TILE>(vbase_p + d * a.v_sr + voff[u], st);
+      });
     }
   };
+
+  // scores are taken in base 2 with a positive factor: a negative sm_scale
+  // is moved onto Q's sign bits (exact)
+  const float sc = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+
   // this wave's tiles: tile t holds 16 tokens of one query head
   int lo_t[TW], hi_t[TW], h_t[TW], tok0_t[TW];
-  int tminlo[TW], tmaxhi[TW], tmaxlo[TW], tminhi[TW];
   u32x4 qf[TW][NC];
-  int wlo = INT32_MAX, whi = INT32_MIN;
+  // over the wave's tiles: keys no live row sees, and keys every live row sees
+  int wlo = INT32_MAX, whi = INT32_MIN, wmaxlo = INT32_MIN, wminhi = INT32_MAX;
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
     const int rho = wave * RW + 16 * t;   // the tile's first row of the workgroup
@@ -246,158 +305,221 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
     lo_t[t] = lo;
     hi_t[t] = hi;
     const bool seen = live && lo <= hi;
-    // blocks no live row sees are skipped; a block is unmasked only when
-    // every live row sees all of it
-    // (wave-uniform: held in scalar registers, so the per-tile tests below
-    // are scalar branches)
-    tminlo[t] = uniform(wave_min(seen ? lo : INT32_MAX));
-    tmaxhi[t] = uniform(wave_maxi(seen ? hi : INT32_MIN));
-    tmaxlo[t] = uniform(wave_maxi(live ? lo : INT32_MIN));
-    tminhi[t] = uniform(wave_min(live ? hi : INT32_MAX));
-    wlo = min(wlo, tminlo[t]);
-    whi = max(whi, tmaxhi[t]);
-    // padding rows load the workgroup's first token (live): never stored
-    const int qtok = live ? tok : t_begin;
+    wlo = min(wlo, seen ? lo : INT32_MAX);
+    whi = max(whi, seen ? hi : INT32_MIN);
+    wmaxlo = max(wmaxlo, live ? lo : INT32_MIN);
+    wminhi = min(wminhi, live ? hi : INT32_MAX);
+  }
+  // Q rows of tile t as the B operand of the scores (padding rows load the
+  // workgroup's first token, which is live: never stored)
+  auto load_q = [&](int t, u32x4 (&dst)[NC]) {
+    const int tok = tok0_t[t] + lj;
+    const int qtok = tok < sq ? tok : t_begin;
     const uint16_t* qp = a.q + (int64_t)(q0 + qtok) * a.q_sr + (int64_t)h_t[t] * a.q_sh + lq * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[t][c] = load16(qp + c * 32);
+    for (int c = 0; c < NC; ++c) dst[c] = load16(qp + c * 32) ^ qsign;
+  };
+#pragma unroll
+  for (int t = 0; t < TW; ++t) load_q(t, qf[t]);
+  // Reference of the FAST pass, per row: the score (base 2, times sc) of
+  // the row's last visible key, plus 8 for fp16 probabilities (so that
+  // keys may score up to 8 + 16 above it before P overflows, and what P
+  // flushes to zero is below 2^-16 of the row's largest probability); -inf
+  // for a row that sees no key.  The row's four lanes each take 8 dims of
+  // every 32 and add across the lanes.
+  float m_ref[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int tok = tok0_t[t] + lj;
+    const bool seen = tok < sq && lo_t[t] <= hi_t[t];
+    float dot = 0.f;
+    if (seen) {   // (a request may have no keys at all)
+      const uint16_t* kp = kbase_p + (int64_t)hi_t[t] * a.k_sr + lq * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 kk = load16(kp + c * 32);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dot = F::dot2(qf[t][c][w], kk[w], dot);
+      }
+    }
+    const Pair p16 = lane_pair<16>(dot);
+    const Pair p32 = lane_pair<32>(p16.lo + p16.hi);
+    m_ref[t] = seen ? sc * (p32.lo + p32.hi) + (BF16 ? 0.f : 8.f) : -INFINITY;
   }
+  // (wave-uniform: scalar registers and scalar branches below)
+  wlo = uniform(wave_min(wlo));
+  whi = uniform(wave_maxi(whi));
+  wmaxlo = uniform(wave_maxi(wmaxlo));
+  wminhi = uniform(wave_min(wminhi));
 
-  // Q rows are in registers (issued above) before any tile load is
-  // outstanding: the loop below waits only for its own tile loads
+  // Q rows are in registers before any tile load is outstanding: the loop
+  // below waits only for its own tile loads
   wait_vmcnt<0>();
 
-  // One pass over the keys for tiles T0 .. T0 + NT - 1.  FAST: a row's maximum is set from the first
-  // chunk it sees and not raised after, so the accumulators are only ever
-  // touched by MFMAs (they stay in accumulation registers); probabilities
-  // may then reach 2^kFast, which bf16 (and the fp32 sums) hold for
-  // kFast = 64 and fp16 for 15.  A score beyond that marks the pass as
-  // overflowed and the workgroup runs it again in the SAFE mode: a lazily
-  // raised maximum (by more than kTau at a time) with the accumulators
-  // rescaled.  Returns true when a FAST pass overflowed (nothing written).
-  auto attend = [&](auto safe_tag, auto t0_tag, auto nt_tag) -> bool {
-    constexpr bool SAFE = decltype(safe_tag)::value;
-    constexpr int T0 = decltype(t0_tag)::value, NT = decltype(nt_tag)::value;   // tiles T0 ..
-    constexpr float kFast = BF16 ? 64.f : 15.f;
+  // B operand of ones: P . 1 gives the row sums of the probabilities as
+  // rounded for P . V
+  const u32x4 ones = BF16 ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                          : u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+
+  // One pass over the keys for tiles T0 .. T0 + NT - 1.  FAST: every row
+  // keeps the reference m_ref (its score of its last visible key, see
+  // above) for the whole pass, so the accumulators are only ever touched by
+  // MFMAs and no chunk takes row maxima; probabilities of keys scoring
+  // above the reference may exceed 1 by as much as P's format holds.  A row
+  // whose probabilities went beyond that marks the pass as overflowed and
+  // the workgroup runs it again in the SAFE mode: a lazily raised maximum
+  // (by more than kTau at a time) with the accumulators rescaled.  Returns
+  // true when a FAST pass overflowed (nothing written).
+  auto attend = [&](auto safe_tag, auto t0_tag, auto nt_tag, auto u0_tag, auto nu_tag) -> bool {
+    static_assert(decltype(safe_tag)::value == SAFE, "one mode per body");
+    constexpr int T0 = decltype(t0_tag)::value, NT = decltype(nt_tag)::value;
+    // output dims 16 U0 .. 16 (U0 + NUP) - 1
+    constexpr int U0 = decltype(u0_tag)::value, NUP = decltype(nu_tag)::value;
     // online softmax state per tile: row j's max (uniform over its four
-    // lanes) and this lane's partial sum; acc[t][u][i]: row 4q + i, dim 16u + j
-    float m_t[NT], l_t[NT];
-    f32x4_t acc[NT][NU];
+    // lanes); acc[t][u][i]: row 4q + i, dim 16 (U0 + u) + j; lsum[t][i]: row 4q + i's
+    // sum of probabilities (the same in every column)
+    float m_t[NT];
+    f32x4_t acc[NT][NUP], lsum[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      m_t[t] = -INFINITY;
-      l_t[t] = 0.f;
+      m_t[t] = SAFE ? -INFINITY : m_ref[T0 + t];
+      lsum[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NU; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NUP; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    bool over = false;
+    // this pass's Q operands: the FAST pass uses those loaded for all
+    // tiles; a SAFE pass loads its own again, so that only one tile's stay
+    // in registers through the rescaling passes
+    u32x4 qv[NT][NC];
+    if constexpr (SAFE) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load_q(T0 + t, qv[t]);
+      wait_vmcnt<0>();
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[t][c] = qf[T0 + t][c];
+    }
+
+    // 32 keys from j0 (tile rows kc * 32 ..) of the stage at sK / sV.
+    // MASKED: some row sees only part of them.
+    auto chunk = [&](auto masked_tag, const uint16_t* sK, const uint16_t* sV, int kc, int j0) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      u32x4 ka[2][NC];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = kc * 32 + 16 * h + lj;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          ka[h][c] = *reinterpret_cast<const u32x4*>(sK + r * D + swz(r, 4 * c + lq) * 8);
+      }
+      // V operand of output tile u: keys (4q .. 4q + 3, 16 + 4q .. + 3), column j
+      auto vread = [&](int u) {
+        u32x4 vb;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = kc * 32 + 16 * h + 4 * lq + (lj >> 2);
+          const int cc = 2 * u + ((lj & 3) >> 1);
+          const u32x2 y = read_tr(sV + r * D + swz(r, cc) * 8 + (lj & 1) * 4);
+          vb[2 * h] = y[0];
+          vb[2 * h + 1] = y[1];
+        }
+        return vb;
+      };
+      constexpr int VPRE = !SAFE && NUP <= 8 ? 4 : 2;   // V operands read ahead of P . V
+      u32x4 vb[VPRE];
+#pragma unroll
+      for (int u = 0; u < VPRE; ++u) vb[u] = vread(U0 + u);
+
+      // phase 1, tile by tile (K operands shared): scores, row maxima
+      // (SAFE, or FAST while some row has none), probabilities
+      // 2^(sc x - m) packed as the A operand of P . V (a row that has seen
+      // no key has m = -inf and only -inf scores: p = 0), and the row sums
+      // P . 1
+      u32x4 pa[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          s0 = Mf::qk(ka[0][c], qv[t][c], s0);
+          s1 = Mf::qk(ka[1][c], qv[t][c], s1);
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = s0[i];
+          x[4 + i] = s1[i];
+        }
+        if constexpr (MASKED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = j0 + (e < 4 ? 4 * lq + e : 16 + 4 * lq + e - 4);
+            x[e] = (key >= lo_t[T0 + t] && key <= hi_t[T0 + t]) ? x[e] : -INFINITY;
+          }
+        }
+        if constexpr (SAFE) {
+          const float lmax = sc * fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          if (wave_any(lmax > m_t[t] + kTau)) {
+            // the chunk max of row j over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
+            const Pair p16 = lane_pair<16>(lmax);
+            const Pair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
+            const float mn = fmaxf(m_t[t], fmaxf(p32.lo, p32.hi));
+            const float alpha = rescale(m_t[t], mn);
+            m_t[t] = mn;
+            // accumulator rows are 4q + i: each row's factor from lane 4q + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float ai = __builtin_bit_cast(
+                  float,
+                  __builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __builtin_bit_cast(int, alpha)));
+              lsum[t][i] *= ai;
+#pragma unroll
+              for (int u = 0; u < NUP; ++u) acc[t][u][i] *= ai;
+            }
+          }
+        }
+        const float nm = -fmaxf(m_t[t], -FLT_MAX);
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], sc, nm));
+        pa[t] = u32x4{F::pack2(p[0], p[1]), F::pack2(p[2], p[3]), F::pack2(p[4], p[5]),
+                      F::pack2(p[6], p[7])};
+        lsum[t] = Mf::qk(pa[t], ones, lsum[t]);
+      }
+      // phase 2: O += P . V, one 16-dim output tile at a time (V operands
+      // shared by the tiles)
+#pragma unroll
+      for (int u = 0; u < NUP; ++u) {
+        const u32x4 v = vb[u % VPRE];
+        if (u + VPRE < NUP) vb[u % VPRE] = vread(U0 + u + VPRE);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][u] = Mf::qk(pa[t], v, acc[t][u]);
+      }
+    };
 
     lds_barrier();   // every wave is past its reads of an earlier pass's ring
-    if (ntiles > 0) issue(0, st0, st0 + TILE);
-    if (ntiles > 1) issue(1, st1, st1 + TILE);
+    if (ntiles > 0) issue(0, lds_st[0]);
+    if (ntiles > 1) issue(1, lds_st[1]);
     if (ntiles > 1) wait_vmcnt<2 * LPT>();
     else wait_vmcnt<0>();
     lds_barrier();
     // step `it` reads stage it % 3 and fills stage (it + 2) % 3
-    auto step = [&](int it, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
-      if (it + 2 < ntiles) issue(it + 2, nK, nV);
+    auto step = [&](int it, const uint16_t* stage, uint32_t next) {
+      if (it + 2 < ntiles) issue(it + 2, next);
+      const uint16_t* sK = stage;
+      const uint16_t* sV = stage + TILE;
       const int kb = kbase + it * BN;
 #pragma unroll 1
       for (int kc = 0; kc < BN / 32; ++kc) {
         const int j0 = kb + kc * 32;
         if (j0 > whi || j0 + 31 < wlo) continue;   // no row of this wave sees these keys
-        // phase 1: scores and probabilities of every tile (K operands shared)
-        u32x4 ka[2][NC];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = kc * 32 + 16 * h + lj;
-#pragma unroll
-          for (int c = 0; c < NC; ++c)
-            ka[h][c] = *reinterpret_cast<const u32x4*>(sK + r * D + swz(r, 4 * c + lq) * 8);
-        }
-        u32x4 pa[NT];
-        bool on[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          on[t] = !(j0 > tmaxhi[T0 + t] || j0 + 31 < tminlo[T0 + t]);   // the tile sees some keys
-          pa[t] = u32x4{0u, 0u, 0u, 0u};
-          if (!on[t]) continue;
-          f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            s0 = Mf::qk(ka[0][c], qf[T0 + t][c], s0);
-            s1 = Mf::qk(ka[1][c], qf[T0 + t][c], s1);
-          }
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = s0[i] * a.scale_log2;
-            x[4 + i] = s1[i] * a.scale_log2;
-          }
-          if (!(j0 >= tmaxlo[T0 + t] && j0 + 31 <= tminhi[T0 + t])) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = j0 + (e < 4 ? 4 * lq + e : 16 + 4 * lq + e - 4);
-              x[e] = (key >= lo_t[T0 + t] && key <= hi_t[T0 + t]) ? x[e] : -INFINITY;
-            }
-          }
-          const float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          if constexpr (SAFE) {
-            if (wave_any(lmax > m_t[t] + kTau)) {
-              // the chunk max of row j over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
-              const Pair p16 = lane_pair<16>(lmax);
-              const Pair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
-              const float mn = fmaxf(m_t[t], fmaxf(p32.lo, p32.hi));
-              const float alpha = rescale(m_t[t], mn);
-              m_t[t] = mn;
-              l_t[t] *= alpha;
-              // accumulator rows are 4q + i: each row's factor from lane 4q + i
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float ai = __builtin_bit_cast(
-                    float,
-                    __builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __builtin_bit_cast(int, alpha)));
-#pragma unroll
-                for (int u = 0; u < NU; ++u) acc[t][u][i] *= ai;
-              }
-            }
-          } else {
-            over |= m_t[t] != -INFINITY && lmax > m_t[t] + kFast;
-            if (wave_any(m_t[t] == -INFINITY && lmax != -INFINITY)) {
-              // rows seeing their first keys take the chunk max (their
-              // accumulators and sums are still zero)
-              const Pair p16 = lane_pair<16>(lmax);
-              const Pair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
-              if (m_t[t] == -INFINITY) m_t[t] = fmaxf(p32.lo, p32.hi);
-            }
-          }
-          // a row that has seen no key yet has m = -inf and only -inf scores: p = 0
-          const float ms = m_t[t] == -INFINITY ? 0.f : m_t[t];
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - ms);
-          l_t[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          pa[t] = u32x4{F::pack2(p[0], p[1]), F::pack2(p[2], p[3]), F::pack2(p[4], p[5]),
-                        F::pack2(p[6], p[7])};
-        }
-        // phase 2: O += P . V, one 16-dim output tile at a time (V operands
-        // shared by the tiles)
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          u32x4 vb;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r = kc * 32 + 16 * h + 4 * lq + (lj >> 2);
-            const int cc = 2 * u + ((lj & 3) >> 1);
-            const u32x2 y = read_tr(sV + r * D + swz(r, cc) * 8 + (lj & 1) * 4);
-            vb[2 * h] = y[0];
-            vb[2 * h + 1] = y[1];
-          }
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            if (on[t]) acc[t][u] = Mf::qk(pa[t], vb, acc[t][u]);
-        }
+        if (j0 >= wmaxlo && j0 + 31 <= wminhi)   // every live row sees all of them
+          chunk(std::false_type{}, sK, sV, kc, j0);
+        else
+          chunk(std::true_type{}, sK, sV, kc, j0);
       }
       if (it + 1 < ntiles) {
         // the next tile's loads have landed (the one after may still be in flight)
@@ -407,62 +529,92 @@ __global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs 
       }
     };
     for (int it = 0; it < ntiles; it += 3) {
-      step(it, st0, st0 + TILE, st2, st2 + TILE);
-      if (it + 1 < ntiles) step(it + 1, st1, st1 + TILE, st0, st0 + TILE);
-      if (it + 2 < ntiles) step(it + 2, st2, st2 + TILE, st1, st1 + TILE);
+      step(it, st0, lds_st[2]);
+      if (it + 1 < ntiles) step(it + 1, st1, lds_st[0]);
+      if (it + 2 < ntiles) step(it + 2, st2, lds_st[1]);
     }
 
     if constexpr (!SAFE) {
-      // the workgroup's vote: any wave overflowed -> all run the SAFE pass
-      // (every wave is past its last read of the ring here)
-      if (wave_any(over)) s_flag = 1;
+      // A probability beyond the range of P's format (or of the fp32 sums)
+      // leaves an infinite or NaN row sum; below it the result is exact to
+      // the formats' precision.  The workgroup's vote: any such row -> all
+      // waves run the SAFE passes (every wave is past its last read of the
+      // ring here).
+      // Padding rows (tokens past the request's last) are not counted: they
+      // are never stored, and in unmasked chunks their scores meet m = -inf.
+      bool over = false;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          over |= tok0_t[T0 + t] + 4 * lq + i < sq && !(lsum[t][i] < INFINITY);
+      if (wave_any(over)) *s_flag = 1;
       lds_barrier();
-      if (s_flag) return true;
+      if (*s_flag) return true;
     }
 
-    // epilogue: row sums over the four lanes of each row, then
-    // out = O / l * output_scale for rows 4q + i, dims 16u + j
+    // epilogue: out = O / l * output_scale for rows 4q + i, dims 16u + j
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const Pair p16 = lane_pair<16>(l_t[t]);
-      const Pair p32 = lane_pair<32>(p16.lo + p16.hi);
-      const float lsum = p32.lo + p32.hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * lq + i;
-        const float L = __builtin_bit_cast(
-            float, __builtin_amdgcn_ds_bpermute(r << 2, __builtin_bit_cast(int, lsum)));
+        const float L = lsum[t][i];
         const int tok = tok0_t[T0 + t] + r;
         if (tok >= sq) continue;
         const float f = L > 0.f ? a.out_scale / L : 0.f;
-        const int64_t off = ((int64_t)(q0 + tok) * a.Hq + h_t[T0 + t]) * D + lj;
+        const int64_t off = ((int64_t)(q0 + tok) * a.Hq + h_t[T0 + t]) * D + 16 * U0 + lj;
         if (a.out_type == kOutF32) {
           float* o = static_cast<float*>(a.out) + off;
 #pragma unroll
-          for (int u = 0; u < NU; ++u) o[16 * u] = acc[t][u][i] * f;
+          for (int u = 0; u < NUP; ++u) o[16 * u] = acc[t][u][i] * f;
         } else {
           uint16_t* o = static_cast<uint16_t*>(a.out) + off;
           if (a.out_type == kOutBf16) {
 #pragma unroll
-            for (int u = 0; u < NU; ++u) o[16 * u] = Fmt<true>::encode(acc[t][u][i] * f);
+            for (int u = 0; u < NUP; ++u) o[16 * u] = Fmt<true>::encode(acc[t][u][i] * f);
           } else {
 #pragma unroll
-            for (int u = 0; u < NU; ++u) o[16 * u] = Fmt<false>::encode(acc[t][u][i] * f);
+            for (int u = 0; u < NUP; ++u) o[16 * u] = Fmt<false>::encode(acc[t][u][i] * f);
           }
         }
       }
     }
     return false;
   };
-  // FAST over all tiles; after an overflow, SAFE over half of the tiles at
-  // a time (half the accumulators: the rescaling path keeps them in
-  // ordinary registers)
   using I0 = std::integral_constant<int, 0>;
-  if (attend(std::false_type{}, I0{}, std::integral_constant<int, TW>{})) {
-    constexpr int H = TW / 2;
-    attend(std::true_type{}, I0{}, std::integral_constant<int, H>{});
-    attend(std::true_type{}, std::integral_constant<int, H>{}, std::integral_constant<int, TW - H>{});
+  using I1 = std::integral_constant<int, 1>;
+  using IH = std::integral_constant<int, NU / 2>;
+  if constexpr (!SAFE) {
+    return attend(std::false_type{}, I0{}, std::integral_constant<int, TW>{}, I0{},
+                  std::integral_constant<int, NU>{});
+  } else {
+    static_for<TW>([&](auto T) {
+      attend(std::true_type{}, T, I1{}, I0{}, IH{});
+      attend(std::true_type{}, T, I1{}, IH{}, IH{});
+    });
+    return false;
   }
+}
+
+// The SAFE passes as a function of their own, so that their register
+// demand (accumulators in ordinary registers) does not shape the register
+// allocation of the FAST loop; it is only called after a FAST pass
+// overflowed.
+template <int D, bool BF16>
+__device__ __noinline__ void prefill_safe(const PrefillArgs& a, uint16_t* st0, uint16_t* st1,
+                                          uint16_t* st2, int* s_range, int* s_flag) {
+  prefill_body<D, BF16, true>(a, st0, st1, st2, s_range, s_flag);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs a) {
+  constexpr int TILE = PrefillGeom<D>::TILE;
+  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
+  __shared__ int s_range[2];
+  __shared__ int s_flag;   // a FAST pass overflowed (see attend)
+  if (prefill_body<D, BF16, false>(a, st0, st1, st2, s_range, &s_flag))
+    prefill_safe<D, BF16>(a, st0, st1, st2, s_range, &s_flag);
 }
 
 }  // namespace
