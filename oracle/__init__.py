@@ -36,6 +36,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "_build", "liboracle_san.so")
+# another build of the same source (the sanitized one) for checking runs
+_LIB_OVERRIDE = os.environ.get("PKVD_ORACLE_LIBRARY")
 
 BF16, F16 = 0, 1
 _ERRORS = {1: "bad argument", 2: "visible key maps outside the page pool", 3: "out of memory"}
@@ -43,21 +46,31 @@ _ERRORS = {1: "bad argument", 2: "visible key maps outside the page pool", 3: "o
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math); with
+    sanitize, into _build/liboracle_san.so with AddressSanitizer and
+    UndefinedBehaviorSanitizer (load it with PKVD_ORACLE_LIBRARY and the gcc
+    ASan runtime preloaded)."""
+    out = _SAN_LIB if sanitize else _LIB
+    if sanitize or force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-g"] if sanitize else []
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11"] + san +
+                              ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
         i64, p = ctypes.c_int64, ctypes.c_void_p
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [
