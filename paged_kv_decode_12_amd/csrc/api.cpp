@@ -54,6 +54,28 @@ bool contiguous(const pkvd_tensor* t) {
   return true;
 }
 
+// CUs of the current device (cached per device); an MI355X (256 CUs) is
+// assumed when no device answers.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  static std::mutex mu;
+  static int cached[64] = {0};
+  if (dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached[dev] = n;
+    else
+      (void)hipGetLastError();
+  }
+  return cached[dev] ? cached[dev] : 256;
+}
+
 }  // namespace api
 }  // namespace pkvd
 
@@ -218,28 +240,6 @@ int check_shapes(const pkvd_tensor* q, const pkvd_tensor* k, const pkvd_tensor* 
       s->Hq > 65535 || (s->Hq / s->Hkv) * Lq > 65535)
     return fail(PKVD_ERR_UNSUPPORTED, "problem dimensions exceed the built index ranges");
   return PKVD_OK;
-}
-
-// CUs of the current device (cached per device); an MI355X (256 CUs) is
-// assumed when no device answers.
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 256;
-  }
-  static std::mutex mu;
-  static int cached[64] = {0};
-  if (dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cached[dev] = n;
-    else
-      (void)hipGetLastError();
-  }
-  return cached[dev] ? cached[dev] : 256;
 }
 
 // Virtual blocks ahead of each unit in the sliced block space, per engine,

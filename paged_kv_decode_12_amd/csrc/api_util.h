@@ -16,6 +16,8 @@ void clear_error();
 bool aligned16(const void* p);
 // Dense row-major strides (size-1 dimensions may have any stride).
 bool contiguous(const pkvd_tensor* t);
+// CUs of the current device (cached per device; 256 when no device answers).
+int device_cus();
 
 }  // namespace api
 }  // namespace pkvd

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "api_util.h"
@@ -161,6 +163,8 @@ extern "C" int pkvd_prefill(const pkvd_prefill_args* x, void* stream) {
   a.groups = (int32_t)groups;
   a.m_tiles = (int32_t)m_tiles;
   a.items = (int32_t)(groups * m_tiles);
+  // the rescaling kernel: one workgroup per CU (its LDS ring fits one)
+  a.safe_grid = std::min(a.items, std::max(device_cus(), 1));
   hipError_t e = pkvd::launch_prefill(a, q->dtype == PKVD_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKVD_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return PKVD_OK;

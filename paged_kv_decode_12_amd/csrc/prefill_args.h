@@ -42,6 +42,7 @@ struct PrefillArgs {
   int32_t groups;              // B * Hkv * (g / hpw)
   int32_t m_tiles;             // token tiles: ceil(Sq / tt)
   int32_t items;               // m_tiles * groups
+  int32_t safe_grid;           // workgroups of the rescaling kernel (<= items)
 };
 
 // Query heads and tokens per workgroup for a head_dim and GQA group size g:

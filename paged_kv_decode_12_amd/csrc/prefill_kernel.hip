@@ -51,18 +51,23 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPW = 4;       // waves per workgroup (one per SIMD)
 constexpr int kStages = 3;   // K/V tiles in the LDS ring
 
+// Workgroup shape per head_dim.  At D = 128 two waves share each SIMD (256
+// registers per lane each) so that one wave's MFMA work covers the other's
+// softmax and LDS reads; at D = 256 a wave's operands need the whole
+// register file of its SIMD.
 template <int D>
 struct PrefillTile;
 template <>
 struct PrefillTile<128> {
-  static constexpr int TW = 4;    // 16-row tiles per wave
+  static constexpr int PW = 8;    // waves per workgroup
+  static constexpr int TW = 2;    // 16-row tiles per wave
   static constexpr int BN = 64;   // keys per LDS tile
 };
 template <>
 struct PrefillTile<256> {
+  static constexpr int PW = 4;
   static constexpr int TW = 2;
   static constexpr int BN = 32;
 };
@@ -150,14 +155,75 @@ struct PrefillGeom {
   static constexpr int TILE = BN * D;   // elements of one K or V tile
 };
 
-// The workgroup's whole computation, in the FAST mode (SAFE = false:
-// returns true when the pass overflowed and wrote nothing) or the SAFE
-// mode (SAFE = true: the rescaling passes, one tile and half of the
-// output dims at a time).  st0 .. st2: the LDS ring's stages (a K tile,
-// then a V tile); s_range, s_flag: LDS scratch of the workgroup.
+// A workgroup item: its request b, kv head, head group hg and token tile mt,
+// the request's rows (packed offsets clamped into the tensors) and the
+// item's first query token.
+struct PrefillItem {
+  int b, kvh, hg, mt;
+  int q0, sq, k0, sk;
+  int t_begin;
+  // false when the item holds no query token of its request (nothing to do)
+  __device__ __forceinline__ bool init(const PrefillArgs& a, int item) {
+    if (item >= a.items) return false;
+    mt = a.m_tiles - 1 - item / a.groups;   // token tiles from the last to the first
+    const int grp = item - (item / a.groups) * a.groups;
+    const int nbk = a.B * a.Hkv;
+    hg = grp / nbk;
+    const int bk = grp - hg * nbk;
+    b = bk / a.Hkv;
+    kvh = bk - b * a.Hkv;
+    if (a.qo) {
+      const int c0 = min(max(a.qo[b], 0), a.rows_q), c1 = min(max(a.qo[b + 1], 0), a.rows_q);
+      const int d0 = min(max(a.kvo[b], 0), a.rows_kv), d1 = min(max(a.kvo[b + 1], 0), a.rows_kv);
+      q0 = c0;
+      sq = min(max(c1 - c0, 0), a.Sq);
+      k0 = d0;
+      sk = max(d1 - d0, 0);
+    } else {
+      q0 = b * a.Sq;
+      sq = a.Sq;
+      k0 = b * a.Sk;
+      sk = a.Sk;
+    }
+    t_begin = mt * a.tt;
+    return t_begin < sq;
+  }
+  // Element offset of the item's first output row (token t_begin, the
+  // group's first query head), dim 0: a live row of the item.
+  __device__ __forceinline__ int64_t first_out(const PrefillArgs& a) const {
+    return ((int64_t)(q0 + t_begin) * a.Hq + kvh * a.g + hg * a.hpw) * a.D;
+  }
+};
+
+// Marker an overflowed FAST pass leaves in its item's first output element
+// (and nothing else): a signalling NaN of the output format.  Arithmetic
+// never yields a signalling NaN (the output conversions and products quiet
+// any NaN), so a marker is never a result; a stale one in a row that a
+// later FAST pass overwrites is gone with it.
+constexpr uint32_t kMarkF32 = 0x7FA5A5A5u;
+constexpr uint16_t kMarkBf16 = 0x7F85u, kMarkF16 = 0x7D05u;
+
+__device__ __forceinline__ void mark_overflow(const PrefillArgs& a, int64_t off) {
+  if (a.out_type == kOutF32) static_cast<uint32_t*>(a.out)[off] = kMarkF32;
+  else static_cast<uint16_t*>(a.out)[off] = a.out_type == kOutBf16 ? kMarkBf16 : kMarkF16;
+}
+
+__device__ __forceinline__ bool marked(const PrefillArgs& a, int64_t off) {
+  if (a.out_type == kOutF32) return static_cast<const uint32_t*>(a.out)[off] == kMarkF32;
+  return static_cast<const uint16_t*>(a.out)[off] ==
+         (a.out_type == kOutBf16 ? kMarkBf16 : kMarkF16);
+}
+
+// The workgroup's whole computation of one item, in the FAST mode (SAFE =
+// false: returns true when the pass overflowed; it then stores only the
+// item's marker) or the SAFE mode (SAFE = true: the rescaling passes, one
+// tile and half of the output dims at a time).  st0 .. st2: the LDS ring's
+// stages (a K tile, then a V tile); s_range, s_flag: LDS scratch of the
+// workgroup.
 template <int D, bool BF16, bool SAFE>
-__device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0, uint16_t* st1,
-                                             uint16_t* st2, int* s_range, int* s_flag) {
+__device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const PrefillItem& it,
+                                             uint16_t* st0, uint16_t* st1, uint16_t* st2,
+                                             int* s_range, int* s_flag) {
   using Mf = Mfma<BF16>;
   using F = Fmt<BF16>;
   constexpr int TW = PrefillTile<D>::TW, BN = PrefillTile<D>::BN;
@@ -167,36 +233,15 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0
   constexpr int CPR = D / 8;              // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;           // key rows per wave-wide 16-byte load
   constexpr int TILE = BN * D;            // elements of one K or V tile
+  constexpr int kPW = PrefillTile<D>::PW;
   constexpr int LPT = TILE / 8 / 64 / kPW;   // wave-wide loads per wave, tile and tensor
   static_assert(LPT >= 1 && TILE / 8 == LPT * 64 * kPW, "tile loads must divide over the waves");
   static_assert(2 * LPT < 16, "outstanding loads must fit the vmcnt field");
   static_assert(kStages == 3, "three ring stages");
 
-  const int item = (int)blockIdx.x;
-  if (item >= a.items) return false;
-  const int mt = a.m_tiles - 1 - item / a.groups;
-  const int grp = item - (item / a.groups) * a.groups;
-  const int nbk = a.B * a.Hkv;
-  const int hg = grp / nbk, bk = grp - hg * nbk;
-  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-
-  // the request's rows (packed offsets clamped into the tensors)
-  int q0, sq, k0, sk;
-  if (a.qo) {
-    const int c0 = min(max(a.qo[b], 0), a.rows_q), c1 = min(max(a.qo[b + 1], 0), a.rows_q);
-    const int d0 = min(max(a.kvo[b], 0), a.rows_kv), d1 = min(max(a.kvo[b + 1], 0), a.rows_kv);
-    q0 = c0;
-    sq = min(max(c1 - c0, 0), a.Sq);
-    k0 = d0;
-    sk = max(d1 - d0, 0);
-  } else {
-    q0 = b * a.Sq;
-    sq = a.Sq;
-    k0 = b * a.Sk;
-    sk = a.Sk;
-  }
-  const int t_begin = mt * a.tt;   // first query token of the workgroup
-  if (t_begin >= sq) return false;   // uniform over the workgroup
+  const int b = it.b, kvh = it.kvh, hg = it.hg;
+  const int q0 = it.q0, sq = it.sq, k0 = it.k0, sk = it.sk;
+  const int t_begin = it.t_begin;   // first query token of the workgroup
 
   // keys query token i sees: [lo, hi] (empty when hi < lo)
   auto bounds = [&](int i, int& lo, int& hi) {
@@ -427,7 +472,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0
         }
         return vb;
       };
-      constexpr int VPRE = !SAFE && NUP <= 8 ? 4 : 2;   // V operands read ahead of P . V
+      constexpr int VPRE = 2;   // V operands read ahead of P . V
       u32x4 vb[VPRE];
 #pragma unroll
       for (int u = 0; u < VPRE; ++u) vb[u] = vread(U0 + u);
@@ -550,7 +595,10 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0
           over |= tok0_t[T0 + t] + 4 * lq + i < sq && !(lsum[t][i] < INFINITY);
       if (wave_any(over)) *s_flag = 1;
       lds_barrier();
-      if (*s_flag) return true;
+      if (*s_flag) {
+        if (threadIdx.x == 0) mark_overflow(a, it.first_out(a));
+        return true;
+      }
     }
 
     // epilogue: out = O / l * output_scale for rows 4q + i, dims 16u + j
@@ -597,32 +645,59 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, uint16_t* st0
   }
 }
 
-// The SAFE passes as a function of their own, so that their register
-// demand (accumulators in ordinary registers) does not shape the register
-// allocation of the FAST loop; it is only called after a FAST pass
-// overflowed.
+// FAST pass: one workgroup per item.
 template <int D, bool BF16>
-__device__ __noinline__ void prefill_safe(const PrefillArgs& a, uint16_t* st0, uint16_t* st1,
-                                          uint16_t* st2, int* s_range, int* s_flag) {
-  prefill_body<D, BF16, true>(a, st0, st1, st2, s_range, s_flag);
-}
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kPW, 1) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * PrefillTile<D>::PW, 1) void prefill_kernel(const PrefillArgs a) {
   constexpr int TILE = PrefillGeom<D>::TILE;
   __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
   __shared__ int s_range[2];
-  __shared__ int s_flag;   // a FAST pass overflowed (see attend)
-  if (prefill_body<D, BF16, false>(a, st0, st1, st2, s_range, &s_flag))
-    prefill_safe<D, BF16>(a, st0, st1, st2, s_range, &s_flag);
+  __shared__ int s_flag;   // the pass overflowed (see attend)
+  PrefillItem it;
+  if (!it.init(a, (int)blockIdx.x)) return;   // uniform over the workgroup
+  prefill_body<D, BF16, false>(a, it, st0, st1, st2, s_range, &s_flag);
+}
+
+// SAFE passes, launched after the FAST kernel on the same stream with at
+// most one workgroup per CU: workgroup w takes the items w, w + G, w + 2G ..
+// (G = its grid), finds with one load per thread which of them hold the
+// marker of an overflowed FAST pass, and recomputes those one by one.  A
+// kernel of its own, so that the rescaling passes' register demand does not
+// shape the register allocation of the FAST loop.
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * PrefillTile<D>::PW, 1) void prefill_safe_kernel(const PrefillArgs a) {
+  constexpr int TILE = PrefillGeom<D>::TILE;
+  constexpr int NT = 64 * PrefillTile<D>::PW;   // items checked per pass
+  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
+  __shared__ int s_range[2];
+  __shared__ int s_flag;
+  __shared__ int s_list[NT];
+  __shared__ int s_n;
+  const int G = (int)gridDim.x, w = (int)blockIdx.x;
+  const int ncand = (a.items - w + G - 1) / G;   // this workgroup's items
+  for (int base = 0; base < ncand; base += NT) {
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    const int j = base + (int)threadIdx.x;
+    PrefillItem it;
+    if (j < ncand && it.init(a, w + j * G) && marked(a, it.first_out(a)))
+      s_list[atomicAdd(&s_n, 1)] = w + j * G;
+    __syncthreads();
+    const int n = uniform(s_n);
+    for (int k = 0; k < n; ++k) {
+      PrefillItem m;
+      m.init(a, uniform(s_list[k]));   // true: it was listed
+      prefill_body<D, BF16, true>(a, m, st0, st1, st2, s_range, &s_flag);
+    }
+    __syncthreads();   // s_n and s_list are reused by the next pass
+  }
 }
 
 }  // namespace
 
 bool prefill_geometry(int head_dim, int g, int* hpw, int* tt) {
   int rows;
-  if (head_dim == 128) rows = kPW * 16 * PrefillTile<128>::TW;
-  else if (head_dim == 256) rows = kPW * 16 * PrefillTile<256>::TW;
+  if (head_dim == 128) rows = PrefillTile<128>::PW * 16 * PrefillTile<128>::TW;
+  else if (head_dim == 256) rows = PrefillTile<256>::PW * 16 * PrefillTile<256>::TW;
   else return false;
   int p = 1;
   while (p * 2 <= rows / 16 && g % (p * 2) == 0) p *= 2;
@@ -631,19 +706,23 @@ bool prefill_geometry(int head_dim, int g, int* hpw, int* tt) {
   return true;
 }
 
+namespace {
+template <int D, bool BF16>
+hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid(a.items), block(64 * PrefillTile<D>::PW);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_safe_kernel<D, BF16>), dim3(a.safe_grid), block, 0, stream, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, hipStream_t stream) {
   if (a.items <= 0) return hipSuccess;
-  const dim3 grid(a.items), block(64 * kPW);
-  if (a.D == 128) {
-    if (bf16) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, a);
-  } else if (a.D == 256) {
-    if (bf16) hipLaunchKernelGGL((prefill_kernel<256, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<256, false>), grid, block, 0, stream, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.D == 128) return bf16 ? launch_prefill_d<128, true>(a, stream) : launch_prefill_d<128, false>(a, stream);
+  if (a.D == 256) return bf16 ? launch_prefill_d<256, true>(a, stream) : launch_prefill_d<256, false>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkvd

@@ -113,13 +113,63 @@ def test_prefill_configs_sampled(name):
     compare(name, got[sel], ref)
 
 
+@pytest.mark.parametrize("out_dtype", [None, "fp32"])
 @pytest.mark.parametrize("dtype,sm_scale", [("bf16", 30.0), ("fp16", 3.0)])
 @pytest.mark.parametrize("D", [128, 256])
-def test_prefill_large_logits(D, dtype, sm_scale):
-    """Scores spread over hundreds of base-2 units: later keys exceed a row's
-    first maximum by far more than the fast pass allows (2^64 for bf16, 2^15
-    for fp16 probabilities), so the kernel must take its rescaling pass."""
+def test_prefill_large_logits(D, dtype, sm_scale, out_dtype):
+    """Scores spread over hundreds of base-2 units: earlier keys exceed the
+    score of a row's last visible key by far more than the fast pass allows
+    (2^128 for bf16 probabilities, 2^24 for fp16), so every workgroup's fast
+    pass overflows and the rescaling kernel recomputes it."""
     inp = workloads.make_prefill_case(B=2, Sq=140, Sk=300, Hq=4, Hkv=2, D=D, dtype=dtype,
                                       mask_type="causal", seed=77)
     inp["sm_scale"] = sm_scale
-    compare(f"large_logits/D{D}/{dtype}", run(inp), oracle.prefill(inp))
+    compare(f"large_logits/D{D}/{dtype}/{out_dtype}", run(inp, ODT.get(out_dtype)),
+            oracle.prefill(inp))
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (256, 16, 4)])
+def test_prefill_large_logits_many_items(D, Hq, Hkv):
+    """Every fast pass overflows and there are more workgroup items (512)
+    than CUs: each workgroup of the rescaling kernel recomputes several.
+    Sampled rows against the oracle."""
+    inp = workloads.make_prefill_case(B=4, Sq=1024, Sk=1024, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                                      mask_type="causal", seed=79)
+    inp["sm_scale"] = 30.0
+    rows = 4 * 1024
+    g = torch.Generator().manual_seed(9)
+    sel = sorted(set(torch.randint(0, rows * Hq, (300,), generator=g).tolist())
+                 | {0, rows * Hq - 1})
+    got = run(inp)
+    compare(f"large_logits_many/D{D}", got[sel], oracle.prefill(inp, sel=sel))
+
+
+# bit patterns of signalling NaNs in each output format (what an output
+# buffer may hold from an earlier call or from the allocator)
+SNAN = {"bf16": (torch.int16, 0x7F85), "fp16": (torch.int16, 0x7D05),
+        "fp32": (torch.int32, 0x7FA5A5A5)}
+
+
+@pytest.mark.parametrize("out_name", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_some_overflow_snan_out(D, out_name):
+    """One kv head of one request has keys scaled far up (its workgroups'
+    fast passes overflow, the others' do not), written into an output
+    buffer that starts out full of signalling NaNs: every row must hold the
+    oracle's value afterwards."""
+    import paged_kv_decode_12_amd as pk
+    inp = workloads.make_prefill_case(B=3, Hq=8, Hkv=2, D=D, dtype="fp16", q_lens=(90, 1, 200),
+                                      kv_lens=(90, 50, 260), mask_type="causal", seed=78)
+    k = inp["k"].clone()
+    r0, r1 = int(inp["kv_indptr"][2]), int(inp["kv_indptr"][3])
+    k[r0:r1, 1] *= 12.0   # request 2, kv head 1
+    inp["k"] = k
+    dt, bits = SNAN[out_name]
+    out = torch.full(inp["q"].shape, bits, dtype=dt, device="cuda").view(ODT[out_name])
+    dev = {n: (v.cuda() if torch.is_tensor(v) else v) for n, v in inp.items()}
+    pk.batch_prefill(dev["q"], dev["k"], dev["v"], qo_indptr=dev["qo_indptr"],
+                     kv_indptr=dev["kv_indptr"], mask_type="causal", sm_scale=dev["sm_scale"],
+                     out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(-1, D)
+    compare(f"some_overflow/D{D}/{out_name}", got, oracle.prefill(inp))
