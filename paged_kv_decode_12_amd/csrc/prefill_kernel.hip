@@ -165,8 +165,16 @@ struct PrefillItem {
   // false when the item holds no query token of its request (nothing to do)
   __device__ __forceinline__ bool init(const PrefillArgs& a, int item) {
     if (item >= a.items) return false;
-    mt = a.m_tiles - 1 - item / a.groups;   // token tiles from the last to the first
-    const int grp = item - (item / a.groups) * a.groups;
+    // Token tiles from the last to the first (the costliest first under a
+    // causal mask).  Within a tile level the head groups rotate by 8 per
+    // level: workgroups reach the XCDs in turn (item mod 8, which the shift
+    // keeps, so an XCD keeps reading the same kv heads) and within an XCD
+    // its shader engines in turn; without the shift a shader engine would
+    // take the same requests at every level, and requests of unequal
+    // lengths would load some engines far more than others.
+    const int lvl = item / a.groups;
+    mt = a.m_tiles - 1 - lvl;
+    const int grp = (int)(((int64_t)(item - lvl * a.groups) + 8 * (int64_t)lvl) % a.groups);
     const int nbk = a.B * a.Hkv;
     hg = grp / nbk;
     const int bk = grp - hg * nbk;
