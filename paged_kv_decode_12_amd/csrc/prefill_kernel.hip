@@ -4,16 +4,24 @@
 // dense or per-query variable windows, a left window, sm_scale,
 // output_scale and the output type.
 //
-// Work split.  A workgroup (four waves, one per SIMD) takes `hpw` query heads
-// that share one kv head (grouped-query packing) times `tt` query tokens:
-// 256 rows at head_dim 128 (64 per wave), 128 at 256 (32 per wave).  Every
-// key/value byte it stages in LDS therefore serves all of those rows, and
-// each wave reads the staged tile once for its 4 (or 2) 16-row MFMA tiles.
-// Items run over (token tile, request, kv head, head group) with the token
-// tiles from the last to the first (the longest causal rows start first);
-// when the number of (request, kv head) pairs is a multiple of eight, the
-// items of one pair share an XCD (hardware dispatch is round-robin over
-// XCDs), so their K/V stays in that XCD's L2.
+// Work split.  A workgroup takes `hpw` query heads that share one kv head
+// (grouped-query packing) times `tt` query tokens: 256 rows at head_dim 128
+// (eight waves, two per SIMD, 32 rows each), 128 at 256 (four waves, 32
+// rows each).  Every key/value byte it stages in LDS therefore serves all of
+// those rows, and each wave reads the staged tile once for its two 16-row
+// MFMA tiles.  Items run over (token tile, request, kv head, head group)
+// with the token tiles from the last to the first (the longest causal rows
+// start first); when the number of (request, kv head, head group) triples is
+// a multiple of eight, the items of one triple share an XCD (hardware
+// dispatch is round-robin over XCDs), so their K/V stays in that XCD's L2.
+//
+// Two kernels.  The FAST kernel scores every row against a fixed reference
+// (the score of the row's last visible key), so its loop holds no running
+// maxima; a workgroup whose probabilities leave the range of their format
+// marks its item and stores nothing else.  The SAFE kernel, launched next on
+// the same stream, recomputes the marked items with a lazily raised running
+// maximum (raised only when a score exceeds it by more than kTau) and
+// rescaled accumulators.
 //
 // Staging.  K and V tiles of BN keys go through a three-stage LDS ring,
 // filled with direct global-to-LDS 16-byte loads (no registers) two tiles
@@ -26,9 +34,8 @@
 //    (j = l % 16, q = l / 16) feeds key j's dims 32c + 8q .. +8 (A) and row
 //    j's same dims of Q (B, in registers); the two 16-key halves give lane l
 //    the scores of row j for keys 4q + i and 16 + 4q + i, i = 0..3;
-//  * masks by select; online softmax in base 2 with a lazily raised
-//    maximum (only when a score exceeds it by more than kTau), row maxima
-//    across the row's four lanes with lane-pair swaps;
+//  * masks by select (only in chunks some row sees in part); probabilities
+//    2^(score - reference) in base 2; row sums by an MFMA against ones;
 //  * O += P . V with the same 16x16x32 instruction: the lane's eight
 //    probabilities are the A operand of row j for the key order
 //    (4q .. 4q + 3, 16 + 4q .. 16 + 4q + 3), and the B operand for output
@@ -456,9 +463,10 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
     }
 
     // 32 keys from j0 (tile rows kc * 32 ..) of the stage at sK / sV.
-    // MASKED: some row sees only part of them.
-    auto chunk = [&](auto masked_tag, const uint16_t* sK, const uint16_t* sV, int kc, int j0) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
+    // masked (uniform): some row sees only part of them.  One body for both
+    // cases, so that the accumulators keep their registers from chunk to
+    // chunk (two bodies had them copied at every join).
+    auto chunk = [&](bool masked, const uint16_t* sK, const uint16_t* sV, int kc, int j0) {
       u32x4 ka[2][NC];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -505,7 +513,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
           x[i] = s0[i];
           x[4 + i] = s1[i];
         }
-        if constexpr (MASKED) {
+        if (masked) {   // uniform
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int key = j0 + (e < 4 ? 4 * lq + e : 16 + 4 * lq + e - 4);
@@ -565,14 +573,12 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
       const uint16_t* sK = stage;
       const uint16_t* sV = stage + TILE;
       const int kb = kbase + it * BN;
-#pragma unroll 1
+#pragma unroll
       for (int kc = 0; kc < BN / 32; ++kc) {
         const int j0 = kb + kc * 32;
         if (j0 > whi || j0 + 31 < wlo) continue;   // no row of this wave sees these keys
-        if (j0 >= wmaxlo && j0 + 31 <= wminhi)   // every live row sees all of them
-          chunk(std::false_type{}, sK, sV, kc, j0);
-        else
-          chunk(std::true_type{}, sK, sV, kc, j0);
+        // masked unless every live row sees all of them
+        chunk(!(j0 >= wmaxlo && j0 + 31 <= wminhi), sK, sV, kc, j0);
       }
       if (it + 1 < ntiles) {
         // the next tile's loads have landed (the one after may still be in flight)
