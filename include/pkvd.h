@@ -281,6 +281,17 @@ int pkvd_decode_workspace_bytes(const pkvd_tensor* q, const pkvd_tensor* k_cache
 int pkvd_reserve_workspace(size_t bytes);
 
 /*
+ * pkvd_workspace_capacity -- bytes the workspace of the next pkvd_decode on
+ * the current device holds: the bound caller-owned buffer's size when one is
+ * bound, else the library-owned buffer's (0 before any call or
+ * reservation).  A call whose pkvd_decode_workspace_bytes is at most this
+ * needs no allocation, so it may be captured into a HIP graph
+ * (batch_decode_with_paged_kv_cache, summary: plan before capture).
+ * Returns a status; the size is written to *bytes.
+ */
+int pkvd_workspace_capacity(size_t* bytes);
+
+/*
  * pkvd_set_workspace -- bind a caller-owned device buffer as the workspace of
  * every later pkvd_decode (and pkvd_decode_ex without its own workspace) on
  * the current device (cudnn_batch_decode_with_kv_cache, Parameters /

@@ -91,6 +91,8 @@ def _load():
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.pkvd_reserve_workspace.restype = ctypes.c_int
     lib.pkvd_reserve_workspace.argtypes = [ctypes.c_size_t]
+    lib.pkvd_workspace_capacity.restype = ctypes.c_int
+    lib.pkvd_workspace_capacity.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
     lib.pkvd_decode_plan.restype = ctypes.c_int
     lib.pkvd_decode_plan.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int64 * 6)]
@@ -490,6 +492,14 @@ def reserve_workspace(nbytes: int, device=None) -> None:
     """Grow the library-owned split workspace of ``device`` before graph capture."""
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
         _check(_lib.pkvd_reserve_workspace(int(nbytes)))
+
+
+def workspace_capacity(device=None) -> int:
+    """Bytes the workspace of ``device``'s next decode holds (pkvd_workspace_capacity)."""
+    n = ctypes.c_size_t(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(_lib.pkvd_workspace_capacity(ctypes.byref(n)))
+    return n.value
 
 
 def set_workspace(buf: Optional[torch.Tensor], device=None) -> None:

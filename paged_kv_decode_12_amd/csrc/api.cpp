@@ -729,6 +729,18 @@ int pkvd_reserve_workspace(size_t bytes) {
   return grow_library_workspace(dev, bytes, nullptr, false);
 }
 
+int pkvd_workspace_capacity(size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(PKVD_ERR_INVALID_ARG, "bytes is NULL");
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != PKVD_OK) return st;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const DeviceWorkspace& w = g_ws[dev];
+  *bytes = w.bound ? w.bound_bytes : w.bytes;
+  return PKVD_OK;
+}
+
 int pkvd_set_workspace(void* dev_ptr, size_t bytes) {
   g_last_error.clear();
   int dev = 0;

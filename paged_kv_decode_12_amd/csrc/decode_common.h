@@ -282,14 +282,15 @@ __device__ __forceinline__ void write_empty_request(const DecodeArgs& a, ReqRows
     }
 }
 
-// Builds pref[0..B], vpref[0..B], the raw lengths nlen[0..B-1], (packed rows)
+// Builds pref[0..B], vpref[0..B], the raw lengths nlen[0..B-1], the blocks
+// per unit nb[0..B-1], (packed rows)
 // the clamped query offsets qo[0..B] and (when staged) the sink logits in
 // LDS (one workgroup, ends with a barrier).  Requests with query rows but no
 // visible key get out = 0, lse = -inf here, written by workgroup b % gridDim.x.
 template <int NT>
 __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref, int* s_vpref,
-                                               int* s_nlen, int* s_qo, int* s_scan, int* s_vscan,
-                                               float* s_sink) {
+                                               int* s_nlen, int* s_nb, int* s_qo, int* s_scan,
+                                               int* s_vscan, float* s_sink) {
   const int B = a.B;
   const int CH = (B + NT - 1) / NT;
   const int t = threadIdx.x;
@@ -309,6 +310,7 @@ __device__ __forceinline__ Prefix build_prefix(const DecodeArgs& a, int* s_pref,
     }
     int nb, units;
     const ReqRows rr = req_blocks(a, b, nraw, c0, c1, nb, units);
+    s_nb[b] = nb;
     sum += nb * units;
     vsum += unit_vspan(a, nb) * units;
     if (nb == 0 && rr.lq > 0 && b % (int)gridDim.x == (int)blockIdx.x) write_empty_request(a, rr);
@@ -380,6 +382,22 @@ __device__ __forceinline__ int find_request(const int* s_pref, int B, int pos) {
   return base + (63 - __builtin_clzll(m));
 }
 
+// find_request for two positions at once (one LDS read per lane when B <= 64).
+__device__ __forceinline__ void find_request2(const int* s_pref, int B, int p0, int p1, int& b0,
+                                              int& b1) {
+  if (B > 64) {
+    b0 = find_request(s_pref, B, p0);
+    b1 = find_request(s_pref, B, p1);
+    return;
+  }
+  const int lane = __lane_id();
+  const int x = lane < B ? s_pref[lane] : 0;
+  const uint64_t m0 = __builtin_amdgcn_ballot_w64(lane < B && x <= p0);
+  const uint64_t m1 = __builtin_amdgcn_ballot_w64(lane < B && x <= p1);
+  b0 = 63 - __builtin_clzll(m0);
+  b1 = 63 - __builtin_clzll(m1);
+}
+
 // A unit's slice of one wave's range.
 struct Segment {
   int b, kvh, tile;
@@ -392,25 +410,25 @@ struct Segment {
   int side;                  // 0: first segment of the wave, 1: a later one
 };
 
-__device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
-                                          const int* s_vpref, const int* s_nlen, const int* s_qo,
-                                          int pos, int wave_lo, int wave_hi) {
+// The segment from real block pos of request b (real and virtual prefixes
+// pref_b, vpref_b), unit uidx of the request, within the wave's range
+// [wave_lo, wave_hi).
+__device__ __forceinline__ Segment segment_at(const DecodeArgs& a, const int* s_nlen,
+                                              const int* s_qo, int b, int pref_b, int vpref_b,
+                                              int uidx, int pos, int wave_lo, int wave_hi) {
   Segment g;
-  g.b = find_request(s_pref, a.B, pos);
-  const ReqInfo ri = req_info(a, s_nlen, s_qo, g.b);
+  g.b = b;
+  const ReqInfo ri = req_info(a, s_nlen, s_qo, b);
   g.u = ri.u;
   g.row0 = ri.rows.row0;
   g.lq = ri.rows.lq;
   g.R = a.g * g.lq;
-  const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[g.b]);
-  const int vpref_b = __builtin_amdgcn_readfirstlane(s_vpref[g.b]);
   const int nb = g.u.nblk > 0 ? g.u.nblk : 1;   // pos lies in a unit with blocks
-  const int off = pos - pref_b;
   const int per_req = ri.units > 0 ? ri.units : 1;
-  const int tiles = per_req / a.Hkv > 0 ? per_req / a.Hkv : 1;
-  int uidx = off / nb;
+  int tiles = a.qo ? tiles_of(a, g.lq) : a.row_tiles;
+  tiles = tiles > 0 ? tiles : 1;
   uidx = uidx < 0 ? 0 : (uidx >= per_req ? per_req - 1 : uidx);
-  g.kvh = uidx / tiles;
+  g.kvh = tiles == 1 ? uidx : uidx / tiles;
   g.tile = uidx - g.kvh * tiles;
   g.ustart = pref_b + uidx * nb;
   g.uend = g.ustart + nb;
@@ -423,15 +441,17 @@ __device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref
   return g;
 }
 
-// The real block at virtual block v (0 <= v <= TV), T at the end (see
-// real_block).
-__device__ __forceinline__ int real_of(const DecodeArgs& a, const int* s_pref, const int* s_vpref,
-                                       const int* s_nlen, const int* s_qo, const Prefix& p, int v) {
-  if (v >= p.TV) return p.T;
-  const int b = find_request(s_vpref, a.B, v);   // a request with blocks
-  const int nb = req_info(a, s_nlen, s_qo, b).u.nblk;
-  return real_block(a, __builtin_amdgcn_readfirstlane(s_pref[b]),
-                    __builtin_amdgcn_readfirstlane(s_vpref[b]), nb, v);
+// The segment that starts at real block pos.
+__device__ __forceinline__ Segment locate(const DecodeArgs& a, const int* s_pref,
+                                          const int* s_vpref, const int* s_nlen, const int* s_nb,
+                                          const int* s_qo, int pos, int wave_lo, int wave_hi) {
+  const int b = find_request(s_pref, a.B, pos);
+  const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[b]);
+  const int vpref_b = __builtin_amdgcn_readfirstlane(s_vpref[b]);
+  int nb = __builtin_amdgcn_readfirstlane(s_nb[b]);
+  nb = nb > 0 ? nb : 1;
+  return segment_at(a, s_nlen, s_qo, b, pref_b, vpref_b, (pos - pref_b) / nb, pos, wave_lo,
+                    wave_hi);
 }
 
 // ---------------------------------------------------------------------------

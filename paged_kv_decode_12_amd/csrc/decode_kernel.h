@@ -198,6 +198,7 @@ void decode_kernel(const DecodeArgs a) {
   int* s_pref = lds + L.pref;
   int* s_vpref = lds + L.vpref;
   int* s_nlen = lds + L.nlen;
+  int* s_nb = lds + L.nb;
   int* s_qo = lds + L.qo;
   float* s_sink = reinterpret_cast<float*>(lds + L.sink);
 
@@ -208,7 +209,8 @@ void decode_kernel(const DecodeArgs a) {
 #ifdef PKVD_TRACE
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 #endif
-  Prefix pf = build_prefix<kThreads>(a, s_pref, s_vpref, s_nlen, s_qo, s_scan, s_vscan, s_sink);
+  Prefix pf = build_prefix<kThreads>(a, s_pref, s_vpref, s_nlen, s_nb, s_qo, s_scan, s_vscan,
+                                     s_sink);
   pf.T = uniform(pf.T);
   pf.TV = uniform(pf.TV);
   const int T = pf.T;
@@ -231,9 +233,23 @@ void decode_kernel(const DecodeArgs a) {
 #ifdef PKVD_TRACE
   const uint64_t t_slices = __builtin_amdgcn_s_memrealtime();
 #endif
-  const int lo = T ? real_of(a, s_pref, s_vpref, s_nlen, s_qo, pf, slice_begin(sl_, gw)) : 0;
-  const int hi = T ? real_of(a, s_pref, s_vpref, s_nlen, s_qo, pf, slice_begin(sl_, gw + 1)) : 0;
-  if (T == 0 || gw >= NW || lo >= hi) return;   // no slice
+  if (T == 0 || gw >= NW) return;   // no slice
+  // The slice's virtual bounds, their requests (one search for both) and
+  // real blocks; the request and unit found for the first bound also give
+  // the first segment (a virtual block maps into its own request).
+  const int v_lo = slice_begin(sl_, gw), v_hi = slice_begin(sl_, gw + 1);
+  int b_lo, b_hi;
+  find_request2(s_vpref, a.B, v_lo, v_hi, b_lo, b_hi);
+  const int pref_lo = __builtin_amdgcn_readfirstlane(s_pref[b_lo]);
+  const int vpref_lo = __builtin_amdgcn_readfirstlane(s_vpref[b_lo]);
+  const int nb_lo = __builtin_amdgcn_readfirstlane(s_nb[b_lo]);
+  const int pref_hi = __builtin_amdgcn_readfirstlane(s_pref[b_hi]);
+  const int vpref_hi = __builtin_amdgcn_readfirstlane(s_vpref[b_hi]);
+  const int nb_hi = __builtin_amdgcn_readfirstlane(s_nb[b_hi]);
+  int ul_lo, ul_hi;
+  const int lo = v_lo < pf.TV ? pref_lo + real_off(a, nb_lo, v_lo - vpref_lo, ul_lo) : T;
+  const int hi = v_hi < pf.TV ? pref_hi + real_off(a, nb_hi, v_hi - vpref_hi, ul_hi) : T;
+  if (lo >= hi) return;
   PKVD_COUNT(a, gw, 0, t_start);
   PKVD_COUNT(a, gw, 1, t_prefix);
   PKVD_COUNT(a, gw, 12, t_slices);
@@ -281,8 +297,21 @@ void decode_kernel(const DecodeArgs a) {
     if (!c.last) {
       n = make_chunk(c.sg, c.ce);
     } else if (pos < hi) {
-      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, s_qo, pos, lo, hi);
-      n = make_chunk(sg, sg.blk_begin);
+      // the segment ended with its unit: the next unit of the same request
+      // (no search) or the first of a later request
+      const Segment& g = c.sg;
+      int tiles = a.qo ? tiles_of(a, g.lq) : a.row_tiles;
+      tiles = tiles > 0 ? tiles : 1;
+      const int uidx = g.kvh * tiles + g.tile;
+      if (uidx + 1 < a.Hkv * tiles && g.u.nblk > 0) {
+        const Segment sg = segment_at(a, s_nlen, s_qo, g.b, g.ustart - uidx * g.u.nblk,
+                                      g.vstart - uidx * unit_vspan(a, g.u.nblk), uidx + 1, pos,
+                                      lo, hi);
+        n = make_chunk(sg, sg.blk_begin);
+      } else {
+        const Segment sg = locate(a, s_pref, s_vpref, s_nlen, s_nb, s_qo, pos, lo, hi);
+        n = make_chunk(sg, sg.blk_begin);
+      }
     }
     return n;
   };
@@ -309,12 +338,15 @@ void decode_kernel(const DecodeArgs a) {
     int pend_unit[2] = {-1, -1}, pend_n[2] = {0, 0}, pend_vs[2] = {0, 0}, pend_nb[2] = {0, 0};
     Chunk cur;
     {
-      const Segment sg = locate(a, s_pref, s_vpref, s_nlen, s_qo, lo, lo, hi);
+      const Segment sg = segment_at(a, s_nlen, s_qo, b_lo, pref_lo, vpref_lo, ul_lo, lo, lo, hi);
       cur = make_chunk(sg, sg.blk_begin);
     }
     PKVD_STAMP(a, gw, 14);
     PageWindow pw = fetch_pages(cur);
     PKVD_STAMP(a, gw, 15);
+    // the next chunk and its page ids before the first K/V loads: a slice
+    // may start with a few blocks of a unit, and then its first chunk ends
+    // soon after those loads return
     Chunk nxt = next_chunk(cur);
     PageWindow pwn = nxt.valid ? fetch_pages(nxt) : pw;
     PKVD_STAMP(a, gw, 3);
@@ -501,17 +533,22 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (b >= a.B) return;
   const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
   const int row = tile * RT + r;
-  const ReqRows rows = req_rows(a, b);
+  // every per-request value in one round of loads (all indices are in range)
+  const int nraw = a.seq_lens[b];
+  const int q0 = a.qo ? a.qo[b] : 0, q1 = a.qo ? a.qo[b + 1] : 0;
+  const int T = a.ws_pref[a.B], TV = a.ws_vpref[a.B];
+  const int pref_b = a.ws_pref[b], vpref_b = a.ws_vpref[b];
+  const ReqRows rows = a.qo ? rows_of(a, clamp_row(a, q0), clamp_row(a, q1), b)
+                            : ReqRows{b * a.Lq, a.Lq};
   if (row >= a.g * rows.lq) return;   // a padding row, or a tile the request does not have
-  const UnitRange u = unit_range_n(a, a.seq_lens[b], rows.lq);
+  const UnitRange u = unit_range_n(a, nraw, rows.lq);
   if (u.nblk == 0) return;
   // the unit's place among its request's units (kv head major, then tiles)
   const int ub = a.qo ? kvh * tiles_of(a, rows.lq) + tile : uidx;
-  const int T = a.ws_pref[a.B];
   const int NW = wave_count(a, T);
-  const Slices sl_ = make_slices(a, a.ws_vpref[a.B], NW);
-  const int64_t us = a.ws_pref[b] + (int64_t)ub * u.nblk, ue = us + u.nblk;
-  const int64_t vs = a.ws_vpref[b] + (int64_t)ub * unit_vspan(a, u.nblk);
+  const Slices sl_ = make_slices(a, TV, NW);
+  const int64_t us = pref_b + (int64_t)ub * u.nblk, ue = us + u.nblk;
+  const int64_t vs = vpref_b + (int64_t)ub * unit_vspan(a, u.nblk);
   if (ue > T) return;
   const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, u.nblk);
   if (up.n == 1) return;   // inside one slice: written whole by the decode kernel
@@ -522,18 +559,33 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #pragma unroll
   for (int e = 0; e < NDL; ++e) pos[e] = Eng::ppos(r, lane * NDL + e);
   int written = 0;   // candidates that wrote a partial state
+  constexpr int kDepth = 8;
   for (int c0 = 0; c0 < up.n; c0 += 64) {
     const int c = c0 + lane;
     int slot = 0;
-    float l = -INFINITY;
     bool valid = false;
-    if (c < up.n) {
-      slot = candidate_slot(up, sl_, vs, c, valid);
-      if (valid) l = a.ws_lse[(int64_t)slot * RT + r];
-    }
+    if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
     uint64_t m = __builtin_amdgcn_ballot_w64(valid);
     if (m == 0) continue;
     written += __builtin_popcountll(m);
+    // The batch's LSEs and the outputs of its first kDepth written pieces
+    // in one round of loads (the outputs' addresses need only the slots);
+    // off entries of a group read the batch's first written piece (finite
+    // values) with weight 0.
+    const float l = valid ? a.ws_lse[(int64_t)slot * RT + r] : -INFINITY;
+    const int sl0 = __builtin_amdgcn_readlane(slot, (int)__builtin_ctzll(m));
+    int qs[kDepth];
+    float oq[kDepth][NDL];
+#pragma unroll
+    for (int e = 0; e < kDepth; ++e) {
+      const bool on = m != 0;
+      qs[e] = on ? (int)__builtin_ctzll(m) : -1;
+      m = on ? m & (m - 1) : m;
+      const int sl = on ? __builtin_amdgcn_readlane(slot, qs[e]) : sl0;
+      const float* po = a.ws_o + (int64_t)sl * RT * D;
+#pragma unroll
+      for (int x = 0; x < NDL; ++x) oq[e][x] = po[pos[x]];
+    }
     const float Mn = fmaxf(M, wave_max(l));
     const float wt = valid ? rescale(l, Mn) : 0.f;
     const float sc = rescale(M, Mn);
@@ -541,20 +593,25 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
 #pragma unroll
     for (int e = 0; e < NDL; ++e) acc[e] *= sc;
     M = Mn;
-    constexpr int kDepth = 8;
-    // off entries of a group read the batch's first written piece (finite
-    // values) with weight 0
-    const int sl0 = __builtin_amdgcn_readlane(slot, (int)__builtin_ctzll(m));
-    while (m) {   // uniform: the written pieces of this batch, in order
-      float wq[kDepth], oq[kDepth][NDL];
+    auto weight_of = [&](int q) {   // piece q's weight (0 for an off entry, q = -1)
+      const float w = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), q < 0 ? 0 : q));
+      return q < 0 ? 0.f : w;
+    };
+#pragma unroll
+    for (int e = 0; e < kDepth; ++e) {
+      const float w_q = weight_of(qs[e]);
+#pragma unroll
+      for (int x = 0; x < NDL; ++x) acc[x] = fmaf(w_q, oq[e][x], acc[x]);
+    }
+    while (m) {   // uniform: the batch's further written pieces, in order
+      float wq[kDepth];
 #pragma unroll
       for (int e = 0; e < kDepth; ++e) {
         const bool on = m != 0;
-        const int q = on ? (int)__builtin_ctzll(m) : 0;
+        const int q = on ? (int)__builtin_ctzll(m) : -1;
         m = on ? m & (m - 1) : m;
-        const float w_q = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), q));
-        wq[e] = on ? w_q : 0.f;
+        wq[e] = weight_of(q);
         const int sl = on ? __builtin_amdgcn_readlane(slot, q) : sl0;
         const float* po = a.ws_o + (int64_t)sl * RT * D;
 #pragma unroll

@@ -116,6 +116,7 @@ struct Slices {
   int64_t SP;    // total weight of one group's PER waves
   int64_t S;     // total weight of the NW waves
   int n_min;     // blocks of the shortest slice (a lower bound)
+  int qT, rT;    // T = qT NW + rT (equal weights)
 };
 // Total weight of the first m waves of a group (0 <= m <= PER).
 __host__ __device__ __forceinline__ int64_t group_weight(const Slices& s, int m) {
@@ -152,12 +153,18 @@ __host__ __device__ __forceinline__ Slices make_slices(const DecodeArgs& a, int 
   }
   s.SP = group_weight(s, s.PER);
   s.S = weight_before(s, NW);
-  s.n_min = s.uniform ? T / NW : (int)qdiv((int64_t)T * wmin, s.S);
+  s.qT = T / NW;
+  s.rT = T - s.qT * NW;
+  s.n_min = s.uniform ? s.qT : (int)qdiv((int64_t)T * wmin, s.S);
   return s;
 }
-// First block of wave w's slice (w <= NW).
+// First block of wave w's slice (w <= NW).  Equal weights: floor(T w / NW)
+// = qT w + floor(rT w / NW), in 32 bits while NW^2 fits.
 __host__ __device__ __forceinline__ int slice_begin(const Slices& s, int w) {
-  if (s.uniform) return (int)qdiv((int64_t)s.T * w, s.NW);
+  if (s.uniform) {
+    if (s.NW <= 32768) return s.qT * w + (s.rT * w) / s.NW;
+    return (int)qdiv((int64_t)s.T * w, s.NW);
+  }
   return (int)qdiv((int64_t)s.T * weight_before(s, w), s.S);
 }
 // The wave whose slice holds block x (0 <= x < T): the largest w with
@@ -224,11 +231,12 @@ __host__ __device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
 }
 
 // Dynamic LDS of a workgroup of NT threads, in 32-bit words: the scan scratch
-// (2 NT), the block prefixes (2 (B + 1)), the raw lengths (B), the clamped
+// (2 NT), the block prefixes (2 (B + 1)), the raw lengths (B), the blocks per
+// unit (B), the clamped
 // packed query offsets (B + 1, packed rows only) and the sink logits (NS).
 // Host (launch size) and kernel (carve-up) both take the offsets from here.
 struct LdsLayout {
-  int scan, vscan, pref, vpref, nlen, qo, sink, total;
+  int scan, vscan, pref, vpref, nlen, nb, qo, sink, total;
 };
 // NS: sink logits staged in LDS (Hq when they are, else 0).
 __host__ __device__ inline LdsLayout lds_layout(int B, int NT, int NS, bool packed) {
@@ -238,7 +246,8 @@ __host__ __device__ inline LdsLayout lds_layout(int B, int NT, int NS, bool pack
   l.pref = l.vscan + NT;
   l.vpref = l.pref + B + 1;
   l.nlen = l.vpref + B + 1;
-  l.qo = l.nlen + B;
+  l.nb = l.nlen + B;
+  l.qo = l.nb + B;
   l.sink = l.qo + (packed ? B + 1 : 0);
   l.total = l.sink + NS;
   return l;
@@ -267,14 +276,23 @@ __host__ __device__ __forceinline__ int unit_vspan(const DecodeArgs& a, int nb) 
 // first real block for its virtual blocks.  With unit_mode each virtual
 // block is one whole unit, so every slice bound is a unit start and no unit
 // is cut.
+// real_off: the same for the request's virtual offset off = v - vpref_b,
+// relative to the request's first real block, and the unit ul (of the
+// request) that holds it.
+__host__ __device__ __forceinline__ int real_off(const DecodeArgs& a, int nb, int off, int& ul) {
+  if (a.unit_mode) {
+    ul = off;
+    return off * nb;
+  }
+  const int vu = nb + a.seg_cost;
+  ul = vu > 0 ? off / vu : 0;
+  const int o = off - ul * vu - a.seg_cost;
+  return ul * nb + (o > 0 ? o : 0);
+}
 __host__ __device__ __forceinline__ int real_block(const DecodeArgs& a, int pref_b, int vpref_b,
                                                    int nb, int v) {
-  const int off = v - vpref_b;
-  if (a.unit_mode) return pref_b + off * nb;
-  const int vu = nb + a.seg_cost;
-  const int ul = vu > 0 ? off / vu : 0;
-  const int o = off - ul * vu - a.seg_cost;
-  return pref_b + ul * nb + (o > 0 ? o : 0);
+  int ul;
+  return pref_b + real_off(a, nb, v - vpref_b, ul);
 }
 
 }  // namespace dev

@@ -30,6 +30,13 @@ def test_header_symbols_exported():
         assert hasattr(lib, n), n
 
 
+def test_workspace_capacity_null():
+    """pkvd_workspace_capacity rejects a NULL result pointer before touching
+    any device."""
+    assert pk._lib.pkvd_workspace_capacity(None) == 1   # PKVD_ERR_INVALID_ARG
+    assert b"NULL" in pk._lib.pkvd_last_error()
+
+
 def test_version_and_status_strings():
     assert pk.version().count(".") == 2
     for code in range(5):

@@ -278,7 +278,8 @@ def test_graph_replay_after_larger_eager_call():
         compare(f"graph_after_growth/{it}", out.float().cpu().numpy().reshape(-1, 128),
                 lse.cpu().numpy().reshape(-1), rs[0], rs[1])
     # a call that needs more than the workspace holds, inside a capture: an
-    # error, no allocation (the capture itself ends cleanly, empty)
+    # error, no allocation (the capture itself ends cleanly, empty); one that
+    # fits what the workspace already holds is captured
     huge = workloads.make_case(B=64, Hq=32, Hkv=2, D=128, page_size=16,
                                seq_lens=tuple([1500] * 64), seed=36)
     dh = to_dev_ex(huge)
@@ -286,6 +287,9 @@ def test_graph_replay_after_larger_eager_call():
         with env_waves("4096"):
             need_h = pk.workspace_bytes(dh["q"], dh["k_cache"], dh["block_tables"])
             assert need_h > need_big
+            # earlier tests of the session may have grown the workspace
+            # beyond need_h already: then the capture needs no growth
+            fits = pk.workspace_capacity() >= need_h
             st2 = torch.cuda.Stream()
             st2.wait_stream(torch.cuda.current_stream())
             g2 = torch.cuda.CUDAGraph()
@@ -298,7 +302,7 @@ def test_graph_replay_after_larger_eager_call():
                     except pk.PkvdError as e:
                         raised = "capturing" in str(e)
             torch.cuda.synchronize()
-            assert raised
+            assert raised != fits, (fits, raised)
 
 
 class env_waves:
