@@ -460,7 +460,9 @@ def summarize(args):
         import workloads
         kt = _csv_rows(d + "/**/*kernel_trace.csv")
         dec = [r for r in kt if kfilter in r["Kernel_Name"]]
-        mer = [r for r in kt if "merge_kernel" in r["Kernel_Name"]]
+        # the second kernel of a call: the merge (decode), the rescaling pass (prefill)
+        second = "prefill_safe_kernel" if pre else "merge_kernel"
+        mer = [r for r in kt if second in r["Kernel_Name"]]
         dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         dd = [dur(r) for r in dec]
         nbytes = (prefill_flops(workloads.make_prefill_config(w)) if pre
@@ -479,10 +481,10 @@ def summarize(args):
         tot = statistics.mean(dd)
         if mer:
             md = [dur(r) for r in mer]
-            L += [f"merge_kernel: {mer[0]['Kernel_Name'][:100]}",
-                  f"merge_dispatches: {len(md)}  median_us: {statistics.median(md):.2f}  mean_us: "
-                  f"{statistics.mean(md):.2f}",
-                  f"decode_plus_merge_mean_us: {tot + statistics.mean(md):.2f}"]
+            L += [f"{second}: {mer[0]['Kernel_Name'][:100]}",
+                  f"{second.split('_kernel')[0]}_dispatches: {len(md)}  median_us: "
+                  f"{statistics.median(md):.2f}  mean_us: {statistics.mean(md):.2f}",
+                  f"{fam}_plus_{second.split('_kernel')[0]}_mean_us: {tot + statistics.mean(md):.2f}"]
             tot += statistics.mean(md)
         if pre:
             L += [f"algorithmic_flops_per_launch: {nbytes}",
