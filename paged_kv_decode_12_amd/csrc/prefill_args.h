@@ -46,8 +46,9 @@ struct PrefillArgs {
 };
 
 // Query heads and tokens per workgroup for a head_dim and GQA group size g:
-// *hpw = the largest power of two dividing g (at most the workgroup's 16-row
-// tiles), *tt = its rows / *hpw.  Returns false for an unsupported head_dim.
+// *hpw = the largest power of two dividing both g and the workgroup's number
+// of 16-row tiles, *tt = its rows / *hpw (a multiple of 16).  Returns false
+// for an unsupported head_dim.
 bool prefill_geometry(int head_dim, int g, int* hpw, int* tt);
 // Launch (prefill_kernel.hip).  Returns the hipError_t of the launch.
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, hipStream_t stream);

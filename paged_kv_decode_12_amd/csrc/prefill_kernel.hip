@@ -6,10 +6,10 @@
 //
 // Work split.  A workgroup takes `hpw` query heads that share one kv head
 // (grouped-query packing) times `tt` query tokens: 256 rows at head_dim 128
-// (eight waves, two per SIMD, 32 rows each), 128 at 256 (four waves, 32
+// (eight waves, two per SIMD, 32 rows each), 128 at 256 (eight waves, 16
 // rows each).  Every key/value byte it stages in LDS therefore serves all of
-// those rows, and each wave reads the staged tile once for its two 16-row
-// MFMA tiles.  Items run over (token tile, request, kv head, head group)
+// those rows, and each wave reads the staged tile once for its one or two
+// 16-row MFMA tiles.  Items run over (token tile, request, kv head, head group)
 // with the token tiles from the last to the first (the longest causal rows
 // start first); when the number of (request, kv head, head group) triples is
 // a multiple of eight, the items of one triple share an XCD (hardware
@@ -60,10 +60,11 @@ using namespace dev;
 
 constexpr int kStages = 3;   // K/V tiles in the LDS ring
 
-// Workgroup shape per head_dim.  At D = 128 two waves share each SIMD (256
-// registers per lane each) so that one wave's MFMA work covers the other's
-// softmax and LDS reads; at D = 256 a wave's operands need the whole
-// register file of its SIMD.
+// Workgroup shape per head_dim: eight waves, two per SIMD (256 registers per
+// lane each), so that one wave's MFMA work covers the other's softmax and
+// LDS reads; 32 rows per wave at D = 128, 16 at D = 256 (whose operands are
+// twice as wide).  (Three waves per SIMD at D = 128, 16 rows each, measured
+// slower: each staged K byte then serves half as many rows.)
 template <int D>
 struct PrefillTile;
 template <>
@@ -74,8 +75,8 @@ struct PrefillTile<128> {
 };
 template <>
 struct PrefillTile<256> {
-  static constexpr int PW = 4;
-  static constexpr int TW = 2;
+  static constexpr int PW = 8;
+  static constexpr int TW = 1;
   static constexpr int BN = 32;
 };
 
@@ -714,7 +715,9 @@ bool prefill_geometry(int head_dim, int g, int* hpw, int* tt) {
   else if (head_dim == 256) rows = PrefillTile<256>::PW * 16 * PrefillTile<256>::TW;
   else return false;
   int p = 1;
-  while (p * 2 <= rows / 16 && g % (p * 2) == 0) p *= 2;
+  // (tiles per workgroup) / p whole 16-row tiles per head: a tile never
+  // holds two heads
+  while ((rows / 16) % (p * 2) == 0 && g % (p * 2) == 0) p *= 2;
   *hpw = p;
   *tt = rows / p;
   return true;
