@@ -83,10 +83,10 @@ def kernel_source_hash(op: str = "decode") -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, op: str = "decode"):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{op}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -95,7 +95,7 @@ def stored_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != kernel_source_hash():
+    if fields.get("source_sha256") != kernel_source_hash(op):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -233,7 +233,8 @@ def bench_prefill(args):
                                           if k != "seed"}},
            "flops_per_call": flops,
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None}}
+                        "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                        "traffic": stored_traffic(name, "prefill")}}
     if not args.no_check or args.cpu_seconds > 0:
         import oracle
         rows = out.shape[0] * (out.shape[1] if out.dim() == 4 else 1)
