@@ -415,8 +415,10 @@ def batch_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     shapes; inclusive int32 [B, Sq] bounds).  With packed rows the largest
     query count sizes the grid: pass max_seq_len_q, or it is derived from
     qo_indptr here (a device-to-host read).  Returns out (q's shape, out_dtype
-    or out's dtype or q's).  Enqueued on torch's current stream; never
-    synchronises otherwise.
+    or out's dtype or q's).  Enqueued on torch's current stream as two
+    kernels (the second recomputes, with a rescaling pass, the row groups
+    whose probabilities overflowed their format in the first, which marks
+    them in out); never synchronises otherwise.
     """
     dev = q.device
     _same_device(dev, (("q", q), ("k", k), ("v", v), ("qo_indptr", qo_indptr),
