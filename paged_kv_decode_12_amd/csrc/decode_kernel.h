@@ -93,94 +93,141 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int slot,
   if (d0 == 0) store_coherent(a.ws_lse + (int64_t)slot * RT + r, L > 0.f ? M + log2f(L) : -INFINITY);
 }
 
-// Merges the partial states of the cut unit `unit` (linear blocks [us, ue))
-// for all output items of the lane and writes the final values.  Candidates
-// are taken 64 at a time (lane c works out whether candidate c wrote a
-// partial state); the written ones are read kDepth at a time in block order
-// (every item's loads in flight), raising the running maximum once per
-// group.  rr: the request's query rows; only rows below R = g * lq hold
-// partial states (the rest of a 16-row MFMA tile is padding).
+// Merge of the partial states of one cut unit (virtual start vs, nblk
+// blocks per unit) for all output items of the lane, in steps, so that a
+// wave completing two units has the first loads of both in flight at once:
+// begin() works out the first batch of candidates and issues its loads,
+// finish() consumes them, takes the remaining pieces and writes the final
+// values.  Candidates are taken 64 at a time (lane c works out whether
+// candidate c wrote a partial state); the written ones are read kDepth at a
+// time in block order (every item's loads in flight), raising the running
+// maximum once per group.  Only rows below R = g * lq hold partial states
+// (the rest of a 16-row MFMA tile is padding).
 template <class Eng, int D>
-__device__ __forceinline__ void merge_unit(const DecodeArgs& a, const float* s_sink,
-                                           const Slices& sl_, int unit, int vs, int nblk,
-                                           ReqRows rows, const typename Eng::Lane& ln, int lane) {
-  constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
+struct UnitMerge {
+  static constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   // (deeper batches for 32-float items, 4 or 8 pieces, measured no faster)
-  constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
-  const int per_req = a.Hkv * a.row_tiles;
-  const int b = unit / per_req, uidx = unit - b * per_req;
-  const int kvh = uidx / a.row_tiles, tile = uidx - kvh * a.row_tiles;
-  const int R = a.g * rows.lq;
-  const UnitPieces up = unit_pieces(sl_, vs, a.seg_cost, nblk);
+  static constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
+  int unit, vs, nblk, tile, kvh, R;
+  ReqRows rows;
+  UnitPieces up;
   int rr[NI], dd[NI];
-#pragma unroll
-  for (int it = 0; it < NI; ++it) Eng::item_pos(ln, it, rr[it], dd[it]);
   float Mx[NI], W[NI], acc[NI][8];
-#pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    Mx[it] = -INFINITY;
-    W[it] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[it][e] = 0.f;
-  }
-  for (int c0 = 0; c0 < up.n; c0 += 64) {
-    const int c = c0 + lane;
-    int slot = 0;
-    bool valid = false;
-    if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
-    uint64_t m = __builtin_amdgcn_ballot_w64(valid);
-    // slot of the batch's first written candidate: off entries of a group
-    // read it (finite values) and get weight 0
-    const int sl0 = __builtin_amdgcn_readlane(slot, m ? (int)__builtin_ctzll(m) : 0);
-    while (m) {
-      float lv[kDepth][NI], ov[kDepth][NI][N];
-      bool on[kDepth];
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
-        on[u] = m != 0;
-        const int q = on[u] ? (int)__builtin_ctzll(m) : 0;
-        m = on[u] ? m & (m - 1) : m;
-        const int sl = on[u] ? __builtin_amdgcn_readlane(slot, q) : sl0;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-          // padding rows read row 0's values (loaded by other lanes anyway)
-          const int r = rr[it] < RT && tile * RT + rr[it] < R ? rr[it] : 0;
-          lv[u][it] = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
-#pragma unroll
-          for (int e = 0; e < N; ++e)
-            ov[u][it][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
-        }
+  // the candidate batch being read: candidates c0 .. c0 + 63, the lane's
+  // slot, the written ones not yet loaded (m), the batch's first written slot
+  int c0, slot, sl0;
+  uint64_t m;
+  float lv[kDepth][NI], ov[kDepth][NI][N];
+  bool on[kDepth];
+
+  // Candidates of the batch at c0 and its mask; skips batches with no
+  // written piece.  False when none remain.
+  __device__ __forceinline__ bool open_batch(const Slices& sl_, int lane) {
+    for (; c0 < up.n; c0 += 64) {
+      const int c = c0 + lane;
+      bool valid = false;
+      slot = 0;
+      if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
+      m = __builtin_amdgcn_ballot_w64(valid);
+      if (m) {
+        // off entries of a group read the batch's first written piece
+        // (finite values) with weight 0
+        sl0 = __builtin_amdgcn_readlane(slot, (int)__builtin_ctzll(m));
+        return true;
       }
+    }
+    return false;
+  }
+  // loads of the batch's next kDepth written pieces
+  __device__ __forceinline__ void issue(const DecodeArgs& a, const typename Eng::Lane& ln) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      on[u] = m != 0;
+      const int q = on[u] ? (int)__builtin_ctzll(m) : 0;
+      m = on[u] ? m & (m - 1) : m;
+      const int sl = on[u] ? __builtin_amdgcn_readlane(slot, q) : sl0;
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        float Mn = Mx[it];
+        // padding rows read row 0's values (loaded by other lanes anyway)
+        const int r = rr[it] < RT && tile * RT + rr[it] < R ? rr[it] : 0;
+        lv[u][it] = load_coherent(a.ws_lse + (int64_t)sl * RT + r);
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, on[u] ? lv[u][it] : -INFINITY);
-        const float sc = rescale(Mx[it], Mn);
-        W[it] *= sc;
-#pragma unroll
-        for (int e = 0; e < N; ++e) acc[it][e] *= sc;
-#pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
-          const float wt = on[u] ? rescale(lv[u][it], Mn) : 0.f;
-          W[it] += wt;
-#pragma unroll
-          for (int e = 0; e < N; ++e) acc[it][e] = fmaf(wt, ov[u][it][e], acc[it][e]);
-        }
-        Mx[it] = Mn;
+        for (int e = 0; e < N; ++e)
+          ov[u][it][e] = load_coherent(a.ws_o + (int64_t)sl * RT * D + Eng::pidx(ln, r, e));
       }
     }
   }
-  // acc / W is the merged normalised output; final_value divides by W + sink
+  __device__ __forceinline__ void consume() {
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    const int r = rr[it], row = tile * RT + r;
-    if (!(r < RT && row < R)) continue;
-    const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
-    store_item<D, N>(a, s_sink, ((int64_t)rows.row0 + ti) * a.Hq + qhead, qhead, dd[it],
-                     dd[it] == 0, Mx[it], W[it], acc[it]);
+    for (int it = 0; it < NI; ++it) {
+      float Mn = Mx[it];
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, on[u] ? lv[u][it] : -INFINITY);
+      const float sc = rescale(Mx[it], Mn);
+      W[it] *= sc;
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[it][e] *= sc;
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const float wt = on[u] ? rescale(lv[u][it], Mn) : 0.f;
+        W[it] += wt;
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[it][e] = fmaf(wt, ov[u][it][e], acc[it][e]);
+      }
+      Mx[it] = Mn;
+    }
   }
-}
+  bool first;   // a first batch was issued (some piece was written)
+  // Set-up and the first batch's loads.
+  __device__ __forceinline__ void begin(const DecodeArgs& a, const Slices& sl_, int unit_, int vs_,
+                                        int nblk_, ReqRows rows_, const typename Eng::Lane& ln,
+                                        int lane) {
+    unit = unit_;
+    vs = vs_;
+    nblk = nblk_;
+    rows = rows_;
+    const int per_req = a.Hkv * a.row_tiles;
+    const int b = unit / per_req, uidx = unit - b * per_req;
+    kvh = uidx / a.row_tiles;
+    tile = uidx - kvh * a.row_tiles;
+    R = a.g * rows.lq;
+    up = unit_pieces(sl_, vs, a.seg_cost, nblk);
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      Eng::item_pos(ln, it, rr[it], dd[it]);
+      Mx[it] = -INFINITY;
+      W[it] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[it][e] = 0.f;
+    }
+    c0 = 0;
+    first = open_batch(sl_, lane);
+    if (first) issue(a, ln);
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs& a, const float* s_sink, const Slices& sl_,
+                                         const typename Eng::Lane& ln, int lane) {
+    if (first) {
+      consume();
+      for (;;) {
+        while (m) {   // uniform: the batch's further written pieces, in order
+          issue(a, ln);
+          consume();
+        }
+        c0 += 64;
+        if (!open_batch(sl_, lane)) break;
+      }
+    }
+    // acc / W is the merged normalised output; final_value divides by W + sink
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = rr[it], row = tile * RT + r;
+      if (!(r < RT && row < R)) continue;
+      const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
+      store_item<D, N>(a, s_sink, ((int64_t)rows.row0 + ti) * a.Hq + qhead, qhead, dd[it],
+                       dd[it] == 0, Mx[it], W[it], acc[it]);
+    }
+  }
+};
 
 template <class Eng, int D, bool PAGE_POW2, int PF, int WPE>
 __global__ __launch_bounds__(64 * kSimdsPerCu * WPE) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
@@ -475,14 +522,25 @@ void decode_kernel(const DecodeArgs a) {
         if (pend_unit[k] >= 0 && lane == 0)
           prev[k] = __hip_atomic_fetch_add(&a.counters[pend_unit[k]], pend_n[k], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
+      // the units this wave completes; both merges' first loads go out
+      // together
+      bool done[2];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (pend_unit[k] < 0) continue;
-        if (uniform(prev[k]) + pend_n[k] != pend_nb[k]) continue;
+      for (int k = 0; k < 2; ++k)
+        done[k] = pend_unit[k] >= 0 && uniform(prev[k]) + pend_n[k] == pend_nb[k];
+      if (done[0] || done[1]) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-        const ReqRows rows = req_info(a, s_nlen, s_qo, pend_unit[k] / (a.Hkv * a.row_tiles)).rows;
-        merge_unit<Eng, D>(a, s_sink, sl_, pend_unit[k], pend_vs[k], pend_nb[k], rows, ln, lane);
+        UnitMerge<Eng, D> mg[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (!done[k]) continue;
+          if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
+          const ReqRows rows = req_info(a, s_nlen, s_qo, pend_unit[k] / (a.Hkv * a.row_tiles)).rows;
+          mg[k].begin(a, sl_, pend_unit[k], pend_vs[k], pend_nb[k], rows, ln, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (done[k]) mg[k].finish(a, s_sink, sl_, ln, lane);
       }
     }
   }
