@@ -23,9 +23,10 @@
 // maximum (raised only when a score exceeds it by more than kTau) and
 // rescaled accumulators.
 //
-// Staging.  K and V tiles of BN keys go through a three-stage LDS ring,
+// Staging.  K and V tiles of BN keys go through a four-stage LDS ring,
 // filled with direct global-to-LDS 16-byte loads (no registers) two tiles
-// ahead of their use.  A key row of D elements is stored as 16-byte chunks
+// ahead of their use (the fourth stage keeps a tile's V for the products
+// the FAST loop defers past the next tile's barrier).  A key row of D elements is stored as 16-byte chunks
 // whose 32-byte slot index is XORed with the key index mod 8, so the reads
 // below touch spread banks.
 //
@@ -36,6 +37,8 @@
 //    the scores of row j for keys 4q + i and 16 + 4q + i, i = 0..3;
 //  * masks by select (only in chunks some row sees in part); probabilities
 //    2^(score - reference) in base 2; row sums by an MFMA against ones;
+//    in the FAST loop a chunk's products P . V run beside the next chunk's
+//    softmax (software pipelining within the wave);
 //  * O += P . V with the same 16x16x32 instruction: the lane's eight
 //    probabilities are the A operand of row j for the key order
 //    (4q .. 4q + 3, 16 + 4q .. 16 + 4q + 3), and the B operand for output
@@ -58,7 +61,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kStages = 3;   // K/V tiles in the LDS ring
+constexpr int kStages = 4;   // K/V tiles in the LDS ring
 
 // Workgroup shape per head_dim: eight waves, two per SIMD (256 registers per
 // lane each), so that one wave's MFMA work covers the other's softmax and
@@ -233,12 +236,13 @@ __device__ __forceinline__ bool marked(const PrefillArgs& a, int64_t off) {
 // The workgroup's whole computation of one item, in the FAST mode (SAFE =
 // false: returns true when the pass overflowed; it then stores only the
 // item's marker) or the SAFE mode (SAFE = true: the rescaling passes, one
-// tile and half of the output dims at a time).  st0 .. st2: the LDS ring's
+// tile and half of the output dims at a time).  st0 .. st3: the LDS ring's
 // stages (a K tile, then a V tile); s_range, s_flag: LDS scratch of the
 // workgroup.
 template <int D, bool BF16, bool SAFE>
 __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const PrefillItem& it,
                                              uint16_t* st0, uint16_t* st1, uint16_t* st2,
+                                             uint16_t* st3,
                                              int* s_range, int* s_flag) {
   using Mf = Mfma<BF16>;
   using F = Fmt<BF16>;
@@ -253,7 +257,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
   constexpr int LPT = TILE / 8 / 64 / kPW;   // wave-wide loads per wave, tile and tensor
   static_assert(LPT >= 1 && TILE / 8 == LPT * 64 * kPW, "tile loads must divide over the waves");
   static_assert(2 * LPT < 16, "outstanding loads must fit the vmcnt field");
-  static_assert(kStages == 3, "three ring stages");
+  static_assert(kStages == 4, "four ring stages");
 
   const int b = it.b, kvh = it.kvh, hg = it.hg;
   const int q0 = it.q0, sq = it.sq, k0 = it.k0, sk = it.sk;
@@ -303,7 +307,8 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
   // (the direct loads' M0 adds a constant per load)
   const uint32_t lds_st[kStages] = {(uint32_t)uniform(lds_address(st0) + wave * 1024),
                                     (uint32_t)uniform(lds_address(st1) + wave * 1024),
-                                    (uint32_t)uniform(lds_address(st2) + wave * 1024)};
+                                    (uint32_t)uniform(lds_address(st2) + wave * 1024),
+                                    (uint32_t)uniform(lds_address(st3) + wave * 1024)};
   // Direct loads of a tile: wave-wide load u of the wave fills key rows
   // (u * kPW + wave) * RPI .. + RPI - 1 of the tile (1 KB of LDS,
   // lane-major); lane l loads chunk swz(row, l % CPR) of its row.  The
@@ -562,13 +567,101 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
       }
     };
 
+    // FAST: chunks software-pipelined within the wave.  Chunk c's scores
+    // are taken first; then chunk c - 1's products P . V (pending) run in
+    // the same stretch as chunk c's probabilities, so that each wave has
+    // MFMA and VALU work in flight together.  No branch touches the
+    // accumulators (a join between arms that do and do not update them
+    // makes the compiler copy them): every chunk of the workgroup's tiles is
+    // taken, those this wave does not see fully masked, and the first
+    // chunk's pending products are zero probabilities against that chunk's
+    // own (loaded) V.  A pending chunk's V tile may be read after the
+    // barrier that opens the next tile: four ring stages keep it from being
+    // refilled until then.
+    u32x4 pend_pa[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pend_pa[t] = u32x4{0u, 0u, 0u, 0u};
+    const uint16_t* pend_sV = st0 + TILE;
+    int pend_kc = 0;
+    auto fast_scores = [&](const uint16_t* sK, int kc, float (&x)[NT][8]) {
+      u32x4 ka[2][NC];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = kc * 32 + 16 * h + lj;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          ka[h][c] = *reinterpret_cast<const u32x4*>(sK + r * D + swz(r, 4 * c + lq) * 8);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          s0 = Mf::qk(ka[0][c], qv[t][c], s0);
+          s1 = Mf::qk(ka[1][c], qv[t][c], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[t][i] = s0[i];
+          x[t][4 + i] = s1[i];
+        }
+      }
+    };
+    auto fast_mask = [&](int j0, float (&x)[NT][8]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = j0 + (e < 4 ? 4 * lq + e : 16 + 4 * lq + e - 4);
+          x[t][e] = (key >= lo_t[T0 + t] && key <= hi_t[T0 + t]) ? x[t][e] : -INFINITY;
+        }
+    };
+    auto fast_probs = [&](const float (&x)[NT][8], u32x4 (&pa)[NT]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float nm = -fmaxf(m_t[t], -FLT_MAX);
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[t][e], sc, nm));
+        pa[t] = u32x4{F::pack2(p[0], p[1]), F::pack2(p[2], p[3]), F::pack2(p[4], p[5]),
+                      F::pack2(p[6], p[7])};
+      }
+    };
+    auto fast_pv = [&](const uint16_t* sV, int kc, const u32x4 (&pa)[NT]) {   // sV: a V tile
+      auto vread = [&](int u) {
+        u32x4 vb;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = kc * 32 + 16 * h + 4 * lq + (lj >> 2);
+          const int cc = 2 * u + ((lj & 3) >> 1);
+          const u32x2 y = read_tr(sV + r * D + swz(r, cc) * 8 + (lj & 1) * 4);
+          vb[2 * h] = y[0];
+          vb[2 * h + 1] = y[1];
+        }
+        return vb;
+      };
+      constexpr int VPRE = 1;
+      u32x4 vb[VPRE];
+#pragma unroll
+      for (int u = 0; u < VPRE; ++u) vb[u] = vread(U0 + u);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) lsum[t] = Mf::qk(pa[t], ones, lsum[t]);
+#pragma unroll
+      for (int u = 0; u < NUP; ++u) {
+        const u32x4 v = vb[u % VPRE];
+        if (u + VPRE < NUP) vb[u % VPRE] = vread(U0 + u + VPRE);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][u] = Mf::qk(pa[t], v, acc[t][u]);
+      }
+    };
+
     lds_barrier();   // every wave is past its reads of an earlier pass's ring
     if (ntiles > 0) issue(0, lds_st[0]);
     if (ntiles > 1) issue(1, lds_st[1]);
     if (ntiles > 1) wait_vmcnt<2 * LPT>();
     else wait_vmcnt<0>();
     lds_barrier();
-    // step `it` reads stage it % 3 and fills stage (it + 2) % 3
+    // step `it` reads stage it % 4 and fills stage (it + 2) % 4
     auto step = [&](int it, const uint16_t* stage, uint32_t next) {
       if (it + 2 < ntiles) issue(it + 2, next);
       const uint16_t* sK = stage;
@@ -577,9 +670,27 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
 #pragma unroll
       for (int kc = 0; kc < BN / 32; ++kc) {
         const int j0 = kb + kc * 32;
-        if (j0 > whi || j0 + 31 < wlo) continue;   // no row of this wave sees these keys
         // masked unless every live row sees all of them
-        chunk(!(j0 >= wmaxlo && j0 + 31 <= wminhi), sK, sV, kc, j0);
+        const bool masked = !(j0 >= wmaxlo && j0 + 31 <= wminhi);
+        if constexpr (SAFE) {
+          if (j0 > whi || j0 + 31 < wlo) continue;   // no row of this wave sees these keys
+          chunk(masked, sK, sV, kc, j0);
+        } else {
+          float x[NT][8];
+          fast_scores(sK, kc, x);
+          if (masked) fast_mask(j0, x);   // uniform
+          // the previous chunk's products beside this chunk's softmax
+          u32x4 pa[NT];
+          fast_pv(pend_sV, pend_kc, pend_pa);
+          fast_probs(x, pa);
+          // computed here, beside the products (not sunk to their use)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(pa[t]));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) pend_pa[t] = pa[t];
+          pend_sV = sV;
+          pend_kc = kc;
+        }
       }
       if (it + 1 < ntiles) {
         // the next tile's loads have landed (the one after may still be in flight)
@@ -588,11 +699,14 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
         lds_barrier();
       }
     };
-    for (int it = 0; it < ntiles; it += 3) {
+    for (int it = 0; it < ntiles; it += 4) {
       step(it, st0, lds_st[2]);
-      if (it + 1 < ntiles) step(it + 1, st1, lds_st[0]);
-      if (it + 2 < ntiles) step(it + 2, st2, lds_st[1]);
+      if (it + 1 < ntiles) step(it + 1, st1, lds_st[3]);
+      if (it + 2 < ntiles) step(it + 2, st2, lds_st[0]);
+      if (it + 3 < ntiles) step(it + 3, st3, lds_st[1]);
     }
+    if constexpr (!SAFE)
+      if (ntiles > 0) fast_pv(pend_sV, pend_kc, pend_pa);   // the last chunk's products
 
     if constexpr (!SAFE) {
       // A probability beyond the range of P's format (or of the fp32 sums)
@@ -664,12 +778,13 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
 template <int D, bool BF16>
 __global__ __launch_bounds__(64 * PrefillTile<D>::PW, 1) void prefill_kernel(const PrefillArgs a) {
   constexpr int TILE = PrefillGeom<D>::TILE;
-  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE],
+      st3[2 * TILE];
   __shared__ int s_range[2];
   __shared__ int s_flag;   // the pass overflowed (see attend)
   PrefillItem it;
   if (!it.init(a, (int)blockIdx.x)) return;   // uniform over the workgroup
-  prefill_body<D, BF16, false>(a, it, st0, st1, st2, s_range, &s_flag);
+  prefill_body<D, BF16, false>(a, it, st0, st1, st2, st3, s_range, &s_flag);
 }
 
 // SAFE passes, launched after the FAST kernel on the same stream with at
@@ -682,7 +797,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(64 * PrefillTile<D>::PW, 1) void prefill_safe_kernel(const PrefillArgs a) {
   constexpr int TILE = PrefillGeom<D>::TILE;
   constexpr int NT = 64 * PrefillTile<D>::PW;   // items checked per pass
-  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE],
+      st3[2 * TILE];
   __shared__ int s_range[2];
   __shared__ int s_flag;
   __shared__ int s_list[NT];
@@ -701,7 +817,7 @@ __global__ __launch_bounds__(64 * PrefillTile<D>::PW, 1) void prefill_safe_kerne
     for (int k = 0; k < n; ++k) {
       PrefillItem m;
       m.init(a, uniform(s_list[k]));   // true: it was listed
-      prefill_body<D, BF16, true>(a, m, st0, st1, st2, s_range, &s_flag);
+      prefill_body<D, BF16, true>(a, m, st0, st1, st2, st3, s_range, &s_flag);
     }
     __syncthreads();   // s_n and s_list are reused by the next pass
   }
