@@ -348,6 +348,14 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
     }
   };
 
+  // FAST (one item per workgroup, the ring not yet used): the first two
+  // tiles' loads go out before Q and the reference scores are read, so that
+  // those latencies overlap (the Q wait below then covers them too)
+  if constexpr (!SAFE) {
+    if (ntiles > 0) issue(0, lds_st[0]);
+    if (ntiles > 1) issue(1, lds_st[1]);
+  }
+
   // scores are taken in base 2 with a positive factor: a negative sm_scale
   // is moved onto Q's sign bits (exact)
   const float sc = fabsf(a.scale_log2);
@@ -418,8 +426,8 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
   wmaxlo = uniform(wave_maxi(wmaxlo));
   wminhi = uniform(wave_min(wminhi));
 
-  // Q rows are in registers before any tile load is outstanding: the loop
-  // below waits only for its own tile loads
+  // Q rows (and, in the FAST mode, the first two tiles) have landed before
+  // the loop: it waits only for the tile loads it issues itself
   wait_vmcnt<0>();
 
   // B operand of ones: P . 1 gives the row sums of the probabilities as
@@ -656,8 +664,10 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
     };
 
     lds_barrier();   // every wave is past its reads of an earlier pass's ring
-    if (ntiles > 0) issue(0, lds_st[0]);
-    if (ntiles > 1) issue(1, lds_st[1]);
+    if constexpr (SAFE) {
+      if (ntiles > 0) issue(0, lds_st[0]);
+      if (ntiles > 1) issue(1, lds_st[1]);
+    }
     if (ntiles > 1) wait_vmcnt<2 * LPT>();
     else wait_vmcnt<0>();
     lds_barrier();
