@@ -54,6 +54,27 @@ bool contiguous(const pkvd_tensor* t) {
   return true;
 }
 
+namespace {
+// [*lo, *hi): the bytes a tensor's elements may occupy; false when empty.
+bool byte_span(const pkvd_tensor* t, uintptr_t* lo, uintptr_t* hi) {
+  const uintptr_t elt = t->dtype == PKVD_F32 || t->dtype == PKVD_I32 ? 4 : 2;
+  uintptr_t last = 0;   // offset of the last element, in elements
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] <= 0) return false;
+    last += (uintptr_t)(t->shape[i] - 1) * (uintptr_t)(t->strides[i] < 0 ? 0 : t->strides[i]);
+  }
+  *lo = reinterpret_cast<uintptr_t>(t->data);
+  *hi = *lo + (last + 1) * elt;
+  return true;
+}
+}  // namespace
+
+bool overlaps(const pkvd_tensor* a, const pkvd_tensor* b) {
+  uintptr_t a0, a1, b0, b1;
+  if (!byte_span(a, &a0, &a1) || !byte_span(b, &b0, &b1)) return false;
+  return a0 < b1 && b0 < a1;
+}
+
 // CUs of the current device (cached per device); an MI355X (256 CUs) is
 // assumed when no device answers.
 int device_cus() {

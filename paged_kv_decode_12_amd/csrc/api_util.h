@@ -18,6 +18,10 @@ bool aligned16(const void* p);
 bool contiguous(const pkvd_tensor* t);
 // CUs of the current device (cached per device; 256 when no device answers).
 int device_cus();
+// Whether the byte ranges two tensors' elements may occupy (from shape,
+// strides and element size; negative strides are not accepted anywhere)
+// intersect.  Empty tensors overlap nothing.
+bool overlaps(const pkvd_tensor* a, const pkvd_tensor* b);
 
 }  // namespace api
 }  // namespace pkvd

@@ -117,6 +117,10 @@ extern "C" int pkvd_prefill(const pkvd_prefill_args* x, void* stream) {
   if (out->dtype != PKVD_BF16 && out->dtype != PKVD_F16 && out->dtype != PKVD_F32)
     return fail(PKVD_ERR_INVALID_ARG, "out must be bf16, fp16 or fp32");
   if (!aligned16(out->data)) return fail(PKVD_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  // out is written while other workgroups still read q, k and v (and the
+  // rescaling kernel reads q again after the first kernel's stores)
+  if (overlaps(out, q) || overlaps(out, k) || overlaps(out, v))
+    return fail(PKVD_ERR_INVALID_ARG, "out must not overlap q, k or v");
   // the kernel's per-lane offsets within a tile of keys are 32-bit
   if (k_sr > (INT32_MAX - 8 * D) / 64 || v_sr > (INT32_MAX - 8 * D) / 64)
     return fail(PKVD_ERR_UNSUPPORTED, "k/v row strides exceed the built index range");

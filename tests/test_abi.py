@@ -430,8 +430,10 @@ def test_static_entry_point_rejects_plans_beyond_its_workspace():
 # ----------------------------------------------------------------------------
 # context attention (pkvd_prefill): argument checks before any launch
 # ----------------------------------------------------------------------------
-def prefill_call(inp, **over):
-    """pkvd_prefill over fake, aligned addresses (only rejected calls)."""
+def prefill_call(inp, alias=None, **over):
+    """pkvd_prefill over fake, aligned addresses (only rejected calls).
+    alias = (name, other, byte_offset) places tensor `name` at `other`'s
+    address plus the offset."""
     d = dict(inp)
     d.update(over)
     base = 1 << 32
@@ -448,6 +450,9 @@ def prefill_call(inp, **over):
         dd.data = base + (i << 24)
         keep.append(dd)
         setattr(x, name, ctypes.pointer(dd))
+    if alias is not None:
+        name, other, off = alias
+        getattr(x, name).contents.data = getattr(x, other).contents.data + off
     x.max_seq_len_q = int(d.get("max_seq_len_q", 0) or 0)
     x.mask = int(d.get("mask", 0))
     x.window_left = int(d.get("window_left", -1))
@@ -520,6 +525,17 @@ def test_prefill_invalid_arguments(name, make, mut):
     st = prefill_call(inp, **over)
     assert st == 1, (name, st, pk._lib.pkvd_last_error())
     assert pk._lib.pkvd_last_error()
+
+
+@pytest.mark.parametrize("other,offset", [("q", 0), ("q", 4096), ("k", 0), ("v", 256)])
+def test_prefill_out_overlapping_inputs(other, offset):
+    """out may not share bytes with q, k or v: the first kernel writes it
+    (including the overflow marker) while q, k and v are still read, and the
+    rescaling kernel reads q again."""
+    inp = prefill_fixed()
+    inp["out"] = torch.empty(inp["q"].shape, dtype=torch.bfloat16)
+    assert prefill_call(inp, alias=("out", other, offset)) == 1
+    assert b"overlap" in pk._lib.pkvd_last_error()
 
 
 @pytest.mark.parametrize("D", [64, 96])
