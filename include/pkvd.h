@@ -355,9 +355,12 @@ void pkvd_reload_tuning(void);
  *            device tensors, 0 <= starts <= ends < Sk (clamped on the device).
  *   sm_scale, output_scale  finite.
  *   out      caller-owned, q's shape, contiguous, 16-byte aligned; bf16,
- *            fp16 or fp32 (out_dtype).
- * Supported: D in {128, 256}.  Work is only enqueued on `stream`; nothing is
- * allocated and nothing is read back.  Errors as for pkvd_decode.
+ *            fp16 or fp32 (out_dtype); shares no byte with q, k or v.
+ * Supported: D in {128, 256}.  Work is only enqueued on `stream` (two
+ * kernels: the second recomputes, with a rescaling pass, the row groups whose
+ * probabilities overflowed their format in the first, which marks them in
+ * `out`; `out` is complete once both have run); nothing is allocated and
+ * nothing is read back.  Errors as for pkvd_decode.
  */
 typedef struct {
   const pkvd_tensor* q;
