@@ -16,8 +16,8 @@ Also reported:
                 8 TB/s HBM3E peak;
   cpu_baseline  the fp64 CPU oracle (test infrastructure) timed on the host
                 cores on the same workload, as a reported baseline only;
-  cold          per-call time with the 256 MB Infinity Cache and L2 flushed
-                before every call (outside the events).
+  cold          per-call time with the 256 MB Infinity Cache and L2 flushed by a
+                1 GiB read before every call (outside the events).
 
 roofline.traffic is the HBM bytes per launch that rocprofv3's FETCH_SIZE and
 WRITE_SIZE counters gave for this workload, scaled by what the same counters
@@ -732,12 +732,14 @@ def main():
     torch.cuda.synchronize()
     per_call_us = [a.elapsed_time(b) * 1e3 for a, b in per_call_us]
 
-    # cold calls: flush the MALL/L2 with a 1 GiB write between calls, outside the events
+    # cold calls: evict the MALL/L2 by reading 1 GiB between calls, outside the
+    # events (a read leaves the caches clean; a write flush would leave dirty
+    # lines whose write-back then overlaps the timed call)
     cold_us = []
     if args.cold_iters > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_iters):
-            flush.fill_(1.0)
+            flush.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             step()
