@@ -440,10 +440,10 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
   // above) for the whole pass, so the accumulators are only ever touched by
   // MFMAs and no chunk takes row maxima; probabilities of keys scoring
   // above the reference may exceed 1 by as much as P's format holds.  A row
-  // whose probabilities went beyond that marks the pass as overflowed and
-  // the workgroup runs it again in the SAFE mode: a lazily raised maximum
-  // (by more than kTau at a time) with the accumulators rescaled.  Returns
-  // true when a FAST pass overflowed (nothing written).
+  // whose probabilities went beyond that marks the pass as overflowed: the
+  // workgroup stores only its item's marker, and the SAFE kernel runs the
+  // item again with a lazily raised maximum (by more than kTau at a time)
+  // and rescaled accumulators.  Returns true when a FAST pass overflowed.
   auto attend = [&](auto safe_tag, auto t0_tag, auto nt_tag, auto u0_tag, auto nu_tag) -> bool {
     static_assert(decltype(safe_tag)::value == SAFE, "one mode per body");
     constexpr int T0 = decltype(t0_tag)::value, NT = decltype(nt_tag)::value;
@@ -476,105 +476,12 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
         for (int c = 0; c < NC; ++c) qv[t][c] = qf[T0 + t][c];
     }
 
-    // 32 keys from j0 (tile rows kc * 32 ..) of the stage at sK / sV.
-    // masked (uniform): some row sees only part of them.  One body for both
-    // cases, so that the accumulators keep their registers from chunk to
-    // chunk (two bodies had them copied at every join).
-    auto chunk = [&](bool masked, const uint16_t* sK, const uint16_t* sV, int kc, int j0) {
-      u32x4 ka[2][NC];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = kc * 32 + 16 * h + lj;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          ka[h][c] = *reinterpret_cast<const u32x4*>(sK + r * D + swz(r, 4 * c + lq) * 8);
-      }
-      // V operand of output tile u: keys (4q .. 4q + 3, 16 + 4q .. + 3), column j
-      auto vread = [&](int u) {
-        u32x4 vb;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = kc * 32 + 16 * h + 4 * lq + (lj >> 2);
-          const int cc = 2 * u + ((lj & 3) >> 1);
-          const u32x2 y = read_tr(sV + r * D + swz(r, cc) * 8 + (lj & 1) * 4);
-          vb[2 * h] = y[0];
-          vb[2 * h + 1] = y[1];
-        }
-        return vb;
-      };
-      constexpr int VPRE = 2;   // V operands read ahead of P . V
-      u32x4 vb[VPRE];
-#pragma unroll
-      for (int u = 0; u < VPRE; ++u) vb[u] = vread(U0 + u);
-
-      // phase 1, tile by tile (K operands shared): scores, row maxima
-      // (SAFE, or FAST while some row has none), probabilities
-      // 2^(sc x - m) packed as the A operand of P . V (a row that has seen
-      // no key has m = -inf and only -inf scores: p = 0), and the row sums
-      // P . 1
-      u32x4 pa[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          s0 = Mf::qk(ka[0][c], qv[t][c], s0);
-          s1 = Mf::qk(ka[1][c], qv[t][c], s1);
-        }
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = s0[i];
-          x[4 + i] = s1[i];
-        }
-        if (masked) {   // uniform
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = j0 + (e < 4 ? 4 * lq + e : 16 + 4 * lq + e - 4);
-            x[e] = (key >= lo_t[T0 + t] && key <= hi_t[T0 + t]) ? x[e] : -INFINITY;
-          }
-        }
-        if constexpr (SAFE) {
-          const float lmax = sc * fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          if (wave_any(lmax > m_t[t] + kTau)) {
-            // the chunk max of row j over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
-            const Pair p16 = lane_pair<16>(lmax);
-            const Pair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
-            const float mn = fmaxf(m_t[t], fmaxf(p32.lo, p32.hi));
-            const float alpha = rescale(m_t[t], mn);
-            m_t[t] = mn;
-            // accumulator rows are 4q + i: each row's factor from lane 4q + i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float ai = __builtin_bit_cast(
-                  float,
-                  __builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __builtin_bit_cast(int, alpha)));
-              lsum[t][i] *= ai;
-#pragma unroll
-              for (int u = 0; u < NUP; ++u) acc[t][u][i] *= ai;
-            }
-          }
-        }
-        const float nm = -fmaxf(m_t[t], -FLT_MAX);
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], sc, nm));
-        pa[t] = u32x4{F::pack2(p[0], p[1]), F::pack2(p[2], p[3]), F::pack2(p[4], p[5]),
-                      F::pack2(p[6], p[7])};
-        lsum[t] = Mf::qk(pa[t], ones, lsum[t]);
-      }
-      // phase 2: O += P . V, one 16-dim output tile at a time (V operands
-      // shared by the tiles)
-#pragma unroll
-      for (int u = 0; u < NUP; ++u) {
-        const u32x4 v = vb[u % VPRE];
-        if (u + VPRE < NUP) vb[u % VPRE] = vread(U0 + u + VPRE);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t][u] = Mf::qk(pa[t], v, acc[t][u]);
-      }
-    };
-
+    // A chunk is 32 keys from j0 (tile rows kc * 32 ..) of a stage's K and V
+    // tiles; masked (uniform): some row sees only part of them.  The steps:
+    // scores, the mask (by select), probabilities 2^(sc x - m) packed as the
+    // A operand of P . V (a row that has seen no key has m = -inf and only
+    // -inf scores: p = 0), and the products P . 1 (row sums) and P . V.
+    //
     // FAST: chunks software-pipelined within the wave.  Chunk c's scores
     // are taken first; then chunk c - 1's products P . V (pending) run in
     // the same stretch as chunk c's probabilities, so that each wave has
@@ -591,7 +498,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
     for (int t = 0; t < NT; ++t) pend_pa[t] = u32x4{0u, 0u, 0u, 0u};
     const uint16_t* pend_sV = st0 + TILE;
     int pend_kc = 0;
-    auto fast_scores = [&](const uint16_t* sK, int kc, float (&x)[NT][8]) {
+    auto chunk_scores = [&](const uint16_t* sK, int kc, float (&x)[NT][8]) {
       u32x4 ka[2][NC];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -615,7 +522,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
         }
       }
     };
-    auto fast_mask = [&](int j0, float (&x)[NT][8]) {
+    auto chunk_mask = [&](int j0, float (&x)[NT][8]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -624,7 +531,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
           x[t][e] = (key >= lo_t[T0 + t] && key <= hi_t[T0 + t]) ? x[t][e] : -INFINITY;
         }
     };
-    auto fast_probs = [&](const float (&x)[NT][8], u32x4 (&pa)[NT]) {
+    auto chunk_probs = [&](const float (&x)[NT][8], u32x4 (&pa)[NT]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float nm = -fmaxf(m_t[t], -FLT_MAX);
@@ -635,7 +542,35 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
                       F::pack2(p[6], p[7])};
       }
     };
-    auto fast_pv = [&](const uint16_t* sV, int kc, const u32x4 (&pa)[NT]) {   // sV: a V tile
+    // SAFE: the running maximum of each row, raised only when a score
+    // exceeds it by more than kTau (base 2), the accumulators rescaled then
+    auto safe_rescale = [&](const float (&x)[NT][8]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float lmax = sc * fmaxf(fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])),
+                                      fmaxf(fmaxf(x[t][4], x[t][5]), fmaxf(x[t][6], x[t][7])));
+        if (wave_any(lmax > m_t[t] + kTau)) {
+          // the chunk max of row j over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
+          const Pair p16 = lane_pair<16>(lmax);
+          const Pair p32 = lane_pair<32>(fmaxf(p16.lo, p16.hi));
+          const float mn = fmaxf(m_t[t], fmaxf(p32.lo, p32.hi));
+          const float alpha = rescale(m_t[t], mn);
+          m_t[t] = mn;
+          // accumulator rows are 4q + i: each row's factor from lane 4q + i
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __builtin_bit_cast(
+                float,
+                __builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __builtin_bit_cast(int, alpha)));
+            lsum[t][i] *= ai;
+#pragma unroll
+            for (int u = 0; u < NUP; ++u) acc[t][u][i] *= ai;
+          }
+        }
+      }
+    };
+    auto chunk_products = [&](const uint16_t* sV, int kc, const u32x4 (&pa)[NT]) {   // sV: a V tile
+      // V operand of output tile u: keys (4q .. 4q + 3, 16 + 4q .. + 3), column j
       auto vread = [&](int u) {
         u32x4 vb;
 #pragma unroll
@@ -648,7 +583,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
         }
         return vb;
       };
-      constexpr int VPRE = 1;
+      constexpr int VPRE = 1;   // V operands read one product ahead
       u32x4 vb[VPRE];
 #pragma unroll
       for (int u = 0; u < VPRE; ++u) vb[u] = vread(U0 + u);
@@ -684,15 +619,21 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
         const bool masked = !(j0 >= wmaxlo && j0 + 31 <= wminhi);
         if constexpr (SAFE) {
           if (j0 > whi || j0 + 31 < wlo) continue;   // no row of this wave sees these keys
-          chunk(masked, sK, sV, kc, j0);
+          float x[NT][8];
+          chunk_scores(sK, kc, x);
+          if (masked) chunk_mask(j0, x);   // uniform
+          safe_rescale(x);
+          u32x4 pa[NT];
+          chunk_probs(x, pa);
+          chunk_products(sV, kc, pa);
         } else {
           float x[NT][8];
-          fast_scores(sK, kc, x);
-          if (masked) fast_mask(j0, x);   // uniform
+          chunk_scores(sK, kc, x);
+          if (masked) chunk_mask(j0, x);   // uniform
           // the previous chunk's products beside this chunk's softmax
           u32x4 pa[NT];
-          fast_pv(pend_sV, pend_kc, pend_pa);
-          fast_probs(x, pa);
+          chunk_products(pend_sV, pend_kc, pend_pa);
+          chunk_probs(x, pa);
           // computed here, beside the products (not sunk to their use)
 #pragma unroll
           for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(pa[t]));
@@ -716,7 +657,7 @@ __device__ __forceinline__ bool prefill_body(const PrefillArgs& a, const Prefill
       if (it + 3 < ntiles) step(it + 3, st3, lds_st[1]);
     }
     if constexpr (!SAFE)
-      if (ntiles > 0) fast_pv(pend_sV, pend_kc, pend_pa);   // the last chunk's products
+      if (ntiles > 0) chunk_products(pend_sV, pend_kc, pend_pa);   // the last chunk's products
 
     if constexpr (!SAFE) {
       // A probability beyond the range of P's format (or of the fp32 sums)
