@@ -591,6 +591,7 @@ void fill_args(const pkvd_decode_args* x, const Shapes& s, const Plan& p, pkvd::
   a.unit_mode = p.unit_mode;
   a.merge_kernel = p.merge_kernel;
   for (int r = 0; r < 4; ++r) a.slot_w[r] = p.slot_w[r];
+  pkvd::dev::set_full_grid(a);
   *out = a;
 }
 
@@ -865,8 +866,17 @@ int pkvd_schedule_stats(const pkvd_decode_args* args, const int32_t* seq_lens,
   pref[B] = T;
   vpref[B] = TV;
   if (TV >= INT32_MAX) return fail(PKVD_ERR_UNSUPPORTED, "block space beyond int32");
-  const int NW = wave_count(a, (int)T);
-  const Slices sl = make_slices(a, (int)TV, NW);
+  int NW;
+  const Slices sl = grid_slices(a, (int)TV, (int)T, NW);
+  // the full grid's host-set constants give the same slices as the
+  // general path
+  const int NWg = wave_count(a, (int)T);
+  const Slices slg = make_slices(a, (int)TV, NWg);
+  int64_t errors = 0;
+  if (NWg != NW) ++errors;
+  else
+    for (int w = 0; w <= NW; ++w)
+      if (slice_begin(sl, w) != slice_begin(slg, w)) ++errors;
   // the real block at virtual block v: the request holding v is the last one
   // whose virtual prefix is <= v (as the kernel's search finds it)
   auto real_at = [&](int64_t v) -> int64_t {
@@ -875,7 +885,6 @@ int pkvd_schedule_stats(const pkvd_decode_args* args, const int32_t* seq_lens,
     return real_block(a, (int)pref[b], (int)vpref[b], nblk[b], (int)v);
   };
   std::vector<int64_t> lo(NW + 1);
-  int64_t errors = 0;
   for (int w = 0; w <= NW; ++w) lo[w] = T ? real_at(slice_begin(sl, w)) : 0;
   if (lo[0] != 0 || lo[NW] != T) ++errors;
   for (int w = 0; w < NW; ++w)

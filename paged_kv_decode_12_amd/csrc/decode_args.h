@@ -62,6 +62,12 @@ struct DecodeArgs {
   int32_t seg_cost;                // virtual blocks ahead of each unit in the sliced space
   int32_t unit_mode;               // 1: slice bounds snap to unit starts (every unit whole)
   int32_t slot_w[4];               // slice weight of the waves at position 0, 1, 2, >= 3 on their SIMD
+  // The full grid (NW = num_waves, which a block space of T >= full_T real
+  // blocks always gets): the parts of its slicing that do not depend on the
+  // lengths, set by the host (schedule.h: grid_slices)
+  int32_t full_T;
+  int32_t full_per, full_uniform;
+  int64_t full_sp, full_s;
 #ifdef PKVD_TRACE
   uint64_t* trace;                 // instrumented builds only: [waves][16] timestamps
 #endif

@@ -269,14 +269,15 @@ void decode_kernel(const DecodeArgs a) {
       a.ws_pref[i] = s_pref[i];
       a.ws_vpref[i] = s_vpref[i];
     }
-  const int NW = wave_count(a, T);
-  // Each workgroup takes a run of consecutive slices (its CU then streams
-  // neighbouring kv heads of the same requests): ceil(NW / groups) waves of
-  // each group are active, so a short grid still spreads over all groups.
-  const int active = (NW + a.groups - 1) / a.groups;
-  const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
   // slices of the virtual block space, mapped back to real blocks
-  const Slices sl_ = make_slices(a, pf.TV, NW);
+  int NW;
+  const Slices sl_ = grid_slices(a, pf.TV, T, NW);
+  // Each workgroup takes a run of consecutive slices (its CU then streams
+  // neighbouring kv heads of the same requests): PER = ceil(NW / groups)
+  // waves of each group are active, so a short grid still spreads over all
+  // groups.
+  const int active = sl_.PER;
+  const int gw = wave < active ? (int)blockIdx.x * active + wave : NW;
 #ifdef PKVD_TRACE
   const uint64_t t_slices = __builtin_amdgcn_s_memrealtime();
 #endif
@@ -365,8 +366,8 @@ void decode_kernel(const DecodeArgs a) {
   // page ids of a chunk's columns (issued early; clamped into the pool where used)
   auto fetch_pages = [&](const Chunk& c) {
     PageWindow w;
-    w.col0 = c.kb / a.ps;
-    const int ncol = (c.ke - 1) / a.ps - w.col0 + 1;
+    w.col0 = PAGE_POW2 ? c.kb >> ps_shift : c.kb / a.ps;
+    const int ncol = (PAGE_POW2 ? (c.ke - 1) >> ps_shift : (c.ke - 1) / a.ps) - w.col0 + 1;
     const int32_t* row = a.bt + (int64_t)c.sg.b * a.bt_sr + w.col0;
     const int p0 = row[min(lane, ncol - 1)];
     const int p1 = row[min(64 + lane, ncol - 1)];
@@ -603,8 +604,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (u.nblk == 0) return;
   // the unit's place among its request's units (kv head major, then tiles)
   const int ub = a.qo ? kvh * tiles_of(a, rows.lq) + tile : uidx;
-  const int NW = wave_count(a, T);
-  const Slices sl_ = make_slices(a, TV, NW);
+  int NW;
+  const Slices sl_ = grid_slices(a, TV, T, NW);
   const int64_t us = pref_b + (int64_t)ub * u.nblk, ue = us + u.nblk;
   const int64_t vs = vpref_b + (int64_t)ub * unit_vspan(a, u.nblk);
   if (ue > T) return;

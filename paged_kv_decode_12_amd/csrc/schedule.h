@@ -115,7 +115,6 @@ struct Slices {
   int W[4];
   int64_t SP;    // total weight of one group's PER waves
   int64_t S;     // total weight of the NW waves
-  int n_min;     // blocks of the shortest slice (a lower bound)
   int qT, rT;    // T = qT NW + rT (equal weights)
 };
 // Total weight of the first m waves of a group (0 <= m <= PER).
@@ -141,21 +140,18 @@ __host__ __device__ __forceinline__ Slices make_slices(const DecodeArgs& a, int 
   s.NW = NW;
   const int groups = a.groups > 0 ? a.groups : 1;
   s.PER = (NW + groups - 1) / groups;
-  int wmin = 1 << 30;
   s.uniform = 1;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     s.W[r] = a.slot_w[r];
     if (r * kSimdsPerCu < s.PER) {
       if (s.W[r] != s.W[0]) s.uniform = 0;
-      if (s.W[r] < wmin) wmin = s.W[r];
     }
   }
   s.SP = group_weight(s, s.PER);
   s.S = weight_before(s, NW);
   s.qT = T / NW;
   s.rT = T - s.qT * NW;
-  s.n_min = s.uniform ? s.qT : (int)qdiv((int64_t)T * wmin, s.S);
   return s;
 }
 // First block of wave w's slice (w <= NW).  Equal weights: floor(T w / NW)
@@ -228,6 +224,38 @@ __host__ __device__ __forceinline__ int candidate_slot(const UnitPieces& p, cons
 __host__ __device__ __forceinline__ int wave_count(const DecodeArgs& a, int T) {
   int nw = T / a.min_wave_blocks;
   return nw < 1 ? 1 : (nw > a.num_waves ? a.num_waves : nw);
+}
+
+// The host's part of the full grid's slicing (DecodeArgs::full_*).
+__host__ __device__ __forceinline__ void set_full_grid(DecodeArgs& a) {
+  const int64_t t = (int64_t)a.num_waves * a.min_wave_blocks;
+  a.full_T = t < 0x7FFFFFFF ? (int32_t)t : 0x7FFFFFFF;
+  const Slices f = make_slices(a, 0, a.num_waves > 0 ? a.num_waves : 1);
+  a.full_per = f.PER;
+  a.full_uniform = f.uniform;
+  a.full_sp = f.SP;
+  a.full_s = f.S;
+}
+// NW = wave_count(a, T) and make_slices(a, TV, NW), with the full grid's
+// length-independent parts taken from the host (one division left).
+__host__ __device__ __forceinline__ Slices grid_slices(const DecodeArgs& a, int TV, int T, int& NW) {
+  if (T < a.full_T || a.full_per <= 0) {
+    NW = wave_count(a, T);
+    return make_slices(a, TV, NW);
+  }
+  NW = a.num_waves;
+  Slices s;
+  s.T = TV;
+  s.NW = NW;
+  s.uniform = a.full_uniform;
+  s.PER = a.full_per;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s.W[r] = a.slot_w[r];
+  s.SP = a.full_sp;
+  s.S = a.full_s;
+  s.qT = TV / NW;
+  s.rT = TV - s.qT * NW;
+  return s;
 }
 
 // Dynamic LDS of a workgroup of NT threads, in 32-bit words: the scan scratch
