@@ -130,19 +130,26 @@ struct UnitMerge {
       if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
       m = __builtin_amdgcn_ballot_w64(valid);
       if (m) {
-        // off entries of a group read the batch's first written piece
-        // (finite values) with weight 0
+        // off entries of a group of two read the batch's first written
+        // piece (finite values) with weight 0
         sl0 = __builtin_amdgcn_readlane(slot, (int)__builtin_ctzll(m));
         return true;
       }
     }
     return false;
   }
+  // Groups of more than two pieces take no loads and no products for their
+  // empty places (those of a unit's last group): each would cost its loads
+  // and products at the end of the kernel.  Groups of two keep their places
+  // (the 16-row tiles' merge compiles to code that measured faster so).
+  static constexpr bool kSkip = kDepth > 2;
   // loads of the batch's next kDepth written pieces
   __device__ __forceinline__ void issue(const DecodeArgs& a, const typename Eng::Lane& ln) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       on[u] = m != 0;
+      if constexpr (kSkip)
+        if (!on[u]) continue;   // uniform
       const int q = on[u] ? (int)__builtin_ctzll(m) : 0;
       m = on[u] ? m & (m - 1) : m;
       const int sl = on[u] ? __builtin_amdgcn_readlane(slot, q) : sl0;
@@ -162,13 +169,21 @@ struct UnitMerge {
     for (int it = 0; it < NI; ++it) {
       float Mn = Mx[it];
 #pragma unroll
-      for (int u = 0; u < kDepth; ++u) Mn = fmaxf(Mn, on[u] ? lv[u][it] : -INFINITY);
+      for (int u = 0; u < kDepth; ++u) {
+        if constexpr (kSkip) {
+          if (on[u]) Mn = fmaxf(Mn, lv[u][it]);
+        } else {
+          Mn = fmaxf(Mn, on[u] ? lv[u][it] : -INFINITY);
+        }
+      }
       const float sc = rescale(Mx[it], Mn);
       W[it] *= sc;
 #pragma unroll
       for (int e = 0; e < N; ++e) acc[it][e] *= sc;
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
+        if constexpr (kSkip)
+          if (!on[u]) continue;   // uniform
         const float wt = on[u] ? rescale(lv[u][it], Mn) : 0.f;
         W[it] += wt;
 #pragma unroll
