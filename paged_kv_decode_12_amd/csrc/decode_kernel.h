@@ -120,6 +120,20 @@ struct UnitMerge {
   float lv[kDepth][NI], ov[kDepth][NI][N];
   bool on[kDepth];
 
+  // Equal slices of at least one block (eq), for the merges with groups of
+  // more than two: the slice of a block by one 32-bit division, and every
+  // candidate after the first holds blocks of the unit (its slice starts
+  // inside the unit: its first segment), so only the first candidate's slot
+  // (slot_first) needs its slice's start.  The same results as unit_pieces
+  // and candidate_slot with far fewer dependent instructions: per-wave
+  // stamps put the general forms at ~1.3 us of a merging wave's tail.
+  bool eq;
+  int slot_first;
+  __device__ __forceinline__ int slice_at(const Slices& sl_, int64_t x) const {
+    const int64_t n = (x + 1) * sl_.NW - 1;
+    if (eq && n < 0x100000000LL) return (int)((uint32_t)n / (uint32_t)sl_.T);
+    return slice_of(sl_, x);
+  }
   // Candidates of the batch at c0 and its mask; skips batches with no
   // written piece.  False when none remain.
   __device__ __forceinline__ bool open_batch(const Slices& sl_, int lane) {
@@ -127,7 +141,16 @@ struct UnitMerge {
       const int c = c0 + lane;
       bool valid = false;
       slot = 0;
-      if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
+      if constexpr (kSkip) {
+        if (eq) {
+          valid = c < up.n;
+          slot = c == 0 ? slot_first : 2 * (up.w0 + c);
+        } else if (c < up.n) {
+          slot = candidate_slot(up, sl_, vs, c, valid);
+        }
+      } else {
+        if (c < up.n) slot = candidate_slot(up, sl_, vs, c, valid);
+      }
       m = __builtin_amdgcn_ballot_w64(valid);
       if (m) {
         // off entries of a group of two read the batch's first written
@@ -206,7 +229,14 @@ struct UnitMerge {
     kvh = uidx / a.row_tiles;
     tile = uidx - kvh * a.row_tiles;
     R = a.g * rows.lq;
-    up = unit_pieces(sl_, vs, a.seg_cost, nblk);
+    if constexpr (kSkip) {
+      eq = sl_.uniform && sl_.qT > 0;
+      up.w0 = slice_at(sl_, (int64_t)vs + a.seg_cost);
+      up.n = slice_at(sl_, (int64_t)vs + a.seg_cost + nblk - 1) - up.w0 + 1;
+      slot_first = 2 * up.w0 + (eq && slice_begin(sl_, up.w0) >= vs ? 0 : 1);
+    } else {
+      up = unit_pieces(sl_, vs, a.seg_cost, nblk);
+    }
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       Eng::item_pos(ln, it, rr[it], dd[it]);
