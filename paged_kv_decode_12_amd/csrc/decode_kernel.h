@@ -129,10 +129,28 @@ struct UnitMerge {
   // stamps put the general forms at ~1.3 us of a merging wave's tail.
   bool eq;
   int slot_first;
+  float inv_t, inv_nw;   // 1 / T and 1 / NW (hardware reciprocals)
+  // floor(n / d) for 0 <= n < 2^30, 0 < d < 2^30 with a quotient below
+  // 2^15, from inv = 1 / d within two ulps: the estimate is within 0.01
+  // of n / d, so its truncation is the quotient or a neighbour, which the
+  // remainder corrects (n + d < 2^31: no overflow).
+  static __device__ __forceinline__ int quot_est(int n, int d, float inv) {
+    int q = (int)((float)n * inv);
+    const int r = n - q * d;
+    return r < 0 ? q - 1 : (r >= d ? q + 1 : q);
+  }
+  // n / d for n >= 0 and d > 0: a shift when d is a power of two
+  static __device__ __forceinline__ int quot_pow2(int n, int d) {
+    return (d & (d - 1)) == 0 ? n >> __builtin_ctz(d) : n / d;
+  }
   __device__ __forceinline__ int slice_at(const Slices& sl_, int64_t x) const {
     const int64_t n = (x + 1) * sl_.NW - 1;
-    if (eq && n < 0x100000000LL) return (int)((uint32_t)n / (uint32_t)sl_.T);
+    if (eq && n < 0x40000000LL) return quot_est((int)n, sl_.T, inv_t);
     return slice_of(sl_, x);
+  }
+  // slice_begin of equal slices: qT w + floor(rT w / NW)
+  __device__ __forceinline__ int slice_start(const Slices& sl_, int w) const {
+    return sl_.qT * w + quot_est(sl_.rT * w, sl_.NW, inv_nw);
   }
   // Candidates of the batch at c0 and its mask; skips batches with no
   // written piece.  False when none remain.
@@ -225,15 +243,24 @@ struct UnitMerge {
     nblk = nblk_;
     rows = rows_;
     const int per_req = a.Hkv * a.row_tiles;
-    const int b = unit / per_req, uidx = unit - b * per_req;
-    kvh = uidx / a.row_tiles;
-    tile = uidx - kvh * a.row_tiles;
+    if constexpr (kSkip) {
+      const int b = quot_pow2(unit, per_req), uidx = unit - b * per_req;
+      kvh = quot_pow2(uidx, a.row_tiles);
+      tile = uidx - kvh * a.row_tiles;
+    } else {
+      const int b = unit / per_req, uidx = unit - b * per_req;
+      kvh = uidx / a.row_tiles;
+      tile = uidx - kvh * a.row_tiles;
+    }
     R = a.g * rows.lq;
     if constexpr (kSkip) {
-      eq = sl_.uniform && sl_.qT > 0;
+      // (NW <= 32768 keeps rT w below 2^30 and every quotient below 2^15)
+      eq = sl_.uniform && sl_.qT > 0 && sl_.NW <= 32768 && sl_.T < 0x40000000;
+      inv_t = __builtin_amdgcn_rcpf((float)sl_.T);
+      inv_nw = __builtin_amdgcn_rcpf((float)sl_.NW);
       up.w0 = slice_at(sl_, (int64_t)vs + a.seg_cost);
       up.n = slice_at(sl_, (int64_t)vs + a.seg_cost + nblk - 1) - up.w0 + 1;
-      slot_first = 2 * up.w0 + (eq && slice_begin(sl_, up.w0) >= vs ? 0 : 1);
+      slot_first = 2 * up.w0 + (eq && slice_start(sl_, up.w0) >= vs ? 0 : 1);
     } else {
       up = unit_pieces(sl_, vs, a.seg_cost, nblk);
     }
@@ -267,7 +294,7 @@ struct UnitMerge {
     for (int it = 0; it < NI; ++it) {
       const int r = rr[it], row = tile * RT + r;
       if (!(r < RT && row < R)) continue;
-      const int ti = row / a.g, qhead = kvh * a.g + (row - ti * a.g);
+      const int ti = kSkip ? quot_pow2(row, a.g) : row / a.g, qhead = kvh * a.g + (row - ti * a.g);
       store_item<D, N>(a, s_sink, ((int64_t)rows.row0 + ti) * a.Hq + qhead, qhead, dd[it],
                        dd[it] == 0, Mx[it], W[it], acc[it]);
     }
@@ -581,7 +608,10 @@ void decode_kernel(const DecodeArgs a) {
         for (int k = 0; k < 2; ++k) {
           if (!done[k]) continue;
           if (lane == 0) store_coherent(&a.counters[pend_unit[k]], 0);   // ready for the next call
-          const ReqRows rows = req_info(a, s_nlen, s_qo, pend_unit[k] / (a.Hkv * a.row_tiles)).rows;
+          const int per_req = a.Hkv * a.row_tiles;
+          const int b = UnitMerge<Eng, D>::kSkip ? UnitMerge<Eng, D>::quot_pow2(pend_unit[k], per_req)
+                                                 : pend_unit[k] / per_req;
+          const ReqRows rows = req_info(a, s_nlen, s_qo, b).rows;
           mg[k].begin(a, sl_, pend_unit[k], pend_vs[k], pend_nb[k], rows, ln, lane);
         }
 #pragma unroll
