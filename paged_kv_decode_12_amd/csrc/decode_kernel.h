@@ -108,6 +108,12 @@ struct UnitMerge {
   static constexpr int RT = Eng::kRows, N = Eng::kItemDims, NI = Eng::kItems;
   // (deeper batches for 32-float items, 4 or 8 pieces, measured no faster)
   static constexpr int kDepth = NI * N <= 8 ? 8 : (NI * N <= 16 ? 4 : 2);
+  // Groups of more than two pieces take no loads and no products for their
+  // empty places (those of a unit's last group), and the set-up of equal
+  // slices below; each would otherwise cost its instructions at the end of
+  // the kernel.  Groups of two (the 16-row tiles' 32-float items) keep the
+  // general forms: with either change the MFMA kernels measured slower.
+  static constexpr bool kSkip = kDepth > 2;
   int unit, vs, nblk, tile, kvh, R;
   ReqRows rows;
   UnitPieces up;
@@ -121,12 +127,14 @@ struct UnitMerge {
   bool on[kDepth];
 
   // Equal slices of at least one block (eq), for the merges with groups of
-  // more than two: the slice of a block by one 32-bit division, and every
-  // candidate after the first holds blocks of the unit (its slice starts
-  // inside the unit: its first segment), so only the first candidate's slot
-  // (slot_first) needs its slice's start.  The same results as unit_pieces
-  // and candidate_slot with far fewer dependent instructions: per-wave
-  // stamps put the general forms at ~1.3 us of a merging wave's tail.
+  // more than two: the slice of a block from a hardware reciprocal of the
+  // sliced space's size, corrected exactly by the remainder (quot_est), and
+  // every candidate after the first holds blocks of the unit (its slice
+  // starts inside the unit: its first segment), so only the first
+  // candidate's slot (slot_first) needs its slice's start.  The same results
+  // as unit_pieces and candidate_slot with far fewer dependent instructions:
+  // per-wave stamps put the general forms at ~1.3 us of a merging wave's
+  // tail.
   bool eq;
   int slot_first;
   float inv_t, inv_nw;   // 1 / T and 1 / NW (hardware reciprocals)
@@ -179,11 +187,6 @@ struct UnitMerge {
     }
     return false;
   }
-  // Groups of more than two pieces take no loads and no products for their
-  // empty places (those of a unit's last group): each would cost its loads
-  // and products at the end of the kernel.  Groups of two keep their places
-  // (the 16-row tiles' merge compiles to code that measured faster so).
-  static constexpr bool kSkip = kDepth > 2;
   // loads of the batch's next kDepth written pieces
   __device__ __forceinline__ void issue(const DecodeArgs& a, const typename Eng::Lane& ln) {
 #pragma unroll
