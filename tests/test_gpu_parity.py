@@ -302,6 +302,37 @@ def test_edge_sweep(case, sched):
     compare(_edge_id(case), out, lse, ref_out, ref_lse, out_atol=atol)
 
 
+# A long request over many waves: units cut into more pieces than one
+# candidate batch of the merge holds (64), on the VALU engine, merged in
+# place from equal slices (4-row tiles, one wave per SIMD: the reciprocal
+# set-up), in place from weighted slices (8-row tiles, two waves per SIMD:
+# the general set-up) and by the merge kernel.  Entries: knobs, query heads.
+MANY_PIECES = {
+    "inplace_equal": (dict(PKVD_WAVES="300", PKVD_MIN_WAVE_BLOCKS="1", PKVD_MERGE_KERNEL="0",
+                           PKVD_FORCE_PATH="0"), 8),
+    "inplace_weighted": (dict(PKVD_WAVES="300", PKVD_MIN_WAVE_BLOCKS="1", PKVD_GROUPS="38",
+                              PKVD_SLOT_W="140,100", PKVD_MERGE_KERNEL="0", PKVD_FORCE_PATH="0"),
+                         16),
+    "kernel": (dict(PKVD_WAVES="300", PKVD_MIN_WAVE_BLOCKS="1", PKVD_MERGE_KERNEL="1",
+                    PKVD_FORCE_PATH="0"), 8),
+}
+
+
+@pytest.mark.parametrize("sched", list(MANY_PIECES))
+def test_units_of_many_pieces(sched):
+    pk = _pk()
+    knobs, hq = MANY_PIECES[sched]
+    inp = workloads.make_case(B=3, Hq=hq, Hkv=2, D=128, page_size=16, seq_lens=(8192, 3000, 17),
+                              seed=11)
+    log(f"[many-pieces] schedule={sched}")
+    with env(**knobs):
+        st = pk.schedule_stats(inp["q"], inp["k_cache"], inp["block_tables"], inp["seq_lens_kv"])
+        assert st["errors"] == 0 and st["max_pieces"] > 64, st
+        out, lse = run_gpu(to_dev(inp))
+    ref_out, ref_lse, _ = oracle.decode(inp)
+    compare(f"many-pieces/{sched}", out, lse, ref_out, ref_lse)
+
+
 def test_combined_kv_tensor():
     """K and V as views of one (pages, 2, Hkv, ps, D) tensor (strided pages)."""
     inp = workloads.make_case(B=3, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=(5, 60, 131), seed=3)
